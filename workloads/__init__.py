@@ -1,0 +1,211 @@
+"""Seeded synthetic inputs for sparse MLA decode.
+
+This module only draws inputs: query vectors, latent cache rows, top-k index
+lists and page tables.  It holds none of the attention arithmetic, and both
+the HIP path's tests and the CPU oracle's tests consume what it produces.
+
+Value recipe: every q and cache element is bf16_rne(0.5 * N(0, 1)).  Index
+lists are drawn uniformly without replacement from each query token's own
+context and left in sampled (random) order.  Paged pools use 64-token pages
+whose physical order is a random permutation; logical positions are turned
+into physical rows (page * 64 + slot) here, before the library sees them.
+
+Seeds: workload k uses base seed 1000 * k, with sub-streams +0 q, +1 cache,
++2 index lists, +3 page permutation, +4 context lengths.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+from typing import Optional
+
+import numpy as np
+
+D = 576          # q / cache row width in bf16 elements (512 latent + 64 rope)
+ROW_BYTES = D * 2
+PAGE = 64        # tokens per page in the paged pools
+SCALE = float(np.float32(1.0 / math.sqrt(192.0)))
+
+SUB_Q, SUB_KV, SUB_IDX, SUB_PAGES, SUB_CTX = 0, 1, 2, 3, 4
+
+
+# ----------------------------------------------------------------- bf16 bits
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); uint16 bits."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = (u + 0x7FFF + lsb) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32 (exact)."""
+    b = np.ascontiguousarray(b, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape, std: float = 0.5) -> np.ndarray:
+    """bf16 bits of std * N(0, 1) samples."""
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+# ----------------------------------------------------------------- workloads
+
+@dataclasses.dataclass
+class Inputs:
+    """One decode call's inputs, host side.
+
+    q:   [B, Lq, H, 576] uint16 (bf16 bits)
+    kv:  [N, 576] uint16, or None when the pool is generated on the device
+    idx: [B, Lq, K] int32 physical row indices (-1 = masked)
+    kv_rows: N
+    pool_seed: seed of the device-side pool when kv is None
+    """
+    name: str
+    q: np.ndarray
+    kv: Optional[np.ndarray]
+    idx: np.ndarray
+    kv_rows: int
+    scale: float = SCALE
+    pool_seed: Optional[int] = None
+    ctx: Optional[np.ndarray] = None          # per-sequence context lengths
+    page_table: Optional[list] = None         # per-sequence physical page ids
+
+    @property
+    def batch(self): return self.q.shape[0]
+
+    @property
+    def q_len(self): return self.q.shape[1]
+
+    @property
+    def heads(self): return self.q.shape[2]
+
+    @property
+    def topk(self): return self.idx.shape[-1]
+
+
+def sample_topk(rng: np.random.Generator, ctx: int, topk: int) -> np.ndarray:
+    """`topk` distinct logical positions drawn uniformly from [0, ctx), in
+    sampled order; when ctx < topk every position is taken and the rest of
+    the list is -1."""
+    k = min(ctx, topk)
+    out = np.full(topk, -1, np.int32)
+    if k > 0:
+        out[:k] = rng.choice(ctx, size=k, replace=False).astype(np.int32)
+    return out
+
+
+def flat_inputs(name: str, seed: int, batch: int, q_len: int, heads: int, kv_rows: int,
+                topk: int, ctx: Optional[int] = None, with_kv: bool = True) -> Inputs:
+    """Flat cache [kv_rows, 576]; each query token draws its own list from [0, ctx)."""
+    ctx = kv_rows if ctx is None else ctx
+    q = normal_bf16(np.random.default_rng(seed + SUB_Q), (batch, q_len, heads, D))
+    kv = normal_bf16(np.random.default_rng(seed + SUB_KV), (kv_rows, D)) if with_kv else None
+    rng = np.random.default_rng(seed + SUB_IDX)
+    idx = np.stack([np.stack([sample_topk(rng, ctx, topk) for _ in range(q_len)])
+                    for _ in range(batch)]).astype(np.int32)
+    return Inputs(name, q, kv, idx, kv_rows, pool_seed=None if with_kv else seed + SUB_KV)
+
+
+def paged_inputs(name: str, seed: int, heads: int, topk: int, ctx: np.ndarray,
+                 q_len: int = 1, with_kv: bool = False) -> Inputs:
+    """Paged pool: sequence b owns ceil(ctx[b] / 64) pages scattered through a
+    randomly permuted pool; its list holds physical rows of its own context."""
+    ctx = np.asarray(ctx, np.int64)
+    batch = len(ctx)
+    pages = (ctx + PAGE - 1) // PAGE
+    total_pages = int(pages.sum())
+    perm = np.random.default_rng(seed + SUB_PAGES).permutation(total_pages).astype(np.int64)
+    table, off = [], 0
+    for b in range(batch):
+        table.append(perm[off: off + pages[b]])
+        off += pages[b]
+    rng = np.random.default_rng(seed + SUB_IDX)
+    idx = np.empty((batch, q_len, topk), np.int32)
+    for b in range(batch):
+        for i in range(q_len):
+            pos = sample_topk(rng, int(ctx[b]), topk).astype(np.int64)
+            phys = np.where(pos >= 0, table[b][np.maximum(pos, 0) // PAGE] * PAGE + np.maximum(pos, 0) % PAGE, -1)
+            idx[b, i] = phys.astype(np.int32)
+    kv_rows = total_pages * PAGE
+    q = normal_bf16(np.random.default_rng(seed + SUB_Q), (batch, q_len, heads, D))
+    kv = normal_bf16(np.random.default_rng(seed + SUB_KV), (kv_rows, D)) if with_kv else None
+    return Inputs(name, q, kv, idx, kv_rows, pool_seed=None if with_kv else seed + SUB_KV,
+                  ctx=ctx, page_table=table)
+
+
+# The five workload shapes: (1) tiny, (2) single request at long context,
+# (3) batched decode over a paged pool, (4) speculative-verify shape (9 query
+# tokens, each with its own list), (5) large ragged batch over a paged pool.
+WORKLOADS = ("tiny", "long", "batched", "spec", "ragged")
+
+
+def workload(name: str, *, spec_ctx: int = 65536, with_kv: Optional[bool] = None,
+             ragged_pad: bool = False, batch: Optional[int] = None) -> Inputs:
+    """Inputs of a named workload.
+
+    with_kv: build the cache on the host (default: only when it is small).
+    batch: keep only the first `batch` sequences (sampling for the oracle).
+    ragged_pad: the ragged workload with its first 16 sequences shorter than
+      the list (contexts in [1, 2047]) so their lists end in -1 padding.
+    """
+    if name == "tiny":
+        return flat_inputs(name, 1000, 1, 1, 8, 1024, 128, with_kv=True if with_kv is None else with_kv)
+    if name == "long":
+        return flat_inputs(name, 2000, 1, 1, 8, 65536, 2048, with_kv=True if with_kv is None else with_kv)
+    if name == "batched":
+        b = 64 if batch is None else batch
+        ctx = np.full(64, 32768, np.int64)
+        inp = paged_inputs(name, 3000, 64, 2048, ctx, with_kv=bool(with_kv))
+        return _first_sequences(inp, b)
+    if name == "spec":
+        return flat_inputs(f"spec{spec_ctx}", 4000, 1, 9, 8, spec_ctx, 2048,
+                           with_kv=True if with_kv is None else with_kv)
+    if name == "ragged":
+        rng = np.random.default_rng(5000 + SUB_CTX)
+        ctx = rng.integers(2048, 131072, size=128, endpoint=True).astype(np.int64)
+        if ragged_pad:
+            ctx[:16] = rng.integers(1, 2047, size=16, endpoint=True)
+        inp = paged_inputs("ragged_pad" if ragged_pad else name, 5000, 128, 2048, ctx,
+                           with_kv=bool(with_kv))
+        return _first_sequences(inp, 128 if batch is None else batch)
+    raise KeyError(name)
+
+
+def _first_sequences(inp: Inputs, b: int) -> Inputs:
+    if b >= inp.batch:
+        return inp
+    return dataclasses.replace(inp, q=inp.q[:b], idx=inp.idx[:b],
+                               ctx=None if inp.ctx is None else inp.ctx[:b],
+                               page_table=None if inp.page_table is None else inp.page_table[:b])
+
+
+def device_pool(kv_rows: int, seed: int, device, chunk_rows: int = 1 << 18):
+    """Cache pool [kv_rows, 576] bf16 drawn on `device` with a seeded torch
+    generator (for pools too large to build on the host)."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    kv = torch.empty((kv_rows, D), dtype=torch.bfloat16, device=device)
+    for r0 in range(0, kv_rows, chunk_rows):
+        r1 = min(kv_rows, r0 + chunk_rows)
+        kv[r0:r1] = (torch.randn((r1 - r0, D), generator=g, device=device, dtype=torch.float32) * 0.5
+                     ).to(torch.bfloat16)
+    return kv
+
+
+def compact_rows(idx: np.ndarray, kv_rows: int):
+    """Unique valid rows of a list set and the list remapped onto them.
+
+    Returns (rows [U] int64, idx2 like idx) with idx2 = position of the row in
+    `rows`, and -1 for every entry outside [0, kv_rows).  Lets the oracle read
+    only the rows a call gathers instead of a multi-GB pool.
+    """
+    flat = idx.reshape(-1).astype(np.int64)
+    valid = (flat >= 0) & (flat < kv_rows)
+    rows, inv = np.unique(flat[valid], return_inverse=True)
+    idx2 = np.full(flat.shape, -1, np.int64)
+    idx2[valid] = inv
+    return rows, idx2.reshape(idx.shape).astype(np.int32)

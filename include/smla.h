@@ -1,0 +1,146 @@
+/*
+ * smla.h -- sparse MLA decode attention with split-K over the top-k list,
+ * for AMD Instinct MI355X (gfx950).  C ABI: plain pointers and sizes.
+ *
+ * What is computed.  Every query token t attends only to the cache rows its
+ * top-k list selects.  A cache row holds 576 bf16 values: 512 latent columns
+ * followed by 64 rope columns; the value vector of a row is its first 512
+ * columns, the key is the whole row.  For head h, with J the list entries
+ * whose row r satisfies 0 <= r < kv_rows:
+ *     s_j = scale * <q[t,h,0:576], kv[r_j,0:576]>
+ *     out[t,h,0:512] = sum_j softmax(s)_j kv[r_j,0:512]   (bf16, RNE)
+ *     lse[t,h]       = ln sum_j exp(s_j)                   (fp32)
+ * An empty J gives out = 0 and lse = -inf.  List entries equal to -1, or any
+ * other value outside [0, kv_rows), carry zero weight; they are data, not
+ * errors.  Duplicate entries are separate softmax terms.
+ *
+ * Split-K ("The Moment of Truth: Validating Split-K Parallelization for
+ * Blackwell MLA Decode", section "The Split-K Imperative"): the list of each
+ * token is cut into NSPLIT contiguous slices of ceil(topk / NSPLIT) entries
+ * (the last one short or empty); each slice yields a partial (O, LSE) and a
+ * log-sum-exp combine merges the partials in fp32.  NSPLIT multiplies the
+ * number of workgroups so that small batches still fill the GPU ("The
+ * Occupancy Hypothesis: How One Kernel Parameter Unlocked 1.8x Decode Speedup
+ * on Blackwell", sections "The Occupancy Insight" and "The Broader Context").
+ *
+ * Layouts (contiguous, row-major, device memory):
+ *   q          [batch, q_len, heads, 576]   bf16
+ *   kv_cache   [kv_rows, 576]               bf16  (a paged pool is passed flat:
+ *                                                  physical row = page*64 + slot)
+ *   topk_idx   [batch, q_len, topk]         int32 physical row indices
+ *   out        [batch, q_len, heads, 512]   bf16
+ *   lse        [batch, q_len, heads]        fp32
+ *   workspace  part_o [T, NSPLIT, heads, 512] fp32, then (at byte offset
+ *              smla_workspace_lse_offset) part_lse [T, NSPLIT, heads] fp32,
+ *              T = batch * q_len.
+ * q, kv_cache, out and workspace must be 16-byte aligned; topk_idx and lse
+ * 4-byte aligned.
+ *
+ * Ownership and execution.  The caller owns every buffer, including the
+ * workspace; the library allocates no device memory and keeps no per-call
+ * state (its only global is a per-device cache of the CU count).  Work is
+ * enqueued on `hip_stream` (a hipStream_t; NULL = the legacy default stream)
+ * and the call returns without waiting for it: buffers must stay alive and
+ * unmodified until the stream has passed the call.  The calls never
+ * synchronise the host, so they can be captured into a HIP graph.  Calls on
+ * different streams that share a workspace race.
+ *
+ * Errors.  Every entry point returns SMLA_OK (0) or a negative smla_status.
+ * Arguments are validated before anything is enqueued; on an error nothing is
+ * launched and nothing is written.  A failed launch returns SMLA_ERR_LAUNCH
+ * (the HIP error state is cleared).  Faults inside a kernel surface at the
+ * caller's next synchronisation.  NaN or Inf inside q or the selected rows
+ * propagate; they are not checked.
+ */
+#ifndef SMLA_H
+#define SMLA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum smla_status {
+  SMLA_OK = 0,
+  SMLA_ERR_NULL = -1,      /* a required pointer is NULL */
+  SMLA_ERR_DIM = -2,       /* a size is negative, zero where it must not be, or above a limit */
+  SMLA_ERR_NSPLIT = -3,    /* nsplit < 0 or > SMLA_MAX_NSPLIT */
+  SMLA_ERR_WORKSPACE = -4, /* nsplit > 1 and the workspace is NULL or too small */
+  SMLA_ERR_ALIGN = -5,     /* a pointer breaks the alignment rules above */
+  SMLA_ERR_DEVICE = -6,    /* no usable gfx950 device / device query failed */
+  SMLA_ERR_LAUNCH = -7     /* a kernel launch failed */
+};
+
+#define SMLA_ROW 576          /* q and cache row width (bf16 elements) */
+#define SMLA_DV 512           /* value / output width (bf16 elements) */
+#define SMLA_MAX_NSPLIT 1024  /* largest NSPLIT accepted */
+#define SMLA_MAX_HEADS 4096   /* largest head count accepted */
+#define SMLA_MAX_TOPK (1 << 24)
+
+/*
+ * NSPLIT the planner picks for a call of this shape on the current device
+ * (its CU count is queried once per device).  Returns >= 1, or a negative
+ * status (SMLA_ERR_DIM for bad sizes, SMLA_ERR_DEVICE if no device).
+ */
+int smla_plan_nsplit(int batch, int q_len, int heads, int topk);
+
+/*
+ * The same planner as a pure function of the CU count: no device access, so
+ * it runs (and is tested) on hosts without a GPU.  The rule aims at enough
+ * workgroups to keep every CU's memory pipeline busy at batch 1 as well as
+ * at batch 128, while each split keeps enough rows to amortise its partial
+ * (O, LSE) write ("The Occupancy Hypothesis", "The Occupancy Insight":
+ * blocks in flight, not per-block work, hide memory latency).
+ */
+int smla_plan_nsplit_cus(int cus, int batch, int q_len, int heads, int topk);
+
+/* Bytes of workspace smla_decode / smla_split need (0 when nsplit <= 1). */
+size_t smla_workspace_bytes(int batch, int q_len, int heads, int nsplit);
+
+/* Byte offset of part_lse inside the workspace (256-byte aligned). */
+size_t smla_workspace_lse_offset(int batch, int q_len, int heads, int nsplit);
+
+/*
+ * Full decode: the split kernel over every (token, split) and, when
+ * NSPLIT > 1, the combine kernel.  nsplit == 0 asks the planner
+ * (smla_plan_nsplit); size the workspace with smla_workspace_bytes for the
+ * NSPLIT actually used.  nsplit > topk is allowed (surplus splits are empty).
+ * batch == 0, q_len == 0 or topk == 0 are valid: the first two launch
+ * nothing; topk == 0 writes out = 0, lse = -inf.
+ */
+int smla_decode(const void *q, const void *kv_cache, const int32_t *topk_idx, void *out,
+                float *lse, float scale, int nsplit, int batch, int q_len, int heads, int topk,
+                int64_t kv_rows, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * The split kernel alone ("The Split-K Imperative": each block computes a
+ * partial attention output over its slice of the list).  With NSPLIT > 1 it
+ * writes part_o / part_lse into the workspace (layout above; an empty slice
+ * gives O = 0, LSE = -inf) and leaves out / lse untouched (they may be NULL);
+ * with NSPLIT == 1 it writes out / lse directly.  Arguments as smla_decode.
+ */
+int smla_split(const void *q, const void *kv_cache, const int32_t *topk_idx, void *out,
+               float *lse, float scale, int nsplit, int batch, int q_len, int heads, int topk,
+               int64_t kv_rows, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * The combine kernel alone ("The Split-K Imperative": the log-sum-exp
+ * combine merges the partials).  For every (token, head): M = max_s LSE_s;
+ * M = -inf gives out = 0, lse = -inf; else w_s = exp(LSE_s - M),
+ * out = sum_s w_s O_s / sum_s w_s (fp32, then bf16 RNE), lse = M + ln sum_s w_s.
+ * part_o [tokens, nsplit, heads, 512] fp32 (16-byte aligned),
+ * part_lse [tokens, nsplit, heads] fp32; 1 <= nsplit <= SMLA_MAX_NSPLIT.
+ */
+int smla_combine(const float *part_o, const float *part_lse, void *out, float *lse, int tokens,
+                 int heads, int nsplit, void *hip_stream);
+
+/* Static description of a status code (never NULL). */
+const char *smla_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMLA_H */

@@ -1,0 +1,190 @@
+"""Python binding of libsmla.so -- sparse MLA decode with split-K over the
+top-k list on MI355X (gfx950).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/smla.h).  torch supplies device memory and
+the stream; there is no CPU fallback, and importing this package without the
+built library raises.
+
+Functions carry the C names: smla_plan_nsplit, smla_plan_nsplit_cus,
+smla_workspace_bytes, smla_workspace_lse_offset, smla_decode, smla_split,
+smla_combine, smla_status_str.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch  # noqa: F401  (loads the HIP runtime the library binds to)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsmla.so")
+
+ROW = 576
+DV = 512
+MAX_NSPLIT = 1024
+
+STATUS = {0: "SMLA_OK", -1: "SMLA_ERR_NULL", -2: "SMLA_ERR_DIM", -3: "SMLA_ERR_NSPLIT",
+          -4: "SMLA_ERR_WORKSPACE", -5: "SMLA_ERR_ALIGN", -6: "SMLA_ERR_DEVICE",
+          -7: "SMLA_ERR_LAUNCH"}
+
+
+class SmlaError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {STATUS.get(code, code)} ({smla_status_str(code)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m sparse_mla_decode_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.smla_plan_nsplit.argtypes = [i32, i32, i32, i32]
+    lib.smla_plan_nsplit.restype = i32
+    lib.smla_plan_nsplit_cus.argtypes = [i32, i32, i32, i32, i32]
+    lib.smla_plan_nsplit_cus.restype = i32
+    lib.smla_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    lib.smla_workspace_bytes.restype = sz
+    lib.smla_workspace_lse_offset.argtypes = [i32, i32, i32, i32]
+    lib.smla_workspace_lse_offset.restype = sz
+    call = [vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i64, vp, sz, vp]
+    lib.smla_decode.argtypes = call
+    lib.smla_decode.restype = i32
+    lib.smla_split.argtypes = call
+    lib.smla_split.restype = i32
+    lib.smla_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.smla_combine.restype = i32
+    lib.smla_status_str.argtypes = [i32]
+    lib.smla_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+lib = _lib  # the raw ctypes handle (tests call the C ABI through it)
+
+
+def smla_status_str(status: int) -> str:
+    return _lib.smla_status_str(int(status)).decode()
+
+
+def smla_plan_nsplit(batch: int, q_len: int, heads: int, topk: int) -> int:
+    r = _lib.smla_plan_nsplit(batch, q_len, heads, topk)
+    if r < 1:
+        raise SmlaError(r, "smla_plan_nsplit")
+    return r
+
+
+def smla_plan_nsplit_cus(cus: int, batch: int, q_len: int, heads: int, topk: int) -> int:
+    r = _lib.smla_plan_nsplit_cus(cus, batch, q_len, heads, topk)
+    if r < 1:
+        raise SmlaError(r, "smla_plan_nsplit_cus")
+    return r
+
+
+def smla_workspace_bytes(batch: int, q_len: int, heads: int, nsplit: int) -> int:
+    return int(_lib.smla_workspace_bytes(batch, q_len, heads, nsplit))
+
+
+def smla_workspace_lse_offset(batch: int, q_len: int, heads: int, nsplit: int) -> int:
+    return int(_lib.smla_workspace_lse_offset(batch, q_len, heads, nsplit))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _shape(q: torch.Tensor, topk_idx: torch.Tensor):
+    if q.dim() != 4 or q.shape[-1] != ROW:
+        raise ValueError(f"q must be [batch, q_len, heads, {ROW}], got {tuple(q.shape)}")
+    b, lq, h, _ = q.shape
+    if topk_idx.dim() != 3 or tuple(topk_idx.shape[:2]) != (b, lq):
+        raise ValueError(f"topk_idx must be [batch, q_len, topk], got {tuple(topk_idx.shape)}")
+    return b, lq, h, topk_idx.shape[2]
+
+
+def _check_tensors(q, kv_cache, topk_idx, out, lse):
+    for name, t, dt in (("q", q, torch.bfloat16), ("kv_cache", kv_cache, torch.bfloat16),
+                        ("topk_idx", topk_idx, torch.int32), ("out", out, torch.bfloat16),
+                        ("lse", lse, torch.float32)):
+        if t is None:
+            continue
+        if t.dtype != dt:
+            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if kv_cache.dim() != 2 or kv_cache.shape[1] != ROW:
+        raise ValueError(f"kv_cache must be [rows, {ROW}], got {tuple(kv_cache.shape)}")
+
+
+def workspace(batch: int, q_len: int, heads: int, nsplit: int, device) -> torch.Tensor | None:
+    """A workspace tensor of the size the call needs (None when nsplit <= 1)."""
+    n = smla_workspace_bytes(batch, q_len, heads, nsplit)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def _call(fn, name, q, kv_cache, topk_idx, out, lse, scale, nsplit, ws, stream):
+    _check_tensors(q, kv_cache, topk_idx, out, lse)
+    b, lq, h, k = _shape(q, topk_idx)
+    if nsplit == 0 and b * lq > 0:
+        nsplit = smla_plan_nsplit(b, lq, h, k)
+    if ws is None and nsplit > 1:
+        ws = workspace(b, lq, h, nsplit, q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = fn(_ptr(q), _ptr(kv_cache), _ptr(topk_idx), _ptr(out), _ptr(lse), float(scale),
+            int(nsplit), b, lq, h, k, kv_cache.shape[0], _ptr(ws), ws_bytes, _stream(stream))
+    if rc != 0:
+        raise SmlaError(rc, name)
+    return nsplit, ws
+
+
+def smla_decode(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int = 0,
+                workspace_t=None, stream=None) -> int:
+    """Sparse MLA decode into `out` [B, Lq, H, 512] bf16 and `lse` [B, Lq, H] fp32.
+
+    nsplit 0 asks the planner.  A workspace is allocated when none is given
+    and NSPLIT > 1.  Returns the NSPLIT used.
+    """
+    return _call(_lib.smla_decode, "smla_decode", q, kv_cache, topk_idx, out, lse, scale, nsplit,
+                 workspace_t, stream)[0]
+
+
+def smla_split(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int,
+               workspace_t=None, stream=None):
+    """Split kernel alone.  Returns (nsplit, workspace) -- the partials live in
+    the workspace (see partials_view) when NSPLIT > 1."""
+    return _call(_lib.smla_split, "smla_split", q, kv_cache, topk_idx, out, lse, scale, nsplit,
+                 workspace_t, stream)
+
+
+def partials_view(ws: torch.Tensor, batch: int, q_len: int, heads: int, nsplit: int):
+    """(part_o [T, S, H, 512], part_lse [T, S, H]) views into a workspace."""
+    t = batch * q_len
+    n_o = t * nsplit * heads * DV
+    off = smla_workspace_lse_offset(batch, q_len, heads, nsplit)
+    part_o = ws[: n_o * 4].view(torch.float32).view(t, nsplit, heads, DV)
+    part_lse = ws[off: off + t * nsplit * heads * 4].view(torch.float32).view(t, nsplit, heads)
+    return part_o, part_lse
+
+
+def smla_combine(part_o: torch.Tensor, part_lse: torch.Tensor, out: torch.Tensor,
+                 lse: torch.Tensor, stream=None) -> None:
+    """Combine kernel alone: part_o [T, S, H, 512] fp32, part_lse [T, S, H] fp32."""
+    if part_o.dtype != torch.float32 or part_lse.dtype != torch.float32:
+        raise TypeError("partials must be float32")
+    if not (part_o.is_contiguous() and part_lse.is_contiguous()):
+        raise ValueError("partials must be contiguous")
+    t, s, h = part_lse.shape
+    if tuple(part_o.shape) != (t, s, h, DV):
+        raise ValueError(f"part_o must be [{t}, {s}, {h}, {DV}], got {tuple(part_o.shape)}")
+    rc = _lib.smla_combine(_ptr(part_o), _ptr(part_lse), _ptr(out), _ptr(lse), t, h, s,
+                           _stream(stream))
+    if rc != 0:
+        raise SmlaError(rc, "smla_combine")

@@ -1,0 +1,230 @@
+// smla_api.cpp -- the C ABI declared in include/smla.h: argument validation,
+// the NSPLIT planner, workspace sizing and kernel launches.  Host code only;
+// the kernels live in smla_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/smla.h"
+#include "smla_internal.h"
+
+#define SMLA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+static_assert(SMLA_MAX_NSPLIT == smla::kMaxNsplit, "limits out of sync");
+static_assert(SMLA_ROW == smla::kRow && SMLA_DV == smla::kDV, "widths out of sync");
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
+
+// CU count of the current device, queried once per device.
+int device_cus(int* cus) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();
+    return SMLA_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices) {
+    int c = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (c > 0) {
+      *cus = c;
+      return SMLA_OK;
+    }
+  }
+  int c = 0;
+  if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      c <= 0) {
+    (void)hipGetLastError();
+    return SMLA_ERR_DEVICE;
+  }
+  if (dev < kMaxDevices) g_cu_count[dev].store(c, std::memory_order_relaxed);
+  *cus = c;
+  return SMLA_OK;
+}
+
+bool dims_ok(int batch, int q_len, int heads, int topk) {
+  if (batch < 0 || q_len < 0 || topk < 0 || topk > SMLA_MAX_TOPK) return false;
+  if (heads < 1 || heads > SMLA_MAX_HEADS) return false;
+  const int64_t tokens = (int64_t)batch * q_len;
+  return tokens <= (int64_t)1 << 30;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+size_t lse_offset(int64_t tokens, int heads, int nsplit) {
+  return round_up((size_t)tokens * nsplit * heads * SMLA_DV * sizeof(float), 256);
+}
+
+size_t ws_bytes(int64_t tokens, int heads, int nsplit) {
+  if (nsplit <= 1) return 0;
+  return lse_offset(tokens, heads, nsplit) + (size_t)tokens * nsplit * heads * sizeof(float);
+}
+
+// Shared by smla_decode (combine = true) and smla_split (combine = false).
+int run(const void* q, const void* kv, const int32_t* idx, void* out, float* lse, float scale,
+        int nsplit, int batch, int q_len, int heads, int topk, int64_t kv_rows, void* ws,
+        size_t ws_size, void* stream, bool combine) {
+  if (!dims_ok(batch, q_len, heads, topk) || kv_rows < 0) return SMLA_ERR_DIM;
+  if (nsplit < 0 || nsplit > SMLA_MAX_NSPLIT) return SMLA_ERR_NSPLIT;
+  const int64_t tokens = (int64_t)batch * q_len;
+  if (tokens == 0) return SMLA_OK;  // nothing to compute, nothing written
+
+  if (nsplit == 0) {
+    int cus = 0;
+    const int rc = device_cus(&cus);
+    if (rc != SMLA_OK) return rc;
+    nsplit = smla_plan_nsplit_cus(cus, batch, q_len, heads, topk);
+    if (nsplit < 1) return nsplit;
+  }
+  const bool partials = nsplit > 1;
+  const bool writes_out = !partials || combine;
+
+  if (!q || (topk > 0 && !idx) || (kv_rows > 0 && !kv)) return SMLA_ERR_NULL;
+  if (writes_out && (!out || !lse)) return SMLA_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(idx, 4)) return SMLA_ERR_ALIGN;
+  if (writes_out && (!aligned(out, 16) || !aligned(lse, 4))) return SMLA_ERR_ALIGN;
+  if (partials) {
+    if (!ws || ws_size < ws_bytes(tokens, heads, nsplit)) return SMLA_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return SMLA_ERR_ALIGN;
+  }
+  const int64_t hblocks = (heads + smla::split_heads_per_block(heads) - 1) /
+                          smla::split_heads_per_block(heads);
+  if ((int64_t)nsplit * tokens * hblocks > 0x7fffffffLL) return SMLA_ERR_DIM;
+
+  hipStream_t st = (hipStream_t)stream;
+  smla::SplitParams sp;
+  sp.q = (const uint16_t*)q;
+  sp.kv = (const uint16_t*)kv;
+  sp.idx = idx;
+  sp.out = (uint16_t*)out;
+  sp.lse = lse;
+  sp.part_o = partials ? (float*)ws : nullptr;
+  sp.part_lse = partials ? (float*)((char*)ws + lse_offset(tokens, heads, nsplit)) : nullptr;
+  sp.kv_rows = kv_rows;
+  sp.tokens = (int)tokens;
+  sp.heads = heads;
+  sp.topk = topk;
+  sp.nsplit = nsplit;
+  sp.per_split = topk == 0 ? 0 : (topk + nsplit - 1) / nsplit;
+  sp.scale_log2 = scale * smla::kLog2e;
+  if (smla::launch_split(sp, st) != hipSuccess) {
+    (void)hipGetLastError();
+    return SMLA_ERR_LAUNCH;
+  }
+  if (partials && combine) {
+    smla::CombineParams cp;
+    cp.part_o = sp.part_o;
+    cp.part_lse = sp.part_lse;
+    cp.out = (uint16_t*)out;
+    cp.lse = lse;
+    cp.tokens = (int)tokens;
+    cp.heads = heads;
+    cp.nsplit = nsplit;
+    if (smla::launch_combine(cp, st) != hipSuccess) {
+      (void)hipGetLastError();
+      return SMLA_ERR_LAUNCH;
+    }
+  }
+  return SMLA_OK;
+}
+
+}  // namespace
+
+SMLA_API int smla_plan_nsplit_cus(int cus, int batch, int q_len, int heads, int topk) {
+  if (cus < 1 || !dims_ok(batch, q_len, heads, topk)) return SMLA_ERR_DIM;
+  const int64_t tokens = (int64_t)batch * q_len;
+  if (tokens == 0 || topk == 0) return 1;
+  const int hpb = smla::split_heads_per_block(heads);
+  const int64_t units = tokens * ((heads + hpb - 1) / hpb);  // workgroups per split
+  // Aim for two workgroups per CU (memory-level parallelism), but keep at
+  // least kMinRows list entries per split so the partial write stays small
+  // next to the rows a split gathers.
+  constexpr int kMinRows = 16;
+  const int64_t target = 2 * (int64_t)cus;
+  int64_t ns = (target + units - 1) / units;
+  const int64_t max_ns = topk / kMinRows > 0 ? topk / kMinRows : 1;
+  if (ns > max_ns) ns = max_ns;
+  if (ns > SMLA_MAX_NSPLIT) ns = SMLA_MAX_NSPLIT;
+  if (ns < 1) ns = 1;
+  // same slice length with the fewest splits: no trailing short or empty split
+  const int64_t per = (topk + ns - 1) / ns;
+  ns = (topk + per - 1) / per;
+  return (int)ns;
+}
+
+SMLA_API int smla_plan_nsplit(int batch, int q_len, int heads, int topk) {
+  if (!dims_ok(batch, q_len, heads, topk)) return SMLA_ERR_DIM;
+  int cus = 0;
+  const int rc = device_cus(&cus);
+  if (rc != SMLA_OK) return rc;
+  return smla_plan_nsplit_cus(cus, batch, q_len, heads, topk);
+}
+
+SMLA_API size_t smla_workspace_bytes(int batch, int q_len, int heads, int nsplit) {
+  if (batch < 0 || q_len < 0 || heads < 1 || nsplit < 0) return 0;
+  return ws_bytes((int64_t)batch * q_len, heads, nsplit);
+}
+
+SMLA_API size_t smla_workspace_lse_offset(int batch, int q_len, int heads, int nsplit) {
+  if (batch < 0 || q_len < 0 || heads < 1 || nsplit < 1) return 0;
+  return lse_offset((int64_t)batch * q_len, heads, nsplit);
+}
+
+SMLA_API int smla_decode(const void* q, const void* kv_cache, const int32_t* topk_idx, void* out,
+                         float* lse, float scale, int nsplit, int batch, int q_len, int heads,
+                         int topk, int64_t kv_rows, void* workspace, size_t workspace_bytes,
+                         void* hip_stream) {
+  return run(q, kv_cache, topk_idx, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
+             workspace, workspace_bytes, hip_stream, true);
+}
+
+SMLA_API int smla_split(const void* q, const void* kv_cache, const int32_t* topk_idx, void* out,
+                        float* lse, float scale, int nsplit, int batch, int q_len, int heads,
+                        int topk, int64_t kv_rows, void* workspace, size_t workspace_bytes,
+                        void* hip_stream) {
+  return run(q, kv_cache, topk_idx, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
+             workspace, workspace_bytes, hip_stream, false);
+}
+
+SMLA_API int smla_combine(const float* part_o, const float* part_lse, void* out, float* lse,
+                          int tokens, int heads, int nsplit, void* hip_stream) {
+  if (tokens < 0 || heads < 1 || heads > SMLA_MAX_HEADS) return SMLA_ERR_DIM;
+  if (nsplit < 1 || nsplit > SMLA_MAX_NSPLIT) return SMLA_ERR_NSPLIT;
+  if (tokens == 0) return SMLA_OK;
+  if (!part_o || !part_lse || !out || !lse) return SMLA_ERR_NULL;
+  if (!aligned(part_o, 16) || !aligned(part_lse, 4) || !aligned(out, 16) || !aligned(lse, 4))
+    return SMLA_ERR_ALIGN;
+  if ((int64_t)tokens * heads > 0x7fffffffLL) return SMLA_ERR_DIM;
+  smla::CombineParams cp;
+  cp.part_o = part_o;
+  cp.part_lse = part_lse;
+  cp.out = (uint16_t*)out;
+  cp.lse = lse;
+  cp.tokens = tokens;
+  cp.heads = heads;
+  cp.nsplit = nsplit;
+  if (smla::launch_combine(cp, (hipStream_t)hip_stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return SMLA_ERR_LAUNCH;
+  }
+  return SMLA_OK;
+}
+
+SMLA_API const char* smla_status_str(int status) {
+  switch (status) {
+    case SMLA_OK: return "ok";
+    case SMLA_ERR_NULL: return "a required pointer is NULL";
+    case SMLA_ERR_DIM: return "invalid size (negative, zero heads, or above a limit)";
+    case SMLA_ERR_NSPLIT: return "nsplit out of range";
+    case SMLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case SMLA_ERR_ALIGN: return "pointer misaligned";
+    case SMLA_ERR_DEVICE: return "no usable device";
+    case SMLA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}

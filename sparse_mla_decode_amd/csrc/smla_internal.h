@@ -1,0 +1,44 @@
+// smla_internal.h -- parameter blocks shared by the C-ABI layer and the
+// gfx950 kernels.  Not part of the public interface (include/smla.h is).
+#ifndef SMLA_INTERNAL_H
+#define SMLA_INTERNAL_H
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smla {
+
+constexpr int kRow = 576;          // q / cache row width (bf16)
+constexpr int kDV = 512;           // value width (bf16)
+constexpr int kMaxNsplit = 1024;   // must equal SMLA_MAX_NSPLIT
+constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLog2e = 1.442695040888963407f;
+
+struct SplitParams {
+  const uint16_t* q;    // [T, H, 576] bf16 bits
+  const uint16_t* kv;   // [kv_rows, 576]
+  const int32_t* idx;   // [T, topk]
+  uint16_t* out;        // [T, H, 512] bf16 (nsplit == 1)
+  float* lse;           // [T, H]            (nsplit == 1)
+  float* part_o;        // [T, S, H, 512]    (nsplit > 1)
+  float* part_lse;      // [T, S, H]         (nsplit > 1)
+  int64_t kv_rows;
+  int tokens, heads, topk, nsplit, per_split;
+  float scale_log2;     // scale * log2(e): scores are kept in base 2
+};
+
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  uint16_t* out;
+  float* lse;
+  int tokens, heads, nsplit;
+};
+
+hipError_t launch_split(const SplitParams& p, hipStream_t st);
+hipError_t launch_combine(const CombineParams& p, hipStream_t st);
+int split_heads_per_block(int heads);
+
+}  // namespace smla
+
+#endif

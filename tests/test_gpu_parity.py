@@ -1,0 +1,130 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (oracle/compare.py): max-abs 1e-2 and relative L2 5e-3 on the bf16
+output, 1e-3 absolute on LSE, -inf/0 exactly where the selection is empty.
+
+Covered: the five workloads (tiny, long, batched, spec at three contexts,
+ragged, plus ragged with -1 padding) at the NSPLIT values the bench sweeps
+and the planner's choice; the large workloads run at full size on the GPU
+and are compared on sampled sequences the oracle computes one by one.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle.compare import check
+from tests.conftest import gpu_available
+from workloads import bf16_bits_to_f32, oracle_view, to_device, torch_to_bits, workload
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
+
+
+@pytest.fixture(scope="module")
+def smla():
+    import sparse_mla_decode_amd as m
+    return m
+
+
+def run_gpu(smla, dev, inp, nsplit, sync=True):
+    import torch
+    b, lq, h = inp.batch, inp.q_len, inp.heads
+    out = torch.empty((b, lq, h, 512), dtype=torch.bfloat16, device=dev["q"].device)
+    lse = torch.empty((b, lq, h), dtype=torch.float32, device=dev["q"].device)
+    used = smla.smla_decode(dev["q"], dev["kv"], dev["idx"], out, lse, inp.scale, nsplit)
+    if sync:
+        torch.cuda.synchronize()
+    return out, lse, used
+
+
+def host(out, lse):
+    return bf16_bits_to_f32(torch_to_bits(out)), lse.cpu().numpy()
+
+
+def assert_parity(out_g, lse_g, out_r, lse_r, what):
+    ok, m = check(out_g, lse_g, out_r, lse_r)
+    print(f"{what}: max_abs={m['max_abs']:.3g} rel_l2={m['rel_l2']:.3g} "
+          f"lse={m['lse_max_abs']:.3g} empty={m['empty']}", flush=True)
+    assert ok, f"{what}: {m['reasons']}"
+
+
+# ---------------------------------------------------------------- workloads
+
+@pytest.fixture(scope="module")
+def tiny(smla):
+    inp = workload("tiny")
+    dev = to_device(inp, "cuda")
+    ref = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
+    return inp, dev, ref
+
+
+@pytest.mark.parametrize("nsplit", [1, 4, 0, 2, 3, 5, 8, 127, 128, 200])
+def test_tiny(smla, tiny, nsplit):
+    inp, dev, (o_r, l_r) = tiny
+    out, lse, used = run_gpu(smla, dev, inp, nsplit)
+    o_g, l_g = host(out, lse)
+    assert_parity(o_g, l_g, o_r, l_r, f"tiny nsplit={nsplit} (used {used})")
+
+
+@pytest.fixture(scope="module")
+def long_ctx(smla):
+    inp = workload("long")
+    dev = to_device(inp, "cuda")
+    ref = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
+    return inp, dev, ref
+
+
+@pytest.mark.parametrize("nsplit", [1, 16, 64, 128, 0])
+def test_long(smla, long_ctx, nsplit):
+    inp, dev, (o_r, l_r) = long_ctx
+    out, lse, used = run_gpu(smla, dev, inp, nsplit)
+    o_g, l_g = host(out, lse)
+    assert_parity(o_g, l_g, o_r, l_r, f"long nsplit={nsplit} (used {used})")
+
+
+@pytest.mark.parametrize("ctx", [4096, 16384, 65536])
+@pytest.mark.parametrize("nsplit", [16, 64, 0])
+def test_spec(smla, ctx, nsplit):
+    inp = workload("spec", spec_ctx=ctx)
+    dev = to_device(inp, "cuda")
+    o_r, l_r = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
+    out, lse, used = run_gpu(smla, dev, inp, nsplit)
+    o_g, l_g = host(out, lse)
+    assert_parity(o_g, l_g, o_r, l_r, f"spec ctx={ctx} nsplit={nsplit} (used {used})")
+
+
+@pytest.fixture(scope="module")
+def batched(smla):
+    inp = workload("batched")
+    dev = to_device(inp, "cuda")
+    seqs = [0, 17, 42, 63]
+    q_s, kv_s, idx_s = oracle_view(inp, dev["kv"], seqs)
+    ref = oracle.decode(q_s, kv_s, idx_s, inp.scale)
+    return inp, dev, seqs, ref
+
+
+@pytest.mark.parametrize("nsplit", [0, 1, 2, 4, 8, 16])
+def test_batched_full_size_sampled(smla, batched, nsplit):
+    inp, dev, seqs, (o_r, l_r) = batched
+    out, lse, used = run_gpu(smla, dev, inp, nsplit)
+    o_g, l_g = host(out[seqs], lse[seqs])
+    assert_parity(o_g, l_g, o_r, l_r, f"batched nsplit={nsplit} (used {used}) seqs={seqs}")
+
+
+@pytest.mark.parametrize("pad", [False, True])
+def test_ragged_full_size_sampled(smla, pad):
+    import torch
+    inp = workload("ragged", ragged_pad=pad)
+    dev = to_device(inp, "cuda")
+    seqs = [0, 5, 15, 16, 77, 127]
+    q_s, kv_s, idx_s = oracle_view(inp, dev["kv"], seqs)
+    o_r, l_r = oracle.decode(q_s, kv_s, idx_s, inp.scale)
+    out, lse, used = run_gpu(smla, dev, inp, 0)
+    o_g, l_g = host(out[seqs], lse[seqs])
+    if pad:
+        assert (inp.idx[:16] == -1).any(), "padded workload must hold -1 entries"
+    assert_parity(o_g, l_g, o_r, l_r, f"ragged pad={pad} planner nsplit={used} seqs={seqs}")
+    del dev
+    torch.cuda.empty_cache()

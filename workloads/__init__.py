@@ -209,3 +209,51 @@ def compact_rows(idx: np.ndarray, kv_rows: int):
     idx2 = np.full(flat.shape, -1, np.int64)
     idx2[valid] = inv
     return rows, idx2.reshape(idx.shape).astype(np.int32)
+
+
+# ------------------------------------------------------------ device helpers
+
+def bits_to_torch(a: np.ndarray):
+    """uint16 bf16 bits -> torch.bfloat16 CPU tensor (same bytes)."""
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+def torch_to_bits(t) -> np.ndarray:
+    """torch.bfloat16 tensor (any device) -> uint16 numpy bits (same bytes)."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_device(inp: Inputs, device) -> dict:
+    """q, kv, idx of `inp` as device tensors (the pool is drawn on the device
+    when the host holds none)."""
+    import torch
+    q = bits_to_torch(inp.q).to(device)
+    if inp.kv is not None:
+        kv = bits_to_torch(inp.kv).to(device)
+    else:
+        kv = device_pool(inp.kv_rows, inp.pool_seed, device)
+    idx = torch.from_numpy(np.ascontiguousarray(inp.idx)).to(device)
+    return {"q": q, "kv": kv, "idx": idx}
+
+
+def oracle_view(inp: Inputs, kv_dev=None, seqs=None):
+    """Host copies of exactly what a call reads, for the CPU oracle.
+
+    seqs: sequence indices to keep (default all).  When the pool lives on the
+    device (or is large), only the rows the kept lists select are copied and
+    the lists are remapped onto them (masked entries stay masked).
+    Returns (q [b, Lq, H, 576] uint16, kv [U, 576] uint16, idx [b, Lq, K] int32).
+    """
+    import torch
+    sel = np.arange(inp.batch) if seqs is None else np.asarray(seqs)
+    q = inp.q[sel]
+    idx = inp.idx[sel]
+    if inp.kv is not None and inp.kv_rows <= (1 << 17):
+        return q, inp.kv, idx
+    rows, idx2 = compact_rows(idx, inp.kv_rows)
+    if inp.kv is not None:
+        return q, inp.kv[rows], idx2
+    r = torch.from_numpy(rows).to(kv_dev.device)
+    return q, torch_to_bits(kv_dev.index_select(0, r)), idx2

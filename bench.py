@@ -1,0 +1,317 @@
+#!/usr/bin/env python3
+"""Benchmark of sparse MLA decode (split-K over the top-k list) on one MI355X.
+
+One step = one smla_decode call (split kernel + LSE-combine kernel) over the
+workload's whole batch, i.e. one attention layer's decode.  Default workload:
+a single request at long context -- batch 1, q_len 1, 8 heads, top-2048 of a
+65536-row 576-wide bf16 latent cache -- with the planner's NSPLIT.
+
+Timing protocol
+  * inputs are resident in HBM before timing; successive steps rotate over
+    (cache, index set) pairs whose distinct gathered rows exceed 512 MB (2x
+    the Infinity Cache), so every step gathers rows from HBM (--warm turns the
+    rotation off: a cache-resident figure, never an HBM one);
+  * steps/s: W warm-up steps, then K steps replayed from a HIP graph that
+    holds one rotation cycle, bracketed by device synchronisation;
+  * per-kernel durations: an eager loop with HIP events recorded around each
+    launch on the launch stream, queued behind a spin kernel so that host
+    enqueue time cannot leak into the measured intervals;
+  * roofline: gathered-KV bytes of one split launch (valid list entries x
+    1152 B) / the split kernel's mean duration, against 8 TB/s HBM3E;
+  * cpu_baseline: the fp64 oracle, as is, on the host cores, over a bounded
+    sample of the same workload, scaled to steps/s.
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode steps/s + gathered-KV HBM GB/s (% of roofline), sparse MLA topk=2048"
+HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+ROW_BYTES = 1152
+KERNEL_SRC = os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", "smla_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+DESCRIPTIONS = {
+    "tiny": "batch 1, q_len 1, 8 heads, top-128 of a 1024-row cache",
+    "long": "batch 1, q_len 1, 8 heads, top-2048 of a 65536-row cache (single request, long context)",
+    "batched": "batch 64, q_len 1, 64 heads, top-2048 per sequence, 32768-token contexts in a paged pool of 32768 x 64-token pages",
+    "spec": "batch 1, q_len 9 (9 verify tokens with their own lists), 8 heads, top-2048 of a {ctx}-row cache",
+    "ragged": "batch 128, q_len 1, 128 heads, top-2048 per sequence, contexts uniform in [2048, 131072], paged 64-token pages",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_sha() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2048)
+    ap.add_argument("--warmup", type=int, default=64)
+    ap.add_argument("--workload", default="long", choices=["tiny", "long", "batched", "spec", "ragged"])
+    ap.add_argument("--spec-ctx", type=int, default=65536)
+    ap.add_argument("--nsplit", type=int, default=0, help="0 = the planner's choice")
+    ap.add_argument("--warm", action="store_true", help="no input rotation (cache-resident figure)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="CPU time budget of the oracle baseline (0 = skip)")
+    ap.add_argument("--kernel-steps", type=int, default=512, help="steps of the per-kernel event loop")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy (counter calibration) and exit")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    import sparse_mla_decode_amd as smla
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t_setup = time.time()
+    inp = wl.workload(args.workload, spec_ctx=args.spec_ctx, with_kv=False)
+    B, Lq, H, K = inp.batch, inp.q_len, inp.heads, inp.topk
+    T = B * Lq
+    if args.warm:
+        n_caches, sets = 1, [inp.idx]
+    else:
+        n_caches, sets = wl.rotation(inp)
+    log(f"[bench] workload={args.workload} B={B} Lq={Lq} H={H} K={K} kv_rows={inp.kv_rows} "
+        f"caches={n_caches} index_sets={len(sets)}")
+
+    q = wl.bits_to_torch(inp.q).to(dev)
+    caches = [wl.device_pool(inp.kv_rows, (inp.pool_seed or 0) + 1000 * c, dev) for c in range(n_caches)]
+    idx_sets = [torch.from_numpy(np.ascontiguousarray(s)).to(dev) for s in sets]
+    nsplit = args.nsplit if args.nsplit > 0 else smla.smla_plan_nsplit(B, Lq, H, K)
+    ws = smla.workspace(B, Lq, H, nsplit, dev)
+    out = torch.empty((B, Lq, H, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, Lq, H), dtype=torch.float32, device=dev)
+    n_rot = n_caches * len(sets)
+    valid_rows = [int((s >= 0).sum()) for s in sets]   # every index set points inside its cache
+    kv_bytes_step = [v * ROW_BYTES for v in valid_rows]
+
+    def step(i, stream=None):
+        c = caches[i % n_caches]
+        ix = idx_sets[(i // n_caches) % len(sets)]
+        smla.smla_decode(q, c, ix, out, lse, inp.scale, nsplit, ws, stream)
+
+    torch.cuda.synchronize()
+    log(f"[bench] setup {time.time() - t_setup:.1f}s nsplit={nsplit} rotation={n_rot} steps")
+
+    # ---- warm-up (eager), then capture one rotation cycle in a HIP graph
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    g_stream = torch.cuda.Stream()
+    g_stream.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(g_stream):
+        with torch.cuda.graph(graph, stream=g_stream):
+            for i in range(n_rot):
+                step(i)
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps from graph replays (whole rotation cycles)
+    reps = max(1, -(-args.steps // n_rot))
+    steps = reps * n_rot
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms_total = t0.elapsed_time(t1)
+    ms_per_step = ms_total / steps
+    steps_per_s = 1000.0 / ms_per_step
+    mean_kv_bytes = sum(kv_bytes_step[(i // n_caches) % len(sets)] for i in range(n_rot)) / n_rot
+    log(f"[bench] graph: {steps} steps in {ms_total:.3f} ms -> {ms_per_step * 1e3:.2f} us/step")
+
+    # ---- per-kernel durations (a): each kernel alone, one rotation cycle of
+    # back-to-back launches per HIP graph, timed with events around replays
+    def graph_of(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(g_stream):
+            with torch.cuda.graph(g, stream=g_stream):
+                for i in range(n_rot):
+                    fn(i)
+        return g
+
+    def split_only(i):
+        c = caches[i % n_caches]
+        ix = idx_sets[(i // n_caches) % len(sets)]
+        smla.smla_split(q, c, ix, out, lse, inp.scale, nsplit, ws)
+
+    part = smla.partials_view(ws, B, Lq, H, nsplit) if nsplit > 1 else None
+
+    def combine_only(i):
+        smla.smla_combine(part[0], part[1], out, lse)
+
+    def time_graph(g, reps):
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / (reps * n_rot)
+
+    kreps = max(1, -(-args.kernel_steps // n_rot))
+    split_us = time_graph(graph_of(split_only), kreps)
+    comb_us = time_graph(graph_of(combine_only), kreps) if nsplit > 1 else 0.0
+    kv_split = mean_kv_bytes
+
+    # ---- per-kernel durations (b), diagnostic: events bracketing each eager
+    # launch, queued behind a spin kernel so host enqueue time cannot leak in
+    ks = min(args.kernel_steps, 4 * n_rot)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ks)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(200_000_000)
+    for i in range(ks):
+        ev[i][0].record()
+        split_only(i)
+        ev[i][1].record()
+        if nsplit > 1:
+            combine_only(i)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    ev_split_us = 1e3 * float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    ev_comb_us = 1e3 * float(np.mean([e[1].elapsed_time(e[2]) for e in ev])) if nsplit > 1 else 0.0
+    eager_us = 1e3 * (ev[0][0].elapsed_time(ev[-1][2])) / ks
+    log(f"[bench] kernels (graph, per launch): split {split_us:.2f} us, combine {comb_us:.2f} us; "
+        f"(event-bracketed: split {ev_split_us:.2f} us, combine {ev_comb_us:.2f} us, eager step {eager_us:.2f} us)")
+
+    flops = T * H * K * 2 * (576 + 512) * (valid_rows[0] / max(1, T * K))
+    achieved = kv_split / (split_us * 1e-6) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE)).get(args.workload if args.workload != "spec" else f"spec{args.spec_ctx}")
+        if rec and rec.get("kernel_sha") == kernel_sha() and rec.get("nsplit") == nsplit and not args.warm:
+            traffic = rec.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(steps_per_s, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{args.workload}: " + DESCRIPTIONS[args.workload].format(ctx=args.spec_ctx),
+            "batch": B, "q_len": Lq, "heads": H, "topk": K, "kv_rows": inp.kv_rows,
+            "nsplit": nsplit, "nsplit_from": "planner" if args.nsplit == 0 else "argument",
+            "cache_state": "warm (no rotation)" if args.warm else
+                           f"cold: rotation over {n_caches} caches x {len(sets)} disjoint index sets",
+            "timing": "HIP graph replay of whole rotation cycles",
+        },
+        "gathered_kv_gbps_per_step": round(mean_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "kernels_us": {"split": round(split_us, 3), "combine": round(comb_us, 3),
+                       "method": "graph of back-to-back launches of one kernel, events around replays",
+                       "event_bracketed_split": round(ev_split_us, 3),
+                       "event_bracketed_combine": round(ev_comb_us, 3),
+                       "eager_step": round(eager_us, 3)},
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "split_kernel (gather + QK^T + online softmax + PV)",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "bytes_per_launch": int(kv_split),
+        },
+        "mfma": {"achieved_tflops": round(flops / (split_us * 1e-6) / 1e12, 3),
+                 "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+                 "frac": round(flops / (split_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
+        "kernel_sha": kernel_sha(),
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(inp, caches[0], torch.from_numpy(sets[0]), args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(inp, kv_dev, idx0, seconds):
+    """The fp64 oracle, as is, on a bounded sample of the workload: whole
+    sequences of the first index set, added until `seconds` of CPU work are
+    spent, scaled to steps/s of the whole batch."""
+    import dataclasses
+
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    inp0 = dataclasses.replace(inp, idx=idx0.numpy())
+    T_seq = inp.batch
+    done_seqs, elapsed = 0, 0.0
+    threads = oracle.threads()
+    used = 0
+    b = 0
+    while elapsed < seconds:
+        q_s, kv_s, idx_s = wl.oracle_view(inp0, kv_dev, [b % T_seq])
+        t0 = time.perf_counter()
+        oracle.decode(q_s, kv_s, idx_s, inp.scale)
+        elapsed += time.perf_counter() - t0
+        used = max(used, min(threads, inp.q_len * inp.heads))
+        done_seqs += 1
+        b += 1
+    steps_per_s = (done_seqs / T_seq) / elapsed
+    return {"value": round(steps_per_s, 4), "unit": "steps/s", "cores": used, "kind": "oracle",
+            "sample": f"{done_seqs} sequence(s) x {inp.q_len} token(s) x {inp.heads} heads of the first "
+                      f"index set in {elapsed:.1f} s of fp64 oracle work, scaled to the {T_seq}-sequence step",
+            "host_threads_available": threads}
+
+
+if __name__ == "__main__":
+    main()

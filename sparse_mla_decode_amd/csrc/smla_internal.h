@@ -13,6 +13,9 @@ constexpr int kDV = 512;           // value width (bf16)
 constexpr int kMaxNsplit = 1024;   // must equal SMLA_MAX_NSPLIT
 constexpr float kLn2 = 0.693147180559945309f;
 constexpr float kLog2e = 1.442695040888963407f;
+// the running max of a head moves only when a tile max exceeds it by this
+// much (base-2 exponent), bounding the unnormalised weights by 2^8
+constexpr float kRescaleLog2 = 8.0f;
 
 struct SplitParams {
   const uint16_t* q;    // [T, H, 576] bf16 bits

@@ -32,30 +32,30 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "smla_internal.h"
 
 namespace smla {
 
+// Native clang vectors throughout: arrays of them stay in registers (HIP's
+// uint4/float4 are class types that keep loop-carried arrays on the stack).
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kRowGran = kRow * 2 / 16;          // 72 16-byte granules per row
 constexpr int kKSteps = kRow / 32;               // 18 MFMA K-steps over 576 columns
 
 // Row read for masked list entries: all zeros, so masked rows add exactly
 // nothing to P*V (and never carry non-finite stale data).
-__device__ __attribute__((aligned(16))) uint4 g_zero_row[kRowGran];
+__device__ __attribute__((aligned(16))) u32x4 g_zero_row[kRowGran];
 
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
-
-// LDS row pitch: 1152 bytes of row + 16 of padding.  The pad shifts each row
-// by one 16-byte bank group, so the 16 rows one MFMA operand read touches
-// land in distinct banks (a bare 1152-byte pitch is a multiple of the bank
-// span), and every operand address is a per-lane base plus a constant.
-constexpr int kPitch = kRow * 2 + 16;
-__device__ __forceinline__ int tile_off(int j, int k) { return j * kPitch + k * 16; }
 
 __device__ __forceinline__ bool row_ok(int32_t r, int64_t kv_rows) {
   return r >= 0 && (int64_t)r < kv_rows;
@@ -70,29 +70,70 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return (uint32_t)ux | ((uint32_t)uy << 16);
 }
 
+// Tile layout in LDS: the row is cut into 9 blocks of 8 granules (16 bytes
+// each, 128 bytes per block); block kb of all TR rows is stored together,
+// 128 bytes per row, and inside a row's 128 bytes granule c sits at
+// c ^ h(j), h(j) = 2*(j % 4) + (j / 4) % 2:
+//     slot(j, k) = (k / 8) * TR * 8 + j * 8 + ((k % 8) ^ h(j))
+//   * an LDS-DMA wave instruction fills 64 consecutive slots = 8 rows x one
+//     full 128-byte line each (coalesced), and every lane keeps one or two
+//     fixed tile rows for all loads of a tile;
+//   * the QK^T operand read (granule k of 16 rows) hits 8 distinct bank
+//     groups in each group of 8 rows (h is a bijection on 8 rows);
+//   * the V^T transpose read (granules 2cb and 2cb+1 of rows 4g..4g+3) hits
+//     all 16 eight-byte bank slots once (h(4g + e) differs in bits 1-2).
+// All operand addresses are a few per-lane bases plus constants.
+__device__ __forceinline__ int hsw(int j) { return ((j & 3) << 1) | ((j >> 2) & 1); }
+
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+
+// LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, output
+// lane i, element e receives element i % 4 of the 8 bytes addressed by lane
+// 4 * e + i / 4 of the same group.
+__device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) shortx4*)(__attribute__((address_space(3))) uint8_t*)p);
+}
+
+constexpr int kListCap = 2048;  // list entries staged in LDS at a time
+
 // ---------------------------------------------------------------------------
 // Split kernel.  HG head groups of 16 per workgroup, NCS column slices of the
 // 512 value columns per head group, one wave per (head group, column slice).
 // Every wave computes S for its head group; the PV work and the O
 // accumulators are divided among the NCS waves that share a head group.
-// TR rows per LDS tile; each thread moves TR*72/threads granules per tile.
+// TR rows per tile, NBUF tile buffers: NBUF-1 tiles are in flight while one
+// is computed.
 // ---------------------------------------------------------------------------
-template <int HG, int NCS, int TR>
+template <int HG, int NCS, int TR, int NBUF>
 __global__ __launch_bounds__(64 * HG * NCS) __attribute__((amdgpu_waves_per_eu(2)))
 void split_kernel(SplitParams p) {
-  constexpr int kThreads = 64 * HG * NCS;
-  constexpr int kTileRows = TR;
-  constexpr int RB = TR / 16;                      // 16-row blocks per tile
-  constexpr int KP = TR / 32;                      // 32-row K-steps of PV per tile
-  constexpr int kTileGran = kTileRows * kRowGran;
-  constexpr int kLoadsPerThread = kTileGran / kThreads;
-  constexpr int kTileBytes = kTileRows * kPitch;
-  constexpr int CB = (kDV / 16) / NCS;  // 16-column blocks of O per wave
-  static_assert(kTileGran % kThreads == 0, "tile must split evenly over the threads");
-  static_assert(TR % 32 == 0, "tile rows must be a multiple of the PV K-step");
+  constexpr int NT = 64 * HG * NCS;
+  constexpr int RB = TR / 16;                 // 16-row blocks per tile (QK^T M blocks)
+  constexpr int KP = TR / 32;                 // 32-row K-steps of PV per tile
+  constexpr int L = TR * kRowGran / NT;       // DMA instructions per thread per tile
+  constexpr int kTileBytes = TR * kRow * 2;
+  constexpr int kRowBytes = kRow * 2;
+  constexpr int CB = (kDV / 16) / NCS;        // 16-column blocks of O per wave
+  static_assert(TR * kRowGran % NT == 0, "tile must split evenly over the threads");
+  static_assert(TR % 32 == 0 && NBUF >= 2 && NBUF <= 3, "tile shape");
+  static_assert(L * (NBUF - 2) < 64, "vmcnt range");
 
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][kTileBytes];
-  __shared__ int tile_valid[2][kTileRows];
+  // One __shared__ object per buffer: each access below names its buffer at
+  // compile time, which lets the compiler see that a read of one buffer does
+  // not alias the LDS-DMA writes in flight into another (otherwise it waits
+  // for every outstanding load before each LDS read).
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tb2[NBUF > 2 ? kTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) int list_s[kListCap];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -113,57 +154,49 @@ void split_kernel(SplitParams p) {
   const bool h_ok = h < p.heads;
 
   // Q^T as the B operand of S^T = KV * Q^T: lane (g, l16) holds
-  // q[h][32*ks + 8*g .. +7] for every K-step ks (zeros for padding heads).
+  // q[h][32*ks + 8*g .. +7] for every K-step ks (zeros for padding heads,
+  // read from the zero row: 72 granules cover 18 K-steps x 4 groups).
   bf16x8 qb[kKSteps];
   {
-    const uint16_t* qrow = p.q + ((int64_t)tok * p.heads + (h_ok ? h : 0)) * kRow + g * 8;
+    const u32x4* qrow = h_ok ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + h) * kRow) + g
+                             : g_zero_row + g;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
-      uint4 v = h_ok ? *(const uint4*)(qrow + ks * 32) : make_uint4(0, 0, 0, 0);
-      qb[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int ks = 0; ks < kKSteps; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, qrow[ks * 4]);
   }
 
-  // this split's slice of the list
-  const int lo = min(split * p.per_split, p.topk);
-  const int hi = min(lo + p.per_split, p.topk);
-  const int ntiles = (hi - lo + kTileRows - 1) / kTileRows;
-  const int32_t* idx_row = p.idx + (int64_t)tok * p.topk;
+  // QK^T operand: row 16*rb + l16, granule 4*ks + g, i.e. block ks/2 and
+  // in-block granule (4*(ks&1) + g) ^ h(l16) = (g ^ h) ^ 4*(ks&1).
+  const int hq = hsw(l16);
+  const int qk_even = l16 * 128 + (g ^ hq) * 16;
+  const int qk_odd = l16 * 128 + ((g ^ hq) ^ 4) * 16;
+  // V^T transpose read: source lane (e, s') of group g reads row 4g + e
+  // (+16 for slots 4-7, +32 per PV K-step), columns 16*cb + 4s' .. +3 =
+  // granule 2cb + b0 (b0 = s' >> 1) at byte 8*b1 (b1 = s' & 1); in-block
+  // granule (2*(cb%4) + b0) ^ h(4g + e) = 2*((cb%4) ^ e) + (b0 ^ (g&1)).
+  const int tr_e = l16 >> 2, tr_b0 = (l16 >> 1) & 1, tr_b1 = l16 & 1;
+  int pv_base[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    pv_base[c] = (4 * g + tr_e) * 128 + (2 * (c ^ tr_e) + (tr_b0 ^ (g & 1))) * 16 + 8 * tr_b1;
 
-  // Gather slots: thread tid moves granules q = it*256 + tid of a tile,
-  // i.e. row j = q / 72, granule k = q % 72.
-  int rows_cur[kLoadsPerThread];
-  int rows_next[kLoadsPerThread];
-  uint4 stage[kLoadsPerThread];
-
-  auto load_rows = [&](int t, int (&rows)[kLoadsPerThread]) {
+  // DMA: wave instruction it fills slots 64*m .. 64*m + 63, m = it*WPB + wave
+  // (WPB = waves per workgroup): block kb = m / RG, rows 8*(m % RG) + lane/8
+  // (RG = TR/8 row groups per block), in-block slot lane % 8, which holds
+  // granule (lane % 8) ^ h(row).  If RG >= WPB a lane cycles through
+  // DP = RG / WPB rows (d = it % DP, kb = it / DP); otherwise it keeps one
+  // row and kb = it * (WPB / RG) + wave / RG.
+  constexpr int WPB = NT / 64;
+  constexpr int RG = TR / 8;
+  static_assert(RG % WPB == 0 || WPB % RG == 0, "row period");
+  constexpr int DP = RG > WPB ? RG / WPB : 1;
+  int dma_row[DP], dma_gran[DP];
 #pragma unroll
-    for (int it = 0; it < kLoadsPerThread; ++it) {
-      const int j = (it * kThreads + tid) / kRowGran;
-      const int e = lo + t * kTileRows + j;
-      rows[it] = e < hi ? idx_row[e] : -1;
-    }
-  };
-  auto issue = [&](const int (&rows)[kLoadsPerThread]) {
-#pragma unroll
-    for (int it = 0; it < kLoadsPerThread; ++it) {
-      const int k = (it * kThreads + tid) % kRowGran;
-      const int32_t r = rows[it];
-      const uint4* src = row_ok(r, p.kv_rows)
-                             ? (const uint4*)(p.kv + (int64_t)r * kRow) + k
-                             : g_zero_row + k;
-      stage[it] = *src;
-    }
-  };
-  auto commit = [&](int buf, const int (&rows)[kLoadsPerThread]) {
-#pragma unroll
-    for (int it = 0; it < kLoadsPerThread; ++it) {
-      const int q = it * kThreads + tid;
-      const int j = q / kRowGran, k = q % kRowGran;
-      *(uint4*)(&tile[buf][tile_off(j, k)]) = stage[it];
-      if (k == 0) tile_valid[buf][j] = row_ok(rows[it], p.kv_rows);
-    }
-  };
+  for (int d = 0; d < DP; ++d) {
+    const int m = d * WPB + wave;
+    dma_row[d] = 8 * (m % RG) + (lane >> 3);
+    dma_gran[d] = (lane & 7) ^ hsw(dma_row[d]);
+    if (DP == 1) dma_gran[d] += 8 * (wave / RG);
+  }
 
   float m_run = -__builtin_inff();  // running max of log2-scaled scores (per head)
   float l_run = 0.f;                // this lane's share of the running sum
@@ -171,68 +204,91 @@ void split_kernel(SplitParams p) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) oacc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  if (ntiles > 0) {
-    load_rows(0, rows_cur);
-    issue(rows_cur);
-    if (ntiles > 1) load_rows(1, rows_next);
-  }
+  const int lo = min(split * p.per_split, p.topk);
+  const int hi = min(lo + p.per_split, p.topk);
+  const int32_t* idx_row = p.idx + (int64_t)tok * p.topk;
 
-  for (int n = 0; n < ntiles; ++n) {
-    const int buf = n & 1;
-    commit(buf, rows_cur);
-    __syncthreads();
-    if (n + 1 < ntiles) {
+  // LDS-DMA loads of tile t (list entries t*TR.. of the staged chunk); a
+  // masked entry (or one past the chunk) loads the zero row.
+  auto issue = [&](uint8_t* buf, int t, int n_ent) __attribute__((always_inline)) {
+    const u32x4* src[DP];
 #pragma unroll
-      for (int it = 0; it < kLoadsPerThread; ++it) rows_cur[it] = rows_next[it];
-      issue(rows_cur);
-      if (n + 2 < ntiles) load_rows(n + 2, rows_next);
+    for (int d = 0; d < DP; ++d) {
+      const int e = t * TR + dma_row[d];          // < kListCap: inside list_s
+      const int32_t r = e < n_ent ? list_s[e] : -1;
+      const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
+      src[d] = (const u32x4*)(row_ok(r, p.kv_rows) ? hit : (uintptr_t)g_zero_row) + dma_gran[d];
     }
-
-    const uint8_t* T = tile[buf];
-
-    // ---- S^T = KV_tile * Q^T: RB 16-row blocks, 18 K-steps of 32 columns
-    floatx4 sacc[RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb) sacc[rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int it = 0; it < L; ++it) {
+      constexpr int kStep = DP > 1 ? 0 : WPB / RG;
+      const int kb = DP > 1 ? it / DP : it * kStep;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[it % DP] + 8 * kb),
+          (__attribute__((address_space(3))) void*)(buf + (it * NT + wave * 64) * 16), 16, 0, 0);
+    }
+  };
+
+  // Consume tile t held in T.
+  auto compute = [&](const uint8_t* T, int t, int n_ent) __attribute__((always_inline)) {
+    // ---- S^T = KV_tile * Q^T: RB 16-row blocks, 18 K-steps of 32 columns;
+    // with fewer than four row blocks, even and odd K-steps accumulate
+    // separately so that enough independent MFMAs are in flight
+    constexpr int CH = RB >= 4 ? 1 : 2;
+    floatx4 sacc[RB][CH];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+      for (int c = 0; c < CH; ++c) sacc[rb][c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int j = rb * 16 + l16;
-        const bf16x8 a = *(const bf16x8*)(T + tile_off(j, ks * 4 + g));
-        sacc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], sacc[rb], 0, 0, 0);
+        const int off = ((ks & 1) ? qk_odd : qk_even) + (ks >> 1) * TR * 128 + rb * 16 * 128;
+        const bf16x8 a = *(const bf16x8*)(T + off);
+        sacc[rb][ks % CH] =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], sacc[rb][ks % CH], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- online softmax; lane holds rows j = 16*rb + 4*g + i of head h
     float s[4 * RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int rb = 0; rb < RB; ++rb) {
+      const int e0 = t * TR + rb * 16 + 4 * g;
+      const i32x4 r4 = *(const i32x4*)(list_s + e0);
+      floatx4 sc = sacc[rb][0];
+#pragma unroll
+      for (int c = 1; c < CH; ++c) sc += sacc[rb][c];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int j = rb * 16 + 4 * g + i;
-        s[rb * 4 + i] = tile_valid[buf][j] ? sacc[rb][i] * p.scale_log2 : -__builtin_inff();
+        const bool ok = (e0 + i < n_ent) && row_ok(r4[i], p.kv_rows);
+        s[rb * 4 + i] = ok ? sc[i] * p.scale_log2 : -__builtin_inff();
       }
+    }
     float tmax = s[0];
 #pragma unroll
     for (int i = 1; i < 4 * RB; ++i) tmax = fmaxf(tmax, s[i]);
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
     tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float m_use = m_new == -__builtin_inff() ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    float psum = 0.f;
+    // Lazy rescaling: the running max only moves when a head's tile max
+    // exceeds it by more than 2^8 (in base 2), so O and l are rescaled
+    // rarely; meanwhile the weights exp2(s - m) stay below 2^8.
+    if (__any(tmax > m_run + kRescaleLog2)) {
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
+      l_run *= alpha;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
     float pv[4 * RB];
 #pragma unroll
     for (int i = 0; i < 4 * RB; ++i) {
       pv[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-      psum += pv[i];
+      l_run += pv[i];
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
 
     // P^T as the B operand of K-step kp: K slot s <-> tile row
     // 32*kp + 16*(s/4) + 4*g + s%4, i.e. the rows this lane already holds.
@@ -240,32 +296,68 @@ void split_kernel(SplitParams p) {
 #pragma unroll
     for (int kp = 0; kp < KP; ++kp) {
       const float* v = pv + 8 * kp;
-      const uint4 pw = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                                  pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7]));
+      const u32x4 pw = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
       pb[kp] = __builtin_bit_cast(bf16x8, pw);
     }
 
-    // ---- O^T += V^T * P^T; A operand: V[row(s)][c], c = column of this lane
+    // ---- O^T += V^T * P^T; the A operand (V^T, tile rows on K) comes from
+    // two transpose reads: slots 0-3 = rows 4g..4g+3, slots 4-7 = rows
+    // 16+4g..16+4g+3 of the K-step, column l16 of the 16-column block.
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
-      const int c = (cs * CB + cb) * 16 + l16;
+      const int cbg = cs * CB + cb;  // 16-column block within the 512
 #pragma unroll
       for (int kp = 0; kp < KP; ++kp) {
-        uint16_t av[8];
-#pragma unroll
-        for (int sl = 0; sl < 8; ++sl) {
-          const int j = 32 * kp + 16 * (sl >> 2) + 4 * g + (sl & 3);
-          av[sl] = *(const uint16_t*)(T + j * kPitch + c * 2);
-        }
-        const uint4 aw = make_uint4((uint32_t)av[0] | ((uint32_t)av[1] << 16),
-                                    (uint32_t)av[2] | ((uint32_t)av[3] << 16),
-                                    (uint32_t)av[4] | ((uint32_t)av[5] << 16),
-                                    (uint32_t)av[6] | ((uint32_t)av[7] << 16));
-        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, aw),
+        const int off = pv_base[cbg & 3] + (cbg >> 2) * TR * 128 + 32 * kp * 128;
+        const shortx4 v_lo = lds_tr16(T + off);
+        const shortx4 v_hi = lds_tr16(T + off + 16 * 128);
+        const shortx4 a8[2] = {v_lo, v_hi};
+        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8),
                                                            pb[kp], oacc[cb], 0, 0, 0);
       }
-      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+
+  // Software pipeline over the tiles of each staged chunk of the list.
+  for (int clo = lo; clo < hi; clo += kListCap) {
+    const int n_ent = min(hi - clo, kListCap);
+    {
+      // stage the chunk in one memory round trip: all loads, then all stores
+      constexpr int LI = kListCap / NT;
+      int v[LI];
+#pragma unroll
+      for (int u = 0; u < LI; ++u) v[u] = idx_row[clo + min(u * NT + tid, n_ent - 1)];
+#pragma unroll
+      for (int u = 0; u < LI; ++u)
+        if (u * NT + tid < n_ent) list_s[u * NT + tid] = v[u];
+    }
+    // every earlier load (q, the list) has landed before the tile loads start,
+    // so the only loads in flight inside the loop are the tile loads
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int ntiles = (n_ent + TR - 1) / TR;
+    issue(tb0, 0, n_ent);
+    if (NBUF > 2 && ntiles > 1) issue(tb1, 1, n_ent);
+    // one pipeline step on buffer b (a compile-time constant)
+    auto step = [&](auto bconst, int n) __attribute__((always_inline)) {
+      constexpr int b = decltype(bconst)::value;
+      constexpr int bn = (b + NBUF - 1) % NBUF;
+      // tile n landed (with three buffers, tile n+1 may still be in flight)
+      if (NBUF > 2 && n + 1 < ntiles) wait_vmcnt<L * (NBUF - 2)>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      // refill the buffer every wave finished with in the previous step
+      if (n + NBUF - 1 < ntiles) issue(bn == 0 ? tb0 : bn == 1 ? tb1 : tb2, n + NBUF - 1, n_ent);
+      compute(b == 0 ? tb0 : b == 1 ? tb1 : tb2, n, n_ent);
+    };
+    for (int n0 = 0; n0 < ntiles; n0 += NBUF) {
+      step(std::integral_constant<int, 0>{}, n0);
+      if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
+      if constexpr (NBUF > 2)
+        if (n0 + 2 < ntiles) step(std::integral_constant<int, 2>{}, n0 + 2);
+    }
+    __syncthreads();  // list_s and the buffers are reused by the next chunk
   }
 
   // ---- epilogue: O / l and LSE = (m * ln 2) + ln l
@@ -283,7 +375,7 @@ void split_kernel(SplitParams p) {
     for (int cb = 0; cb < CB; ++cb) {
       const int c0 = (cs * CB + cb) * 16 + 4 * g;
       const floatx4 o = oacc[cb] * inv;
-      *(uint2*)(orow + c0) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
+      *(u32x2*)(orow + c0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
     }
     if (g == 0 && cs == 0) p.lse[th] = lse_v;
   } else {
@@ -292,46 +384,49 @@ void split_kernel(SplitParams p) {
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb) {
       const int c0 = (cs * CB + cb) * 16 + 4 * g;
-      const floatx4 o = oacc[cb] * inv;
-      *(float4*)(orow + c0) = make_float4(o[0], o[1], o[2], o[3]);
+      *(floatx4*)(orow + c0) = oacc[cb] * inv;
     }
     if (g == 0 && cs == 0) p.part_lse[slot] = lse_v;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Combine kernel ([SPLITK] "The Split-K Imperative").  One workgroup per
-// (token, head); 128 threads cover the 512 columns as float4, and SG such
-// groups take interleaved splits before an LDS reduction.
+// Combine kernel ([SPLITK] "The Split-K Imperative").  Workgroup = (token,
+// head, quarter of the 512 columns): 32 threads cover the quarter in 4-float
+// and SG groups of them take interleaved splits; each thread issues all of
+// its partial-O loads before any arithmetic (a chain of dependent loads would
+// cost one cache round trip per split), then an LDS reduction over the groups.
 // ---------------------------------------------------------------------------
-template <int SG>
-__global__ __launch_bounds__(128 * SG) void combine_kernel(CombineParams p) {
-  constexpr int NT = 128 * SG;
+constexpr int kCombCols = 128;               // columns per workgroup
+constexpr int kCombC4 = kCombCols / 4;       // 4-float lanes per split group
+
+template <int SG, int PER>
+__global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) {
+  constexpr int NT = kCombC4 * SG;
   __shared__ float w_s[kMaxNsplit];
-  __shared__ float red[NT / 64];
-  __shared__ float4 acc_s[SG > 1 ? SG - 1 : 1][128];
+  __shared__ float red[2][(NT + 63) / 64];
+  __shared__ floatx4 acc_s[SG][kCombC4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int tok = blockIdx.x / p.heads;
-  const int h = blockIdx.x % p.heads;
+  const int quarter = blockIdx.x & 3;
+  const int th_id = blockIdx.x >> 2;          // token * heads + head
+  const int tok = th_id / p.heads;
+  const int h = th_id % p.heads;
   const int S = p.nsplit;
   const float* lse_in = p.part_lse + (int64_t)tok * S * p.heads + h;
 
-  // M = max_s LSE_s
+  // M = max_s LSE_s and W = sum_s exp(LSE_s - M), both block-wide
   float mx = -__builtin_inff();
   for (int s = tid; s < S; s += NT) mx = fmaxf(mx, lse_in[(int64_t)s * p.heads]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if (lane == 0) red[wave] = mx;
+  if (lane == 0) red[0][wave] = mx;
   __syncthreads();
-  mx = red[0];
+  mx = red[0][0];
 #pragma unroll
-  for (int w = 1; w < NT / 64; ++w) mx = fmaxf(mx, red[w]);
-  __syncthreads();
-
-  // w_s = exp(LSE_s - M); W = sum_s w_s
+  for (int w = 1; w < (NT + 63) / 64; ++w) mx = fmaxf(mx, red[0][w]);
   float ws = 0.f;
   for (int s = tid; s < S; s += NT) {
     const float l = lse_in[(int64_t)s * p.heads];
@@ -343,82 +438,84 @@ __global__ __launch_bounds__(128 * SG) void combine_kernel(CombineParams p) {
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o, 64);
-  if (lane == 0) red[wave] = ws;
+  if (lane == 0) red[1][wave] = ws;
   __syncthreads();
   float wsum = 0.f;
 #pragma unroll
-  for (int w = 0; w < NT / 64; ++w) wsum += red[w];
+  for (int w = 0; w < (NT + 63) / 64; ++w) wsum += red[1][w];
 
-  // sum_s w_s O_s over this thread's splits
-  const int c4 = tid % 128;
-  const int sg = tid / 128;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  const float* o_in = p.part_o + ((int64_t)tok * S * p.heads + h) * kDV + c4 * 4;
-  for (int s = sg; s < S; s += SG) {
-    const float w = w_s[s];
-    if (w != 0.f) {
-      const float4 v = *(const float4*)(o_in + (int64_t)s * p.heads * kDV);
-      acc.x += w * v.x;
-      acc.y += w * v.y;
-      acc.z += w * v.z;
-      acc.w += w * v.w;
+  // sum_s w_s O_s over this thread's splits, PER loads in flight at a time
+  const int c4 = tid % kCombC4;
+  const int sg = tid / kCombC4;
+  const int col = quarter * kCombCols + c4 * 4;
+  const float* o_in = p.part_o + ((int64_t)tok * S * p.heads + h) * kDV + col;
+  const int64_t stride = (int64_t)p.heads * kDV;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg; s0 < S; s0 += SG * PER) {
+    floatx4 v[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int s = s0 + u * SG;
+      v[u] = s < S ? *(const floatx4*)(o_in + s * stride) : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int s = s0 + u * SG;
+      const float w = s < S ? w_s[s] : 0.f;
+      // a zero weight (empty split) contributes nothing, whatever its slot holds
+      if (w != 0.f) acc += w * v[u];
     }
   }
   if (SG > 1) {
-    if (sg > 0) acc_s[sg - 1][c4] = acc;
+    acc_s[sg][c4] = acc;
     __syncthreads();
     if (sg == 0) {
 #pragma unroll
-      for (int i = 0; i < SG - 1; ++i) {
-        const float4 v = acc_s[i][c4];
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
-      }
+      for (int i = 1; i < SG; ++i) acc += acc_s[i][c4];
     }
   }
   if (sg != 0) return;
   const bool any = wsum > 0.f;
   const float inv = any ? 1.f / wsum : 0.f;
   const int64_t th = (int64_t)tok * p.heads + h;
-  *(uint2*)(p.out + th * kDV + c4 * 4) =
-      make_uint2(pack_bf16x2(acc.x * inv, acc.y * inv), pack_bf16x2(acc.z * inv, acc.w * inv));
-  if (tid == 0) p.lse[th] = any ? mx + __logf(wsum) : -__builtin_inff();
+  *(u32x2*)(p.out + th * kDV + col) =
+      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (tid == 0 && quarter == 0) p.lse[th] = any ? mx + __logf(wsum) : -__builtin_inff();
 }
 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int HG, int NCS, int TR>
+template <int HG, int NCS, int TR, int NBUF>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
-  hipLaunchKernelGGL((split_kernel<HG, NCS, TR>), dim3((unsigned)nwg), dim3(64 * HG * NCS), 0,
-                     st, p);
+  hipLaunchKernelGGL((split_kernel<HG, NCS, TR, NBUF>), dim3((unsigned)nwg), dim3(64 * HG * NCS),
+                     0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
-  if (p.heads <= 16) return launch_split_t<1, 4, 32>(p, 1, st);
-  if (p.heads <= 32) return launch_split_t<2, 2, 32>(p, 1, st);
-  return launch_split_t<4, 2, 64>(p, (p.heads + 63) / 64, st);
+  if (p.heads <= 16) return launch_split_t<1, 4, 32, 2>(p, 1, st);
+  if (p.heads <= 32) return launch_split_t<2, 2, 32, 2>(p, 1, st);
+  return launch_split_t<4, 1, 64, 2>(p, (p.heads + 63) / 64, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }
 
-template <int SG>
+template <int SG, int PER>
 static hipError_t launch_combine_t(const CombineParams& p, hipStream_t st) {
-  const int64_t nwg = (int64_t)p.tokens * p.heads;
-  hipLaunchKernelGGL((combine_kernel<SG>), dim3((unsigned)nwg), dim3(128 * SG), 0, st, p);
+  const int64_t nwg = (int64_t)p.tokens * p.heads * (kDV / kCombCols);
+  hipLaunchKernelGGL((combine_kernel<SG, PER>), dim3((unsigned)nwg), dim3(kCombC4 * SG), 0, st,
+                     p);
   return hipGetLastError();
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t st) {
-  // more split groups when there are many splits per (token, head)
-  if (p.nsplit >= 32) return launch_combine_t<8>(p, st);
-  if (p.nsplit >= 8) return launch_combine_t<4>(p, st);
-  if (p.nsplit >= 2) return launch_combine_t<2>(p, st);
-  return launch_combine_t<1>(p, st);
+  // split groups x loads in flight per thread, sized so one pass covers up
+  // to 128 splits
+  if (p.nsplit > 32) return launch_combine_t<16, 8>(p, st);
+  if (p.nsplit > 8) return launch_combine_t<8, 4>(p, st);
+  return launch_combine_t<4, 2>(p, st);
 }
 
 }  // namespace smla

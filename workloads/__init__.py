@@ -257,3 +257,59 @@ def oracle_view(inp: Inputs, kv_dev=None, seqs=None):
         return q, inp.kv[rows], idx2
     r = torch.from_numpy(rows).to(kv_dev.device)
     return q, torch_to_bits(kv_dev.index_select(0, r)), idx2
+
+
+# ------------------------------------------------------------ bench rotation
+
+def rotation(inp: Inputs, min_bytes: int = 512 << 20, seed: int = 77):
+    """Input sets for timing with cold caches.
+
+    Successive timed steps cycle through (cache, index set) pairs whose
+    distinct gathered rows together exceed `min_bytes` (default 2x the
+    256 MB Infinity Cache), so a row is never still cached from an earlier
+    step.  Each index set keeps the workload's recipe (uniform, without
+    replacement, from each token's own context); sets over one cache use
+    disjoint rows while the context allows it.
+
+    Returns (n_caches, sets): step i uses cache i % n_caches and
+    sets[(i // n_caches) % len(sets)], each set an int32 [B, Lq, K] array.
+    Paged workloads use their one pool (n_caches == 1).
+    """
+    rng = np.random.default_rng(seed)
+    B, Lq, K = inp.idx.shape
+    T = B * Lq
+    if inp.page_table is None:
+        ctx = inp.kv_rows
+        distinct = min(T * K, ctx) * ROW_BYTES
+        need = -(-min_bytes // distinct)
+        n_sets = max(1, min(need, ctx // (T * K)))
+        sets = []
+        for _ in range(n_sets):
+            if T * K <= ctx:
+                perm = rng.permutation(ctx)[: T * K].astype(np.int32)
+                sets.append(perm.reshape(B, Lq, K))
+            else:
+                sets.append(np.stack([np.stack([sample_topk(rng, ctx, K) for _ in range(Lq)])
+                                      for _ in range(B)]).astype(np.int32))
+        n_caches = max(1, -(-need // n_sets))
+        return n_caches, sets
+    ctx = np.asarray(inp.ctx)
+    valid = int((inp.idx >= 0).sum())
+    need = -(-min_bytes // max(1, valid * ROW_BYTES))
+    n_sets = max(1, min(need, int(max(1, (ctx // K).min()))))
+    sets = []
+    for s in range(n_sets):
+        idx = np.empty((B, Lq, K), np.int32)
+        for b in range(B):
+            perm = rng.permutation(int(ctx[b]))
+            for i in range(Lq):
+                j = s * Lq + i
+                if (j + 1) * K <= ctx[b]:
+                    pos = perm[j * K:(j + 1) * K].astype(np.int64)
+                else:
+                    pos = sample_topk(rng, int(ctx[b]), K).astype(np.int64)
+                page = inp.page_table[b]
+                safe = np.maximum(pos, 0)
+                idx[b, i] = np.where(pos >= 0, page[safe // PAGE] * PAGE + safe % PAGE, -1)
+        sets.append(idx)
+    return 1, sets

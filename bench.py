@@ -72,13 +72,16 @@ def parse():
                     help="CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--kernel-steps", type=int, default=512, help="steps of the per-kernel event loop")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 256 MiB device copy (counter calibration) and exit")
+                    help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
 
 
 def copy_calibration():
+    """A plain 1 GiB device-to-device copy (larger than the Infinity Cache),
+    launched three times: the reference dispatch for scaling the HBM byte
+    counters (it reads and writes exactly 1 GiB)."""
     import torch
-    n = 256 << 20
+    n = 1 << 30
     src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()

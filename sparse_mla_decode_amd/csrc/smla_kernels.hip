@@ -53,12 +53,31 @@ constexpr int kKSteps = kRow / 32;               // 18 MFMA K-steps over 576 col
 // nothing to P*V (and never carry non-finite stale data).
 __device__ __attribute__((aligned(16))) u32x4 g_zero_row[kRowGran];
 
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
-  return __shfl_xor(v, mask, 64);
+// Reductions over the four lanes l, l^16, l^32, l^48 (one MFMA column: the
+// same head in the four lane groups) with the gfx950 permlane swaps: a swap
+// of a value with itself leaves each lane holding its own value and the
+// partner's, so no LDS round trip is needed.
+__device__ __forceinline__ float max4_lanes(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const unsigned w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float sum4_lanes(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto a = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  const float y = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const unsigned w = __float_as_uint(y);
+  const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-__device__ __forceinline__ bool row_ok(int32_t r, int64_t kv_rows) {
-  return r >= 0 && (int64_t)r < kv_rows;
+// Row indices are int32, so a row is valid iff 0 <= r < min(kv_rows, 2^31-1);
+// one unsigned compare covers both bounds.
+__device__ __forceinline__ uint32_t rows32(int64_t kv_rows) {
+  return (uint32_t)(kv_rows < 0x7fffffffLL ? kv_rows : 0x7fffffffLL);
 }
 
 // Round to bf16 (nearest even) and pack two values.
@@ -92,6 +111,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Workgroup barriers without the vmcnt(0) a __syncthreads() fence implies.
+// The signal fences stop the compiler from moving memory accesses across the
+// barrier (they emit no instructions).
+__device__ __forceinline__ void barrier_raw() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+// LDS writes of this wave complete, then barrier.
+__device__ __forceinline__ void barrier_lds() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt((0xF) | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt(0)
+  barrier_raw();
+}
+
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 
 // LDS transpose read (ds_read_b64_tr_b16): within each 16-lane group, output
@@ -105,17 +139,21 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
 constexpr int kListCap = 2048;  // list entries staged in LDS at a time
 
 // ---------------------------------------------------------------------------
-// Split kernel.  HG head groups of 16 per workgroup, NCS column slices of the
-// 512 value columns per head group, one wave per (head group, column slice).
-// Every wave computes S for its head group; the PV work and the O
-// accumulators are divided among the NCS waves that share a head group.
-// TR rows per tile, NBUF tile buffers: NBUF-1 tiles are in flight while one
-// is computed.
+// Split kernel.  HG head groups of 16 per workgroup; each wave owns GPW
+// head groups and one of NCS column slices of the 512 value columns.  Every
+// wave computes S for its head groups; the PV work and the O accumulators
+// are divided among the NCS waves that share head groups.  With GPW = 2 a
+// wave feeds every LDS operand read (a K-tile of QK^T, a V^T block of PV) to
+// two MFMAs, one per head group, halving LDS traffic per head; it then needs
+// about 460 registers and runs one wave per SIMD.  TR rows per tile, NBUF
+// tile buffers: NBUF-1 tiles are in flight while one is computed.
 // ---------------------------------------------------------------------------
-template <int HG, int NCS, int TR, int NBUF>
-__global__ __launch_bounds__(64 * HG * NCS) __attribute__((amdgpu_waves_per_eu(2)))
+template <int HG, int NCS, int GPW, int TR, int NBUF>
+__global__ __launch_bounds__(64 * (HG / GPW) * NCS)
+__attribute__((amdgpu_waves_per_eu(GPW == 1 ? 2 : 1)))
 void split_kernel(SplitParams p) {
-  constexpr int NT = 64 * HG * NCS;
+  static_assert(HG % GPW == 0, "whole head groups per wave");
+  constexpr int NT = 64 * (HG / GPW) * NCS;
   constexpr int RB = TR / 16;                 // 16-row blocks per tile (QK^T M blocks)
   constexpr int KP = TR / 32;                 // 32-row K-steps of PV per tile
   constexpr int L = TR * kRowGran / NT;       // DMA instructions per thread per tile
@@ -140,7 +178,7 @@ void split_kernel(SplitParams p) {
   const int wave = tid >> 6;
   const int g = lane >> 4;    // lane group: selects the K slots of MFMA operands
   const int l16 = lane & 15;  // MFMA row / column within a 16-wide block
-  const int hg = wave / NCS;
+  const int hg0 = (wave / NCS) * GPW;  // first head group of this wave
   const int cs = wave % NCS;
 
   // workgroup -> (split, token, head block); splits vary fastest
@@ -150,18 +188,39 @@ void split_kernel(SplitParams p) {
   const int tok = rest % p.tokens;
   const int hblk = rest / p.tokens;
 
-  const int h = hblk * (HG * 16) + hg * 16 + l16;  // this lane's head
-  const bool h_ok = h < p.heads;
+  // this lane's head in each of the wave's head groups
+  int h[GPW];
+  bool h_ok[GPW];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    h[gi] = hblk * (HG * 16) + (hg0 + gi) * 16 + l16;
+    h_ok[gi] = h[gi] < p.heads;
+  }
 
   // Q^T as the B operand of S^T = KV * Q^T: lane (g, l16) holds
   // q[h][32*ks + 8*g .. +7] for every K-step ks (zeros for padding heads,
   // read from the zero row: 72 granules cover 18 K-steps x 4 groups).
-  bf16x8 qb[kKSteps];
-  {
-    const u32x4* qrow = h_ok ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + h) * kRow) + g
-                             : g_zero_row + g;
+  // this split's slice of the list; the first chunk's entries are loaded
+  // before q, so that the tile loads can start as soon as the list is in
+  const int lo = min(split * p.per_split, p.topk);
+  const int hi = min(lo + p.per_split, p.topk);
+  const int32_t* idx_row = p.idx + (int64_t)tok * p.topk;
+  constexpr int LI = kListCap / NT;
+  int lv[LI];
+  auto load_list = [&](int clo, int n_ent) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qb[ks] = __builtin_bit_cast(bf16x8, qrow[ks * 4]);
+    for (int u = 0; u < LI; ++u) lv[u] = idx_row[clo + min(u * NT + tid, n_ent - 1)];
+  };
+  if (lo < hi) load_list(lo, min(hi - lo, kListCap));
+
+  bf16x8 qb[GPW][kKSteps];
+#pragma unroll
+  for (int gi = 0; gi < GPW; ++gi) {
+    const u32x4* qrow = h_ok[gi]
+                            ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + h[gi]) * kRow) + g
+                            : g_zero_row + g;
+#pragma unroll
+    for (int ks = 0; ks < kKSteps; ++ks) qb[gi][ks] = __builtin_bit_cast(bf16x8, qrow[ks * 4]);
   }
 
   // QK^T operand: row 16*rb + l16, granule 4*ks + g, i.e. block ks/2 and
@@ -198,26 +257,25 @@ void split_kernel(SplitParams p) {
     if (DP == 1) dma_gran[d] += 8 * (wave / RG);
   }
 
-  float m_run = -__builtin_inff();  // running max of log2-scaled scores (per head)
-  float l_run = 0.f;                // this lane's share of the running sum
-  floatx4 oacc[CB];
+  float m_run[GPW], l_run[GPW];  // running max (log2 units) and this lane's share of the sum
+  floatx4 oacc[GPW][CB];
 #pragma unroll
-  for (int cb = 0; cb < CB; ++cb) oacc[cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-
-  const int lo = min(split * p.per_split, p.topk);
-  const int hi = min(lo + p.per_split, p.topk);
-  const int32_t* idx_row = p.idx + (int64_t)tok * p.topk;
+  for (int gi = 0; gi < GPW; ++gi) {
+    m_run[gi] = -__builtin_inff();
+    l_run[gi] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb) oacc[gi][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // LDS-DMA loads of tile t (list entries t*TR.. of the staged chunk); a
   // masked entry (or one past the chunk) loads the zero row.
-  auto issue = [&](uint8_t* buf, int t, int n_ent) __attribute__((always_inline)) {
+  auto issue = [&](uint8_t* buf, int t) __attribute__((always_inline)) {
     const u32x4* src[DP];
 #pragma unroll
     for (int d = 0; d < DP; ++d) {
-      const int e = t * TR + dma_row[d];          // < kListCap: inside list_s
-      const int32_t r = e < n_ent ? list_s[e] : -1;
+      const int32_t r = list_s[t * TR + dma_row[d]];  // < kListCap: inside list_s
       const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
-      src[d] = (const u32x4*)(row_ok(r, p.kv_rows) ? hit : (uintptr_t)g_zero_row) + dma_gran[d];
+      src[d] = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran[d];
     }
 #pragma unroll
     for (int it = 0; it < L; ++it) {
@@ -230,75 +288,89 @@ void split_kernel(SplitParams p) {
   };
 
   // Consume tile t held in T.
-  auto compute = [&](const uint8_t* T, int t, int n_ent) __attribute__((always_inline)) {
+  auto compute = [&](const uint8_t* T, int t) __attribute__((always_inline)) {
     // ---- S^T = KV_tile * Q^T: RB 16-row blocks, 18 K-steps of 32 columns;
     // with fewer than four row blocks, even and odd K-steps accumulate
     // separately so that enough independent MFMAs are in flight
-    constexpr int CH = RB >= 4 ? 1 : 2;
-    floatx4 sacc[RB][CH];
+    floatx4 sacc[GPW][RB];
 #pragma unroll
-    for (int rb = 0; rb < RB; ++rb)
+    for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
-      for (int c = 0; c < CH; ++c) sacc[rb][c] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int rb = 0; rb < RB; ++rb) sacc[gi][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < kKSteps; ++ks) {
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         const int off = ((ks & 1) ? qk_odd : qk_even) + (ks >> 1) * TR * 128 + rb * 16 * 128;
         const bf16x8 a = *(const bf16x8*)(T + off);
-        sacc[rb][ks % CH] =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[ks], sacc[rb][ks % CH], 0, 0, 0);
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi)
+          sacc[gi][rb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[gi][ks], sacc[gi][rb], 0, 0, 0);
       }
     }
 
     // ---- online softmax; lane holds rows j = 16*rb + 4*g + i of head h
-    float s[4 * RB];
+    // validity of the rows this lane holds (shared by the wave's head groups)
+    bool ok[4 * RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       const int e0 = t * TR + rb * 16 + 4 * g;
       const i32x4 r4 = *(const i32x4*)(list_s + e0);
-      floatx4 sc = sacc[rb][0];
 #pragma unroll
-      for (int c = 1; c < CH; ++c) sc += sacc[rb][c];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool ok = (e0 + i < n_ent) && row_ok(r4[i], p.kv_rows);
-        s[rb * 4 + i] = ok ? sc[i] * p.scale_log2 : -__builtin_inff();
-      }
+      for (int i = 0; i < 4; ++i) ok[rb * 4 + i] = r4[i] >= 0;
     }
-    float tmax = s[0];
+    float s[GPW][4 * RB];
+    float tmax[GPW];
 #pragma unroll
-    for (int i = 1; i < 4 * RB; ++i) tmax = fmaxf(tmax, s[i]);
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
-    tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
+    for (int gi = 0; gi < GPW; ++gi) {
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          s[gi][rb * 4 + i] = ok[rb * 4 + i] ? sacc[gi][rb][i] * p.scale_log2 : -__builtin_inff();
+      float mx = s[gi][0];
+#pragma unroll
+      for (int i = 1; i < 4 * RB; ++i) mx = fmaxf(mx, s[gi][i]);
+      tmax[gi] = max4_lanes(mx);
+    }
     // Lazy rescaling: the running max only moves when a head's tile max
     // exceeds it by more than 2^8 (in base 2), so O and l are rescaled
     // rarely; meanwhile the weights exp2(s - m) stay below 2^8.
-    if (__any(tmax > m_run + kRescaleLog2)) {
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);  // 0 while m_run = -inf
-      l_run *= alpha;
+    bool grow = false;
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) oacc[cb] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == -__builtin_inff() ? 0.f : m_run;
-    float pv[4 * RB];
+    for (int gi = 0; gi < GPW; ++gi) grow |= tmax[gi] > m_run[gi] + kRescaleLog2;
+    if (__any(grow)) {
 #pragma unroll
-    for (int i = 0; i < 4 * RB; ++i) {
-      pv[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-      l_run += pv[i];
+      for (int gi = 0; gi < GPW; ++gi) {
+        const float m_new = fmaxf(m_run[gi], tmax[gi]);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[gi] - m_new);  // 0 while m_run = -inf
+        l_run[gi] *= alpha;
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) oacc[gi][cb] *= alpha;
+        m_run[gi] = m_new;
+      }
     }
 
     // P^T as the B operand of K-step kp: K slot s <-> tile row
     // 32*kp + 16*(s/4) + 4*g + s%4, i.e. the rows this lane already holds.
-    bf16x8 pb[KP];
+    bf16x8 pb[GPW][KP];
 #pragma unroll
-    for (int kp = 0; kp < KP; ++kp) {
-      const float* v = pv + 8 * kp;
-      const u32x4 pw = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
-                        pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
-      pb[kp] = __builtin_bit_cast(bf16x8, pw);
+    for (int gi = 0; gi < GPW; ++gi) {
+      const float m_use = m_run[gi] == -__builtin_inff() ? 0.f : m_run[gi];
+      float pv[4 * RB];
+#pragma unroll
+      for (int i = 0; i < 4 * RB; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(s[gi][i] - m_use);
+        l_run[gi] += pv[i];
+      }
+#pragma unroll
+      for (int kp = 0; kp < KP; ++kp) {
+        const float* v = pv + 8 * kp;
+        const u32x4 pw = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+        pb[gi][kp] = __builtin_bit_cast(bf16x8, pw);
+      }
     }
 
     // ---- O^T += V^T * P^T; the A operand (V^T, tile rows on K) comes from
@@ -313,32 +385,35 @@ void split_kernel(SplitParams p) {
         const shortx4 v_lo = lds_tr16(T + off);
         const shortx4 v_hi = lds_tr16(T + off + 16 * 128);
         const shortx4 a8[2] = {v_lo, v_hi};
-        oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a8),
-                                                           pb[kp], oacc[cb], 0, 0, 0);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi)
+          oacc[gi][cb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[gi][kp], oacc[gi][cb], 0, 0, 0);
       }
     }
   };
 
   // Software pipeline over the tiles of each staged chunk of the list.
+  // stage a chunk of the list in one memory round trip: all loads (issued
+  // earlier), then all stores; the first chunk's loads went out before q.
+  // Every slot is written, and any entry that is masked (-1, out of range,
+  // past the chunk) is stored as -1, so later reads test only r >= 0.
+  const uint32_t kv32 = rows32(p.kv_rows);
+  auto store_list = [&](int n_ent) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LI; ++u) {
+      const int e = u * NT + tid;
+      list_s[e] = (e < n_ent && (uint32_t)lv[u] < kv32) ? lv[u] : -1;
+    }
+    barrier_lds();
+  };
+  if (lo < hi) store_list(min(hi - lo, kListCap));
   for (int clo = lo; clo < hi; clo += kListCap) {
     const int n_ent = min(hi - clo, kListCap);
-    {
-      // stage the chunk in one memory round trip: all loads, then all stores
-      constexpr int LI = kListCap / NT;
-      int v[LI];
-#pragma unroll
-      for (int u = 0; u < LI; ++u) v[u] = idx_row[clo + min(u * NT + tid, n_ent - 1)];
-#pragma unroll
-      for (int u = 0; u < LI; ++u)
-        if (u * NT + tid < n_ent) list_s[u * NT + tid] = v[u];
-    }
-    // every earlier load (q, the list) has landed before the tile loads start,
-    // so the only loads in flight inside the loop are the tile loads
-    wait_vmcnt<0>();
-    __syncthreads();
     const int ntiles = (n_ent + TR - 1) / TR;
-    issue(tb0, 0, n_ent);
-    if (NBUF > 2 && ntiles > 1) issue(tb1, 1, n_ent);
+    issue(tb0, 0);
+    if (NBUF > 2 && ntiles > 1) issue(tb1, 1);
     // one pipeline step on buffer b (a compile-time constant)
     auto step = [&](auto bconst, int n) __attribute__((always_inline)) {
       constexpr int b = decltype(bconst)::value;
@@ -346,10 +421,10 @@ void split_kernel(SplitParams p) {
       // tile n landed (with three buffers, tile n+1 may still be in flight)
       if (NBUF > 2 && n + 1 < ntiles) wait_vmcnt<L * (NBUF - 2)>();
       else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
+      barrier_raw();
       // refill the buffer every wave finished with in the previous step
-      if (n + NBUF - 1 < ntiles) issue(bn == 0 ? tb0 : bn == 1 ? tb1 : tb2, n + NBUF - 1, n_ent);
-      compute(b == 0 ? tb0 : b == 1 ? tb1 : tb2, n, n_ent);
+      if (n + NBUF - 1 < ntiles) issue(bn == 0 ? tb0 : bn == 1 ? tb1 : tb2, n + NBUF - 1);
+      compute(b == 0 ? tb0 : b == 1 ? tb1 : tb2, n);
     };
     for (int n0 = 0; n0 < ntiles; n0 += NBUF) {
       step(std::integral_constant<int, 0>{}, n0);
@@ -357,36 +432,42 @@ void split_kernel(SplitParams p) {
       if constexpr (NBUF > 2)
         if (n0 + 2 < ntiles) step(std::integral_constant<int, 2>{}, n0 + 2);
     }
-    __syncthreads();  // list_s and the buffers are reused by the next chunk
+    barrier_raw();  // list_s and the buffers are reused by the next chunk
+    const int nxt = clo + kListCap;
+    if (nxt < hi) {
+      load_list(nxt, min(hi - nxt, kListCap));
+      store_list(min(hi - nxt, kListCap));
+    }
   }
 
   // ---- epilogue: O / l and LSE = (m * ln 2) + ln l
-  float l_tot = l_run + shfl_xor_f(l_run, 16);
-  l_tot += shfl_xor_f(l_tot, 32);
-  const bool any = l_tot > 0.f;
-  const float inv = any ? 1.f / l_tot : 0.f;
-  const float lse_v = any ? m_run * kLn2 + __logf(l_tot) : -__builtin_inff();
-
-  if (!h_ok) return;
-  const int64_t th = (int64_t)tok * p.heads + h;
-  if (p.nsplit == 1) {
-    uint16_t* orow = p.out + th * kDV;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int c0 = (cs * CB + cb) * 16 + 4 * g;
-      const floatx4 o = oacc[cb] * inv;
-      *(u32x2*)(orow + c0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-    }
-    if (g == 0 && cs == 0) p.lse[th] = lse_v;
-  } else {
-    const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + h;
-    float* orow = p.part_o + slot * kDV;
+  for (int gi = 0; gi < GPW; ++gi) {
+    const float l_tot = sum4_lanes(l_run[gi]);
+    const bool any = l_tot > 0.f;
+    const float inv = any ? 1.f / l_tot : 0.f;
+    const float lse_v = any ? m_run[gi] * kLn2 + __logf(l_tot) : -__builtin_inff();
+    if (!h_ok[gi]) continue;
+    const int64_t th = (int64_t)tok * p.heads + h[gi];
+    if (p.nsplit == 1) {
+      uint16_t* orow = p.out + th * kDV;
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int c0 = (cs * CB + cb) * 16 + 4 * g;
-      *(floatx4*)(orow + c0) = oacc[cb] * inv;
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c0 = (cs * CB + cb) * 16 + 4 * g;
+        const floatx4 o = oacc[gi][cb] * inv;
+        *(u32x2*)(orow + c0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      }
+      if (g == 0 && cs == 0) p.lse[th] = lse_v;
+    } else {
+      const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + h[gi];
+      float* orow = p.part_o + slot * kDV;
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int c0 = (cs * CB + cb) * 16 + 4 * g;
+        *(floatx4*)(orow + c0) = oacc[gi][cb] * inv;
+      }
+      if (g == 0 && cs == 0) p.part_lse[slot] = lse_v;
     }
-    if (g == 0 && cs == 0) p.part_lse[slot] = lse_v;
   }
 }
 
@@ -417,6 +498,23 @@ __global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) 
   const int S = p.nsplit;
   const float* lse_in = p.part_lse + (int64_t)tok * S * p.heads + h;
 
+  // this thread's first round of partial-O loads goes out before the LSE
+  // pass, so the two memory latencies overlap
+  const int c4 = tid % kCombC4;
+  const int sg = tid / kCombC4;
+  const int col = quarter * kCombCols + c4 * 4;
+  const float* o_in = p.part_o + ((int64_t)tok * S * p.heads + h) * kDV + col;
+  const int64_t stride = (int64_t)p.heads * kDV;
+  floatx4 v[PER];
+  auto load_round = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int s = s0 + u * SG;
+      v[u] = s < S ? *(const floatx4*)(o_in + s * stride) : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_round(sg);
+
   // M = max_s LSE_s and W = sum_s exp(LSE_s - M), both block-wide
   float mx = -__builtin_inff();
   for (int s = tid; s < S; s += NT) mx = fmaxf(mx, lse_in[(int64_t)s * p.heads]);
@@ -445,19 +543,8 @@ __global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) 
   for (int w = 0; w < (NT + 63) / 64; ++w) wsum += red[1][w];
 
   // sum_s w_s O_s over this thread's splits, PER loads in flight at a time
-  const int c4 = tid % kCombC4;
-  const int sg = tid / kCombC4;
-  const int col = quarter * kCombCols + c4 * 4;
-  const float* o_in = p.part_o + ((int64_t)tok * S * p.heads + h) * kDV + col;
-  const int64_t stride = (int64_t)p.heads * kDV;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = sg; s0 < S; s0 += SG * PER) {
-    floatx4 v[PER];
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int s = s0 + u * SG;
-      v[u] = s < S ? *(const floatx4*)(o_in + s * stride) : floatx4{0.f, 0.f, 0.f, 0.f};
-    }
+  for (int s0 = sg;;) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int s = s0 + u * SG;
@@ -465,6 +552,9 @@ __global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) 
       // a zero weight (empty split) contributes nothing, whatever its slot holds
       if (w != 0.f) acc += w * v[u];
     }
+    s0 += SG * PER;
+    if (s0 >= S) break;
+    load_round(s0);
   }
   if (SG > 1) {
     acc_s[sg][c4] = acc;
@@ -486,18 +576,20 @@ __global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) 
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int HG, int NCS, int TR, int NBUF>
+template <int HG, int NCS, int GPW, int TR, int NBUF>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
-  hipLaunchKernelGGL((split_kernel<HG, NCS, TR, NBUF>), dim3((unsigned)nwg), dim3(64 * HG * NCS),
-                     0, st, p);
+  hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF>), dim3((unsigned)nwg),
+                     dim3(64 * (HG / GPW) * NCS), 0, st, p);
   return hipGetLastError();
 }
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
-  if (p.heads <= 16) return launch_split_t<1, 4, 32, 2>(p, 1, st);
-  if (p.heads <= 32) return launch_split_t<2, 2, 32, 2>(p, 1, st);
-  return launch_split_t<4, 1, 64, 2>(p, (p.heads + 63) / 64, st);
+  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, 2>(p, 1, st);
+  if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, 2>(p, 1, st);
+  // more than 64 heads: 64-head blocks (an 8-wave, 128-head workgroup was
+  // measured slower: it spills inside the tile loop)
+  return launch_split_t<4, 1, 1, 32, 2>(p, (p.heads + 63) / 64, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }

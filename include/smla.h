@@ -88,11 +88,14 @@ int smla_plan_nsplit(int batch, int q_len, int heads, int topk);
 
 /*
  * The same planner as a pure function of the CU count: no device access, so
- * it runs (and is tested) on hosts without a GPU.  The rule aims at enough
- * workgroups to keep every CU's memory pipeline busy at batch 1 as well as
- * at batch 128, while each split keeps enough rows to amortise its partial
- * (O, LSE) write ("The Occupancy Hypothesis", "The Occupancy Insight":
- * blocks in flight, not per-block work, hide memory latency).
+ * it runs (and is tested) on hosts without a GPU.  The rule: the largest
+ * NSPLIT whose workgroups (batch * q_len * head blocks * NSPLIT) all fit on
+ * the device at once, two per CU, with at least one 32-row tile per split;
+ * then the fewest splits that keep the same number of tiles per split.  It
+ * fills every CU at batch 1 and drops to NSPLIT 1 once the batch alone
+ * fills the device ("The Occupancy Hypothesis", "The Occupancy Insight":
+ * blocks in flight, not per-block work, hide memory latency; "The Split-K
+ * Imperative": split the list only as far as the grid needs).
  */
 int smla_plan_nsplit_cus(int cus, int batch, int q_len, int heads, int topk);
 
@@ -130,6 +133,8 @@ int smla_split(const void *q, const void *kv_cache, const int32_t *topk_idx, voi
  * combine merges the partials).  For every (token, head): M = max_s LSE_s;
  * M = -inf gives out = 0, lse = -inf; else w_s = exp(LSE_s - M),
  * out = sum_s w_s O_s / sum_s w_s (fp32, then bf16 RNE), lse = M + ln sum_s w_s.
+ * A split with LSE_s = -inf has weight 0 and its O_s slot is not used, so it
+ * may hold anything (NaN included).
  * part_o [tokens, nsplit, heads, 512] fp32 (16-byte aligned),
  * part_lse [tokens, nsplit, heads] fp32; 1 <= nsplit <= SMLA_MAX_NSPLIT.
  */

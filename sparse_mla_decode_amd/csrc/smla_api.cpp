@@ -141,19 +141,22 @@ SMLA_API int smla_plan_nsplit_cus(int cus, int batch, int q_len, int heads, int 
   if (tokens == 0 || topk == 0) return 1;
   const int hpb = smla::split_heads_per_block(heads);
   const int64_t units = tokens * ((heads + hpb - 1) / hpb);  // workgroups per split
-  // Aim for two workgroups per CU (memory-level parallelism), but keep at
-  // least kMinRows list entries per split so the partial write stays small
-  // next to the rows a split gathers.
-  constexpr int kMinRows = 16;
-  const int64_t target = 2 * (int64_t)cus;
-  int64_t ns = (target + units - 1) / units;
-  const int64_t max_ns = topk / kMinRows > 0 ? topk / kMinRows : 1;
+  // A split workgroup costs a fixed start-up (list, q, first gather) plus one
+  // step per 32-row tile, and at small batch the whole call is one such
+  // latency chain.  So: the most splits whose workgroups are all resident at
+  // once (one wave of workgroups over the device), each split at least one
+  // whole tile ...
+  constexpr int kTile = smla::kTileRows;
+  const int64_t slots = (int64_t)cus * smla::kSplitBlocksPerCu;
+  int64_t ns = slots / units;
+  const int64_t max_ns = topk / kTile;
   if (ns > max_ns) ns = max_ns;
   if (ns > SMLA_MAX_NSPLIT) ns = SMLA_MAX_NSPLIT;
   if (ns < 1) ns = 1;
-  // same slice length with the fewest splits: no trailing short or empty split
-  const int64_t per = (topk + ns - 1) / ns;
-  ns = (topk + per - 1) / per;
+  // ... then the fewest splits with that many tiles each: same latency, fewer
+  // workgroups and less partial (O, LSE) traffic for the combine
+  const int64_t tiles = ((topk + ns - 1) / ns + kTile - 1) / kTile;
+  ns = (topk + tiles * kTile - 1) / (tiles * kTile);
   return (int)ns;
 }
 

@@ -16,6 +16,14 @@ constexpr float kLog2e = 1.442695040888963407f;
 // the running max of a head moves only when a tile max exceeds it by this
 // much (base-2 exponent), bounding the unnormalised weights by 2^8
 constexpr float kRescaleLog2 = 8.0f;
+// rows of the list a split workgroup gathers and contracts per step
+constexpr int kTileRows = 32;
+// LDS of one split workgroup: two tile buffers plus the staged index list;
+// a CU's 160 KiB holds two such workgroups at once
+constexpr int kListCap = 2048;
+constexpr int kSplitLdsBytes = 2 * kTileRows * kRow * 2 + kListCap * 4;
+constexpr int kSplitBlocksPerCu = (160 * 1024) / kSplitLdsBytes;
+static_assert(kSplitBlocksPerCu == 2, "two split workgroups per CU");
 
 struct SplitParams {
   const uint16_t* q;    // [T, H, 576] bf16 bits

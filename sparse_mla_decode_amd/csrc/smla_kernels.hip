@@ -136,7 +136,6 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
       (__attribute__((address_space(3))) shortx4*)(__attribute__((address_space(3))) uint8_t*)p);
 }
 
-constexpr int kListCap = 2048;  // list entries staged in LDS at a time
 
 // ---------------------------------------------------------------------------
 // Split kernel.  HG head groups of 16 per workgroup; each wave owns GPW
@@ -573,11 +572,73 @@ __global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) 
   if (tid == 0 && quarter == 0) p.lse[th] = any ? mx + __logf(wsum) : -__builtin_inff();
 }
 
+// Combine for many (token, head) pairs: one thread per 4 output columns of
+// one pair, 128 threads per pair, two pairs per workgroup.  Every thread
+// walks all splits itself (the pair's LSE values are the same addresses for
+// its 128 threads), so there is no LDS, no barrier and no cross-wave
+// reduction; the grid alone supplies the parallelism.
+constexpr int kWidePairs = 2;
+// from this many (token, head) pairs on, the wide combine has >= 512
+// workgroups, enough to cover the device
+constexpr int64_t kWideMinPairs = 1024;
+
+template <int CH>
+__global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineParams p) {
+  const int64_t th = (int64_t)blockIdx.x * kWidePairs + (threadIdx.x >> 7);
+  if (th >= (int64_t)p.tokens * p.heads) return;
+  const int c4 = threadIdx.x & 127;
+  const int64_t tok = th / p.heads;
+  const int h = (int)(th - tok * p.heads);
+  const int S = p.nsplit;
+  const float* lse_in = p.part_lse + tok * S * p.heads + h;
+  const float* o_in = p.part_o + (tok * S * p.heads + h) * kDV + c4 * 4;
+  const int64_t stride = (int64_t)p.heads * kDV;
+
+  floatx4 v[CH];
+  auto load_round = [&](int s0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int s = s0 + u;
+      v[u] = s < S ? *(const floatx4*)(o_in + s * stride) : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_round(0);  // in flight while the LSE values are read
+
+  float mx = -__builtin_inff();
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lse_in[(int64_t)s * p.heads]);
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  for (int s0 = 0;;) {
+#pragma unroll
+    for (int u = 0; u < CH; ++u) {
+      const int s = s0 + u;
+      const float l = s < S ? lse_in[(int64_t)s * p.heads] : -__builtin_inff();
+      const float w = (mx == -__builtin_inff() || l == -__builtin_inff())
+                          ? 0.f
+                          : __builtin_amdgcn_exp2f((l - mx) * kLog2e);
+      wsum += w;
+      // a zero weight (empty split) contributes nothing, whatever its slot holds
+      if (w != 0.f) acc += w * v[u];
+    }
+    s0 += CH;
+    if (s0 >= S) break;
+    load_round(s0);
+  }
+  const bool any = wsum > 0.f;
+  const float inv = any ? 1.f / wsum : 0.f;
+  *(u32x2*)(p.out + th * kDV + c4 * 4) =
+      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+  if (c4 == 0) p.lse[th] = any ? mx + __logf(wsum) : -__builtin_inff();
+}
+
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
 template <int HG, int NCS, int GPW, int TR, int NBUF>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
+  static_assert(TR == kTileRows && NBUF == 2 &&
+                    NBUF * TR * kRow * 2 + kListCap * 4 == kSplitLdsBytes,
+                "the planner's tile and residency model");
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
   hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF>), dim3((unsigned)nwg),
                      dim3(64 * (HG / GPW) * NCS), 0, st, p);
@@ -603,8 +664,16 @@ static hipError_t launch_combine_t(const CombineParams& p, hipStream_t st) {
 }
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t st) {
-  // split groups x loads in flight per thread, sized so one pass covers up
-  // to 128 splits
+  const int64_t pairs = (int64_t)p.tokens * p.heads;
+  if (pairs >= kWideMinPairs) {
+    const int64_t nwg = (pairs + kWidePairs - 1) / kWidePairs;
+    hipLaunchKernelGGL((combine_wide_kernel<8>), dim3((unsigned)nwg), dim3(128 * kWidePairs), 0,
+                       st, p);
+    return hipGetLastError();
+  }
+  // few pairs: the splits of one pair are spread over the waves of a
+  // workgroup (split groups x loads in flight per thread, sized so one pass
+  // covers up to 128 splits)
   if (p.nsplit > 32) return launch_combine_t<16, 8>(p, st);
   if (p.nsplit > 8) return launch_combine_t<8, 4>(p, st);
   return launch_combine_t<4, 2>(p, st);

@@ -67,6 +67,18 @@ SHAPES = [(1, 1, 8, 128), (1, 1, 8, 2048), (64, 1, 64, 2048), (1, 9, 8, 2048),
           (128, 1, 128, 2048), (1, 1, 16, 2048), (32, 1, 8, 2048), (4, 2, 128, 100)]
 
 
+TILE = 32          # list rows one split workgroup contracts per step
+BLOCKS_PER_CU = 2  # split workgroups resident per CU
+
+
+def _hpb(h):
+    return 16 if h <= 16 else 32 if h <= 32 else 64
+
+
+def _tiles(k, ns):
+    return -(-(-(-k // ns)) // TILE)
+
+
 @pytest.mark.parametrize("cus", [80, 188, 256, 304])
 @pytest.mark.parametrize("shape", SHAPES)
 def test_planner_bounds(smla, cus, shape):
@@ -75,20 +87,29 @@ def test_planner_bounds(smla, cus, shape):
     assert ns == smla.smla_plan_nsplit_cus(cus, b, lq, h, k)  # deterministic
     assert 1 <= ns <= smla.MAX_NSPLIT
     per = -(-k // ns)
-    assert per >= min(16, k)                     # at least 16 entries per split
+    assert ns == 1 or per >= TILE                # a split holds at least one tile
     assert -(-k // per) == ns                    # no trailing empty split
-    # either the grid reaches two workgroups per CU, or splits are at their floor
-    hpb = 16 if h <= 16 else 32 if h <= 32 else 64
-    wgs = b * lq * -(-h // hpb) * ns
-    assert wgs >= 2 * cus or per < 32 or ns == 1
+    units = b * lq * -(-h // _hpb(h))            # workgroups per split
+    slots = BLOCKS_PER_CU * cus
+    assert ns == 1 or units * ns <= slots        # one wave of workgroups
+    # no NSPLIT that still fits in one wave needs fewer tiles per split ...
+    best = max(1, min(slots // units, k // TILE))
+    assert _tiles(k, ns) == _tiles(k, best)
+    # ... and none below ns keeps the same tile count
+    assert ns == 1 or _tiles(k, ns - 1) > _tiles(k, ns)
 
 
 def test_planner_fills_small_batches(smla):
-    # batch 1, one head group: split until each split holds 16 entries
-    assert smla.smla_plan_nsplit_cus(256, 1, 1, 8, 2048) == 128
-    # batch 128 x 128 heads already fills 256 CUs twice over: no split needed
-    assert smla.smla_plan_nsplit_cus(256, 128, 1, 128, 2048) == 1 or \
-        smla.smla_plan_nsplit_cus(256, 128, 1, 128, 2048) <= 2
+    # batch 1, one head group: one 32-row tile per split
+    assert smla.smla_plan_nsplit_cus(256, 1, 1, 8, 2048) == 64
+    # 9 query tokens: 56 splits would fit, but 2 tiles each already needs only 32
+    assert smla.smla_plan_nsplit_cus(256, 1, 9, 8, 2048) == 32
+    # batch 64 x 64 heads: 64 workgroups per split, 8 splits fill 512 slots
+    assert smla.smla_plan_nsplit_cus(256, 64, 1, 64, 2048) == 8
+    # batch 128 x 128 heads: 256 workgroups per split
+    assert smla.smla_plan_nsplit_cus(256, 128, 1, 128, 2048) == 2
+    # topk below one tile: no split
+    assert smla.smla_plan_nsplit_cus(256, 1, 1, 8, 31) == 1
     # NSPLIT never grows with the batch
     prev = 10 ** 9
     for b in (1, 2, 4, 8, 16, 32, 64, 128):

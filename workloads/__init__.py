@@ -23,6 +23,7 @@ import numpy as np
 
 D = 576          # q / cache row width in bf16 elements (512 latent + 64 rope)
 ROW_BYTES = D * 2
+DV = 512         # value width: the first 512 columns of a row
 PAGE = 64        # tokens per page in the paged pools
 SCALE = float(np.float32(1.0 / math.sqrt(192.0)))
 
@@ -313,3 +314,40 @@ def rotation(inp: Inputs, min_bytes: int = 512 << 20, seed: int = 77):
                 idx[b, i] = np.where(pos >= 0, page[safe // PAGE] * PAGE + safe % PAGE, -1)
         sets.append(idx)
     return 1, sets
+
+
+def edge_inputs(seed: int = 4242, kv_rows: int = 4096, heads: int = 16, topk: int = 300) -> Inputs:
+    """Index lists that exercise masking: [2, 3, topk] lists over a flat cache.
+
+    (0,0) all -1; (0,1) first half -1; (0,2) one row repeated through most of
+    the list; (1,0) out-of-range entries (kv_rows, kv_rows + 5, 2**31 - 1, -2,
+    -2**31) mixed with valid ones; (1,1) a single valid entry, in the last
+    slot; (1,2) an ordinary list.
+    """
+    inp = flat_inputs("edge", seed, 2, 3, heads, kv_rows, topk)
+    idx = inp.idx
+    idx[0, 0, :] = -1
+    idx[0, 1, : topk // 2] = -1
+    idx[0, 2, 5:] = idx[0, 2, 0]
+    bad = np.array([kv_rows, kv_rows + 5, 2 ** 31 - 1, -2, -2 ** 31], np.int64)
+    pos = np.random.default_rng(seed + 9).choice(topk, size=min(topk, 40), replace=False)
+    idx[1, 0, pos] = bad[np.arange(len(pos)) % len(bad)].astype(np.int32)
+    idx[1, 1, :] = -1
+    idx[1, 1, -1] = kv_rows - 1
+    return inp
+
+
+def partials_inputs(seed: int, tokens: int, nsplit: int, heads: int, empty_frac: float = 0.2):
+    """Synthetic combine inputs: part_o [T, S, H, 512] fp32 ~ N(0, 0.5) and
+    part_lse [T, S, H] fp32 ~ U(-20, 20), with about `empty_frac` of the
+    (token, split, head) slots empty (LSE = -inf, O slot filled with NaN) and
+    the last (token, head) pair empty in every split."""
+    rng = np.random.default_rng(seed)
+    part_o = rng.normal(0.0, 0.5, (tokens, nsplit, heads, DV)).astype(np.float32)
+    part_lse = rng.uniform(-20.0, 20.0, (tokens, nsplit, heads)).astype(np.float32)
+    empty = rng.random((tokens, nsplit, heads)) < empty_frac
+    empty[-1, :, -1] = True
+    part_lse[empty] = -np.inf
+    part_o[empty] = np.nan
+    return part_o, part_lse
+

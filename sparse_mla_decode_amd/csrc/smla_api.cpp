@@ -147,7 +147,7 @@ SMLA_API int smla_plan_nsplit_cus(int cus, int batch, int q_len, int heads, int 
   // once (one wave of workgroups over the device), each split at least one
   // whole tile ...
   constexpr int kTile = smla::kTileRows;
-  const int64_t slots = (int64_t)cus * smla::kSplitBlocksPerCu;
+  const int64_t slots = (int64_t)cus * smla::split_blocks_per_cu(heads);
   int64_t ns = slots / units;
   const int64_t max_ns = topk / kTile;
   if (ns > max_ns) ns = max_ns;

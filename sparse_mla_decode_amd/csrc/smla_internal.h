@@ -18,12 +18,8 @@ constexpr float kLog2e = 1.442695040888963407f;
 constexpr float kRescaleLog2 = 8.0f;
 // rows of the list a split workgroup gathers and contracts per step
 constexpr int kTileRows = 32;
-// LDS of one split workgroup: two tile buffers plus the staged index list;
-// a CU's 160 KiB holds two such workgroups at once
+// list entries a split workgroup stages in LDS at a time
 constexpr int kListCap = 2048;
-constexpr int kSplitLdsBytes = 2 * kTileRows * kRow * 2 + kListCap * 4;
-constexpr int kSplitBlocksPerCu = (160 * 1024) / kSplitLdsBytes;
-static_assert(kSplitBlocksPerCu == 2, "two split workgroups per CU");
 
 struct SplitParams {
   const uint16_t* q;    // [T, H, 576] bf16 bits
@@ -49,6 +45,8 @@ struct CombineParams {
 hipError_t launch_split(const SplitParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, hipStream_t st);
 int split_heads_per_block(int heads);
+// split workgroups of a call with this many heads that one CU holds at once
+int split_blocks_per_cu(int heads);
 
 }  // namespace smla
 

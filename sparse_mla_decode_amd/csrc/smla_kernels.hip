@@ -33,6 +33,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <utility>
 
 #include "smla_internal.h"
 
@@ -92,17 +93,22 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
 // Tile layout in LDS: the row is cut into 9 blocks of 8 granules (16 bytes
 // each, 128 bytes per block); block kb of all TR rows is stored together,
 // 128 bytes per row, and inside a row's 128 bytes granule c sits at
-// c ^ h(j), h(j) = 2*(j % 4) + (j / 4) % 2:
+// c ^ h(j), h(j) = 2*((j / 2) % 4) + (j / 8) % 2:
 //     slot(j, k) = (k / 8) * TR * 8 + j * 8 + ((k % 8) ^ h(j))
+// The gfx950 LDS has 64 four-byte banks (256 bytes per cycle): a 16-byte
+// read serves 16 lanes per cycle, an 8-byte read 32 lanes; a request is
+// conflict-free when those lanes touch distinct banks.
 //   * an LDS-DMA wave instruction fills 64 consecutive slots = 8 rows x one
-//     full 128-byte line each (coalesced), and every lane keeps one or two
-//     fixed tile rows for all loads of a tile;
-//   * the QK^T operand read (granule k of 16 rows) hits 8 distinct bank
-//     groups in each group of 8 rows (h is a bijection on 8 rows);
-//   * the V^T transpose read (granules 2cb and 2cb+1 of rows 4g..4g+3) hits
-//     all 16 eight-byte bank slots once (h(4g + e) differs in bits 1-2).
+//     full 128-byte line each (coalesced, and a contiguous 1 KiB in LDS), and
+//     every lane keeps one fixed tile row for all loads of a tile;
+//   * the QK^T operand read (one granule of 16 consecutive rows per 16
+//     lanes): rows of one parity share a 256-byte bank row half, and h maps
+//     the 8 even (and the 8 odd) rows of 16 to 8 distinct granules;
+//   * the V^T transpose read (32 lanes: rows 8a..8a+7, two granules, two
+//     8-byte halves): among rows of one parity h/2 takes 4 distinct values,
+//     so the granule pairs {2c, 2c+1} ^ h land on distinct bank groups.
 // All operand addresses are a few per-lane bases plus constants.
-__device__ __forceinline__ int hsw(int j) { return ((j & 3) << 1) | ((j >> 2) & 1); }
+__device__ __forceinline__ int hsw(int j) { return (((j >> 1) & 3) << 1) | ((j >> 3) & 1); }
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding).
 template <int N>
@@ -147,21 +153,78 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
 // about 460 registers and runs one wave per SIMD.  TR rows per tile, NBUF
 // tile buffers: NBUF-1 tiles are in flight while one is computed.
 // ---------------------------------------------------------------------------
-template <int HG, int NCS, int GPW, int TR, int NBUF>
+// The dispatcher hands workgroup i to XCD i % kXcds (round robin over the
+// eight XCDs, each with its own L2).  This renumbering gives every XCD a
+// contiguous range of logical ids, so that neighbouring logical workgroups,
+// which share input rows, also share an L2.  It is a bijection for any grid
+// size, so correctness does not depend on the dispatch order.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_contiguous(int bid, int n) {
+  const int xcd = bid % kXcds, k = bid / kXcds;
+  const int per = n / kXcds, rem = n % kXcds;
+  return xcd < rem ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
+}
+
+// The L LDS-DMA loads of one lane for one tile: load `it` copies the 16 bytes
+// at src + 128*STEP*it to lds + 16*NT*it + 16*lane.  The builtin's immediate
+// offset moves the global and the LDS address alike, so every load takes its
+// global offset as that immediate and the LDS pointer is moved back by the
+// same amount: all loads of the tile then read one address register, rather
+// than one temporary each (a register that a load in flight reads must not be
+// reused until the load completes, which would force waits on every load).
+//
+// The LDS destination is passed through an empty asm statement, so the
+// compiler no longer knows which buffer a load writes.  Its own wait
+// insertion would otherwise guard reads of one buffer against loads in flight
+// into another, and at some control-flow joins it loses track of which is
+// which and waits for every outstanding load, draining the pipeline.  The
+// order of loads and reads is kept by hand instead: a tile is read only after
+// the loading waves have waited for its loads (vmcnt) and the workgroup has
+// passed a barrier, and the opaque store still keeps the compiler from moving
+// LDS accesses across the load.
+template <int NT, int STEP, int IT>
+__device__ __forceinline__ void dma_one(const u32x4* src, uint8_t* lds) {
+  constexpr int off = 128 * STEP * IT;
+  static_assert(off < 4096, "immediate offset range");
+  auto* dst = (__attribute__((address_space(3))) uint8_t*)(lds + 16 * NT * IT - off);
+  asm volatile("" : "+v"(dst));
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)dst, 16, off, 0);
+}
+template <int NT, int STEP, int... IT>
+__device__ __forceinline__ void dma_tile(const u32x4* src, uint8_t* lds,
+                                         std::integer_sequence<int, IT...>) {
+  (dma_one<NT, STEP, IT>(src, lds), ...);
+}
+
+// Keeps a value in its registers up to this point.
+__device__ __forceinline__ void keep_live(uint64_t v) { asm volatile("" ::"v"(v)); }
+
+template <int HG, int NCS, int GPW, int TR, int NBUF, bool KSPLIT>
 __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
-__attribute__((amdgpu_waves_per_eu(GPW == 1 ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(GPW == 1 && (NBUF == 2 || KSPLIT) ? 2 : 1)))
 void split_kernel(SplitParams p) {
   static_assert(HG % GPW == 0, "whole head groups per wave");
+  static_assert(!KSPLIT || (NCS == 2 && GPW == 1), "K-split pairs the two column halves");
   constexpr int NT = 64 * (HG / GPW) * NCS;
+  // waves that issue the tile loads: all of them, or with K-split pairs the
+  // first half (a 32-row tile is 36 wave loads, which 8 waves cannot share)
+  constexpr int DW = KSPLIT ? NT / 128 : NT / 64;
+  constexpr int NTD = 64 * DW;
   constexpr int RB = TR / 16;                 // 16-row blocks per tile (QK^T M blocks)
   constexpr int KP = TR / 32;                 // 32-row K-steps of PV per tile
-  constexpr int L = TR * kRowGran / NT;       // DMA instructions per thread per tile
+  constexpr int L = TR * kRowGran / NTD;      // DMA instructions per loading thread per tile
   constexpr int kTileBytes = TR * kRow * 2;
   constexpr int kRowBytes = kRow * 2;
   constexpr int CB = (kDV / 16) / NCS;        // 16-column blocks of O per wave
-  static_assert(TR * kRowGran % NT == 0, "tile must split evenly over the threads");
-  static_assert(TR % 32 == 0 && NBUF >= 2 && NBUF <= 3, "tile shape");
+  // QK^T K-steps per wave: all 18, or with K-split pairs the 9 of one parity
+  constexpr int KSW = KSPLIT ? kKSteps / 2 : kKSteps;
+  static_assert(TR * kRowGran % NTD == 0, "tile must split evenly over the loading threads");
+  static_assert(TR % 32 == 0 && NBUF >= 2 && NBUF <= 4, "tile shape");
   static_assert(L * (NBUF - 2) < 64, "vmcnt range");
+  // with always-issued refills the tile count of a chunk is rounded up to a
+  // multiple of NBUF; the list's tail pad (all -1) covers those tiles
+  constexpr int kListPad = NBUF > 2 ? TR * NBUF : 0;
 
   // One __shared__ object per buffer: each access below names its buffer at
   // compile time, which lets the compiler see that a read of one buffer does
@@ -170,7 +233,10 @@ void split_kernel(SplitParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[NBUF > 2 ? kTileBytes : 16];
-  __shared__ __attribute__((aligned(16))) int list_s[kListCap];
+  __shared__ __attribute__((aligned(16))) uint8_t tb3[NBUF > 3 ? kTileBytes : 16];
+  __shared__ __attribute__((aligned(16))) int list_s[kListCap + kListPad];
+  // partial S^T of every wave (K-split pairs exchange them), [wave][rb][lane]
+  __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? (NT / 64) * RB * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,19 +246,23 @@ void split_kernel(SplitParams p) {
   const int hg0 = (wave / NCS) * GPW;  // first head group of this wave
   const int cs = wave % NCS;
 
-  // workgroup -> (split, token, head block); splits vary fastest
-  const int wg = blockIdx.x;
+  // workgroup -> (token, head block, split), splits fastest, in the XCD-
+  // contiguous numbering: a token's head blocks and splits share one XCD, so
+  // its q rows and the KV rows both head blocks gather meet in that L2
+  const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+  constexpr int kHeadsPerBlock = HG * 16;
+  const int hblocks = (p.heads + kHeadsPerBlock - 1) / kHeadsPerBlock;
   const int split = wg % p.nsplit;
   const int rest = wg / p.nsplit;
-  const int tok = rest % p.tokens;
-  const int hblk = rest / p.tokens;
+  const int hblk = rest % hblocks;
+  const int tok = rest / hblocks;
 
   // this lane's head in each of the wave's head groups
   int h[GPW];
   bool h_ok[GPW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    h[gi] = hblk * (HG * 16) + (hg0 + gi) * 16 + l16;
+    h[gi] = hblk * kHeadsPerBlock + (hg0 + gi) * 16 + l16;
     h_ok[gi] = h[gi] < p.heads;
   }
 
@@ -212,14 +282,17 @@ void split_kernel(SplitParams p) {
   };
   if (lo < hi) load_list(lo, min(hi - lo, kListCap));
 
-  bf16x8 qb[GPW][kKSteps];
+  // with K-split pairs wave half cs holds K-steps 2k + cs
+  bf16x8 qb[GPW][KSW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
     const u32x4* qrow = h_ok[gi]
                             ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + h[gi]) * kRow) + g
                             : g_zero_row + g;
+    if (KSPLIT) qrow += 4 * cs;
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) qb[gi][ks] = __builtin_bit_cast(bf16x8, qrow[ks * 4]);
+    for (int k = 0; k < KSW; ++k)
+      qb[gi][k] = __builtin_bit_cast(bf16x8, qrow[k * 4 * (KSPLIT ? 2 : 1)]);
   }
 
   // QK^T operand: row 16*rb + l16, granule 4*ks + g, i.e. block ks/2 and
@@ -227,15 +300,19 @@ void split_kernel(SplitParams p) {
   const int hq = hsw(l16);
   const int qk_even = l16 * 128 + (g ^ hq) * 16;
   const int qk_odd = l16 * 128 + ((g ^ hq) ^ 4) * 16;
+  // K-split: K-step 2k + cs is block k, in-block half cs
+  const int qk_half = cs ? qk_odd : qk_even;
   // V^T transpose read: source lane (e, s') of group g reads row 4g + e
   // (+16 for slots 4-7, +32 per PV K-step), columns 16*cb + 4s' .. +3 =
   // granule 2cb + b0 (b0 = s' >> 1) at byte 8*b1 (b1 = s' & 1); in-block
-  // granule (2*(cb%4) + b0) ^ h(4g + e) = 2*((cb%4) ^ e) + (b0 ^ (g&1)).
+  // granule (2*(cb%4) + b0) ^ h(4g + e) (rows +16 and +32 share h).
   const int tr_e = l16 >> 2, tr_b0 = (l16 >> 1) & 1, tr_b1 = l16 & 1;
+  const int tr_h = hsw(4 * g + tr_e);
   int pv_base[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c)
-    pv_base[c] = (4 * g + tr_e) * 128 + (2 * (c ^ tr_e) + (tr_b0 ^ (g & 1))) * 16 + 8 * tr_b1;
+  for (int c = 0; c < 4; ++c)  // (this wave's columns start at block 4*CB*cs / 4)
+    pv_base[c] = (4 * g + tr_e) * 128 + ((2 * c + tr_b0) ^ tr_h) * 16 + 8 * tr_b1 +
+                 cs * (CB / 4) * TR * 128;
 
   // DMA: wave instruction it fills slots 64*m .. 64*m + 63, m = it*WPB + wave
   // (WPB = waves per workgroup): block kb = m / RG, rows 8*(m % RG) + lane/8
@@ -243,7 +320,7 @@ void split_kernel(SplitParams p) {
   // granule (lane % 8) ^ h(row).  If RG >= WPB a lane cycles through
   // DP = RG / WPB rows (d = it % DP, kb = it / DP); otherwise it keeps one
   // row and kb = it * (WPB / RG) + wave / RG.
-  constexpr int WPB = NT / 64;
+  constexpr int WPB = DW;
   constexpr int RG = TR / 8;
   static_assert(RG % WPB == 0 || WPB % RG == 0, "row period");
   constexpr int DP = RG > WPB ? RG / WPB : 1;
@@ -267,45 +344,70 @@ void split_kernel(SplitParams p) {
   }
 
   // LDS-DMA loads of tile t (list entries t*TR.. of the staged chunk); a
-  // masked entry (or one past the chunk) loads the zero row.
-  auto issue = [&](uint8_t* buf, int t) __attribute__((always_inline)) {
-    const u32x4* src[DP];
-#pragma unroll
-    for (int d = 0; d < DP; ++d) {
-      const int32_t r = list_s[t * TR + dma_row[d]];  // < kListCap: inside list_s
-      const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
-      src[d] = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran[d];
-    }
-#pragma unroll
-    for (int it = 0; it < L; ++it) {
-      constexpr int kStep = DP > 1 ? 0 : WPB / RG;
-      const int kb = DP > 1 ? it / DP : it * kStep;
-      __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)(src[it % DP] + 8 * kb),
-          (__attribute__((address_space(3))) void*)(buf + (it * NT + wave * 64) * 16), 16, 0, 0);
-    }
+  // masked entry, one past the chunk or a tile past the last (t >= ntiles)
+  // loads the zero row.  The L loads of a lane share one 64-bit address (see
+  // dma_tile), returned so that the caller keeps it live until the loads are
+  // known to be complete.
+  static_assert(DP == 1, "one row per lane per tile");
+  auto issue = [&](uint8_t* buf, int t, int ntiles) __attribute__((always_inline)) -> uint64_t {
+    const int e = min(t * TR + dma_row[0], kListCap - 1);  // inside list_s
+    const int32_t r = t < ntiles ? list_s[e] : -1;
+    const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
+    const u32x4* src = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran[0];
+    if (wave < DW)
+      dma_tile<NTD, WPB / RG>(src, buf + wave * 64 * 16, std::make_integer_sequence<int, L>{});
+    return (uint64_t)(uintptr_t)src;
   };
 
   // Consume tile t held in T.
   auto compute = [&](const uint8_t* T, int t) __attribute__((always_inline)) {
-    // ---- S^T = KV_tile * Q^T: RB 16-row blocks, 18 K-steps of 32 columns;
-    // with fewer than four row blocks, even and odd K-steps accumulate
-    // separately so that enough independent MFMAs are in flight
+    // ---- S^T = KV_tile * Q^T: RB 16-row blocks, 18 K-steps of 32 columns
     floatx4 sacc[GPW][RB];
+    if constexpr (KSPLIT) {
+      // this wave's 9 K-steps (parity cs): all operand reads first, then the
+      // MFMAs in two chains per row block
+      bf16x8 av[KSW][RB];
 #pragma unroll
-    for (int gi = 0; gi < GPW; ++gi)
+      for (int k = 0; k < KSW; ++k)
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[gi][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int rb = 0; rb < RB; ++rb)
+          av[k][rb] = *(const bf16x8*)(T + qk_half + k * TR * 128 + rb * 16 * 128);
+      floatx4 acc2[2][RB];
 #pragma unroll
-    for (int ks = 0; ks < kKSteps; ++ks) {
+      for (int rb = 0; rb < RB; ++rb) acc2[0][rb] = acc2[1][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KSW; ++k)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc2[k & 1][rb] =
+              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k][rb], qb[0][k], acc2[k & 1][rb], 0, 0, 0);
+      // exchange the half sums with the partner wave (same heads, other
+      // parity); own + partner is the same sum in both waves (addition
+      // commutes), so both hold bitwise the same scores
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
-        const int off = ((ks & 1) ? qk_odd : qk_even) + (ks >> 1) * TR * 128 + rb * 16 * 128;
-        const bf16x8 a = *(const bf16x8*)(T + off);
+        sacc[0][rb] = acc2[0][rb] + acc2[1][rb];
+        xs[(wave * RB + rb) * 64 + lane] = sacc[0][rb];
+      }
+      barrier_lds();
 #pragma unroll
-        for (int gi = 0; gi < GPW; ++gi)
-          sacc[gi][rb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[gi][ks], sacc[gi][rb], 0, 0, 0);
+      for (int rb = 0; rb < RB; ++rb) sacc[0][rb] += xs[((wave ^ 1) * RB + rb) * 64 + lane];
+    } else {
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) sacc[gi][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kKSteps; ++ks) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          const int off = ((ks & 1) ? qk_odd : qk_even) + (ks >> 1) * TR * 128 + rb * 16 * 128;
+          const bf16x8 a = *(const bf16x8*)(T + off);
+#pragma unroll
+          for (int gi = 0; gi < GPW; ++gi)
+            sacc[gi][rb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[gi][ks], sacc[gi][rb], 0, 0, 0);
+        }
       }
     }
 
@@ -375,20 +477,39 @@ void split_kernel(SplitParams p) {
     // ---- O^T += V^T * P^T; the A operand (V^T, tile rows on K) comes from
     // two transpose reads: slots 0-3 = rows 4g..4g+3, slots 4-7 = rows
     // 16+4g..16+4g+3 of the K-step, column l16 of the 16-column block.
+    if constexpr (KSPLIT) {
+      // all transpose reads of the wave's column blocks first, then the MFMAs
+      shortx4 vt[CB][KP][2];
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb) {
-      const int cbg = cs * CB + cb;  // 16-column block within the 512
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
-      for (int kp = 0; kp < KP; ++kp) {
-        const int off = pv_base[cbg & 3] + (cbg >> 2) * TR * 128 + 32 * kp * 128;
-        const shortx4 v_lo = lds_tr16(T + off);
-        const shortx4 v_hi = lds_tr16(T + off + 16 * 128);
-        const shortx4 a8[2] = {v_lo, v_hi};
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+        for (int kp = 0; kp < KP; ++kp) {
+          const int off = pv_base[cb & 3] + (cb >> 2) * TR * 128 + 32 * kp * 128;
+          vt[cb][kp][0] = lds_tr16(T + off);
+          vt[cb][kp][1] = lds_tr16(T + off + 16 * 128);
+        }
 #pragma unroll
-        for (int gi = 0; gi < GPW; ++gi)
-          oacc[gi][cb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[gi][kp], oacc[gi][cb], 0, 0, 0);
+      for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp) {
+          const bf16x8 av = __builtin_bit_cast(bf16x8, vt[cb][kp]);
+          oacc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[0][kp], oacc[0][cb], 0, 0, 0);
+        }
+    } else {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+        for (int kp = 0; kp < KP; ++kp) {
+          const int off = pv_base[cb & 3] + (cb >> 2) * TR * 128 + 32 * kp * 128;
+          const shortx4 v_lo = lds_tr16(T + off);
+          const shortx4 v_hi = lds_tr16(T + off + 16 * 128);
+          const shortx4 a8[2] = {v_lo, v_hi};
+          const bf16x8 av = __builtin_bit_cast(bf16x8, a8);
+#pragma unroll
+          for (int gi = 0; gi < GPW; ++gi)
+            oacc[gi][cb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[gi][kp], oacc[gi][cb], 0, 0, 0);
+        }
       }
     }
   };
@@ -405,32 +526,63 @@ void split_kernel(SplitParams p) {
       const int e = u * NT + tid;
       list_s[e] = (e < n_ent && (uint32_t)lv[u] < kv32) ? lv[u] : -1;
     }
+    static_assert(kListPad <= NT, "one pad entry per thread at most");
+    if (kListPad > 0 && tid < kListPad) list_s[kListCap + tid] = -1;
     barrier_lds();
   };
   if (lo < hi) store_list(min(hi - lo, kListCap));
+  auto buf = [&](auto bconst) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int b = decltype(bconst)::value;
+    return b == 0 ? tb0 : b == 1 ? tb1 : b == 2 ? tb2 : tb3;
+  };
   for (int clo = lo; clo < hi; clo += kListCap) {
     const int n_ent = min(hi - clo, kListCap);
     const int ntiles = (n_ent + TR - 1) / TR;
-    issue(tb0, 0);
-    if (NBUF > 2 && ntiles > 1) issue(tb1, 1);
+    // With two buffers the refill of the next tile is skipped past the
+    // last tile.  With more, every step issues one refill (a tile past the
+    // last loads the zero row): the number of loads in flight is then the
+    // same at every wait, and no branch joins paths with different loads
+    // outstanding, which would make the compiler wait for all of them.
+    constexpr bool kAlwaysIssue = NBUF > 2;
+    uint64_t addr[NBUF] = {};  // per buffer: the address its last loads read
+    addr[0] = issue(tb0, 0, ntiles);
+    if constexpr (NBUF > 2) addr[1] = issue(tb1, 1, ntiles);
+    if constexpr (NBUF > 3) addr[2] = issue(tb2, 2, ntiles);
     // one pipeline step on buffer b (a compile-time constant)
     auto step = [&](auto bconst, int n) __attribute__((always_inline)) {
       constexpr int b = decltype(bconst)::value;
-      constexpr int bn = (b + NBUF - 1) % NBUF;
-      // tile n landed (with three buffers, tile n+1 may still be in flight)
-      if (NBUF > 2 && n + 1 < ntiles) wait_vmcnt<L * (NBUF - 2)>();
+      // tile n landed; tiles n+1 .. n+NBUF-2 may still be in flight
+      if constexpr (kAlwaysIssue) wait_vmcnt<L * (NBUF - 2)>();
       else wait_vmcnt<0>();
+      keep_live(addr[b]);  // tile n's loads are done: its address may go
       barrier_raw();
       // refill the buffer every wave finished with in the previous step
-      if (n + NBUF - 1 < ntiles) issue(bn == 0 ? tb0 : bn == 1 ? tb1 : tb2, n + NBUF - 1);
-      compute(b == 0 ? tb0 : b == 1 ? tb1 : tb2, n);
+      constexpr int bn = (b + NBUF - 1) % NBUF;
+      if (kAlwaysIssue || n + NBUF - 1 < ntiles)
+        addr[bn] = issue(buf(std::integral_constant<int, bn>{}), n + NBUF - 1, ntiles);
+      compute(buf(bconst), n);
     };
-    for (int n0 = 0; n0 < ntiles; n0 += NBUF) {
-      step(std::integral_constant<int, 0>{}, n0);
-      if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
-      if constexpr (NBUF > 2)
-        if (n0 + 2 < ntiles) step(std::integral_constant<int, 2>{}, n0 + 2);
+    if constexpr (kAlwaysIssue) {
+      // all NBUF steps of a round unconditionally (a skipped step would again
+      // join paths with different loads outstanding): the tile count is
+      // rounded up to a multiple of NBUF, and a tile past the last holds
+      // only masked entries (-1 in list_s, zero rows in the buffer), which
+      // leave m, l and O unchanged
+      for (int n0 = 0; n0 < ntiles; n0 += NBUF) {
+        step(std::integral_constant<int, 0>{}, n0);
+        step(std::integral_constant<int, 1>{}, n0 + 1);
+        step(std::integral_constant<int, 2>{}, n0 + 2);
+        if constexpr (NBUF > 3) step(std::integral_constant<int, 3>{}, n0 + 3);
+      }
+    } else {
+      for (int n0 = 0; n0 < ntiles; n0 += NBUF) {
+        step(std::integral_constant<int, 0>{}, n0);
+        if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
+      }
     }
+    if constexpr (kAlwaysIssue) wait_vmcnt<0>();  // the refills past the last tile
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) keep_live(addr[b]);
     barrier_raw();  // list_s and the buffers are reused by the next chunk
     const int nxt = clo + kListCap;
     if (nxt < hi) {
@@ -634,26 +786,47 @@ __global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineP
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-template <int HG, int NCS, int GPW, int TR, int NBUF>
+// LDS of one split workgroup: NBUF tile buffers, the staged index list (with
+// its pad), and with K-split pairs the exchange buffer of partial scores
+constexpr int split_lds_bytes(int nbuf, int waves, bool ksplit) {
+  return nbuf * kTileRows * kRow * 2 + (kListCap + (nbuf > 2 ? kTileRows * nbuf : 0)) * 4 +
+         (ksplit ? waves * (kTileRows / 16) * 64 * 16 : 0);
+}
+constexpr int kCuLdsBytes = 160 * 1024;
+
+template <int HG, int NCS, int GPW, int TR, int NBUF, bool KSPLIT>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
-  static_assert(TR == kTileRows && NBUF == 2 &&
-                    NBUF * TR * kRow * 2 + kListCap * 4 == kSplitLdsBytes,
-                "the planner's tile and residency model");
+  static_assert(TR == kTileRows, "the planner's tile");
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
-  hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF>), dim3((unsigned)nwg),
+  hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF, KSPLIT>), dim3((unsigned)nwg),
                      dim3(64 * (HG / GPW) * NCS), 0, st, p);
   return hipGetLastError();
 }
 
+// Per head class.  Up to 32 heads: 4 waves, two tile buffers, two workgroups
+// per CU.  More heads (64-head blocks): 8 waves in K-split pairs (each pair
+// shares 16 heads: one wave takes the even K-steps of QK^T and the first 256
+// V columns, the other the odd K-steps and the last 256), three tile buffers,
+// one workgroup per CU.  The pairs halve the registers a wave needs, so that
+// two waves share each SIMD and each wave can keep its LDS operand reads in
+// flight together (a 4-wave 64-head workgroup spends most of a tile waiting
+// on one LDS read after another).
+constexpr int kNbufSmall = 2, kNbufLarge = 3;
+static_assert(kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, false) == 2, "two small workgroups per CU");
+static_assert(kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, true) == 1, "one large workgroup per CU");
+
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
-  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, 2>(p, 1, st);
-  if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, 2>(p, 1, st);
-  // more than 64 heads: 64-head blocks (an 8-wave, 128-head workgroup was
-  // measured slower: it spills inside the tile loop)
-  return launch_split_t<4, 1, 1, 32, 2>(p, (p.heads + 63) / 64, st);
+  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, kNbufSmall, false>(p, 1, st);
+  if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, kNbufSmall, false>(p, 1, st);
+  return launch_split_t<4, 2, 1, 32, kNbufLarge, true>(p, (p.heads + 63) / 64, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }
+
+int split_blocks_per_cu(int heads) {
+  return heads <= 32 ? kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, false)
+                     : kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, true);
+}
 
 template <int SG, int PER>
 static hipError_t launch_combine_t(const CombineParams& p, hipStream_t st) {

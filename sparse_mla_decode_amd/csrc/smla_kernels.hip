@@ -207,11 +207,11 @@ __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
 __attribute__((amdgpu_waves_per_eu(GPW == 1 && (NBUF == 2 || KSPLIT) ? 2 : 1)))
 void split_kernel(SplitParams p) {
   static_assert(HG % GPW == 0, "whole head groups per wave");
-  static_assert(!KSPLIT || (NCS == 2 && GPW == 1), "K-split pairs the two column halves");
+  static_assert(!KSPLIT || NCS == 2, "K-split pairs the two column halves");
   constexpr int NT = 64 * (HG / GPW) * NCS;
-  // waves that issue the tile loads: all of them, or with K-split pairs the
-  // first half (a 32-row tile is 36 wave loads, which 8 waves cannot share)
-  constexpr int DW = KSPLIT ? NT / 128 : NT / 64;
+  // waves that issue the tile loads: all of them, or half of them when the
+  // tile's wave loads do not split evenly (36 per 32-row tile: not over 8)
+  constexpr int DW = (TR * kRowGran) % NT == 0 ? NT / 64 : NT / 128;
   constexpr int NTD = 64 * DW;
   constexpr int RB = TR / 16;                 // 16-row blocks per tile (QK^T M blocks)
   constexpr int KP = TR / 32;                 // 32-row K-steps of PV per tile
@@ -238,7 +238,7 @@ void split_kernel(SplitParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tb3[NBUF > 3 ? kTileBytes : 16];
   __shared__ __attribute__((aligned(16))) int list_s[kListCap + kListPad];
   // partial S^T of every wave (K-split pairs exchange them), [wave][rb][lane]
-  __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? (NT / 64) * RB * 64 : 1];
+  __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? (NT / 64) * GPW * RB * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -367,33 +367,44 @@ void split_kernel(SplitParams p) {
     floatx4 sacc[GPW][RB];
     if constexpr (KSPLIT) {
       // this wave's 9 K-steps (parity cs): all operand reads first, then the
-      // MFMAs in two chains per row block
+      // MFMAs (each read feeds the wave's GPW head groups) in two chains per
+      // row block and head group
       bf16x8 av[KSW][RB];
 #pragma unroll
       for (int k = 0; k < KSW; ++k)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           av[k][rb] = *(const bf16x8*)(T + qk_half + k * TR * 128 + rb * 16 * 128);
-      floatx4 acc2[2][RB];
+      floatx4 acc2[2][GPW][RB];
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc2[0][rb] = acc2[1][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          acc2[0][gi][rb] = acc2[1][gi][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int k = 0; k < KSW; ++k)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          acc2[k & 1][rb] =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k][rb], qb[0][k], acc2[k & 1][rb], 0, 0, 0);
+#pragma unroll
+          for (int gi = 0; gi < GPW; ++gi)
+            acc2[k & 1][gi][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                av[k][rb], qb[gi][k], acc2[k & 1][gi][rb], 0, 0, 0);
       // exchange the half sums with the partner wave (same heads, other
       // parity); own + partner is the same sum in both waves (addition
       // commutes), so both hold bitwise the same scores
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) {
-        sacc[0][rb] = acc2[0][rb] + acc2[1][rb];
-        xs[(wave * RB + rb) * 64 + lane] = sacc[0][rb];
-      }
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+          sacc[gi][rb] = acc2[0][gi][rb] + acc2[1][gi][rb];
+          xs[((wave * GPW + gi) * RB + rb) * 64 + lane] = sacc[gi][rb];
+        }
       barrier_lds();
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) sacc[0][rb] += xs[((wave ^ 1) * RB + rb) * 64 + lane];
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          sacc[gi][rb] += xs[(((wave ^ 1) * GPW + gi) * RB + rb) * 64 + lane];
     } else {
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi)
@@ -495,7 +506,10 @@ void split_kernel(SplitParams p) {
 #pragma unroll
         for (int kp = 0; kp < KP; ++kp) {
           const bf16x8 av = __builtin_bit_cast(bf16x8, vt[cb][kp]);
-          oacc[0][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[0][kp], oacc[0][cb], 0, 0, 0);
+#pragma unroll
+          for (int gi = 0; gi < GPW; ++gi)
+            oacc[gi][cb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[gi][kp], oacc[gi][cb], 0, 0, 0);
         }
     } else {
 #pragma unroll
@@ -790,9 +804,10 @@ __global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineP
 // ---------------------------------------------------------------------------
 // LDS of one split workgroup: NBUF tile buffers, the staged index list (with
 // its pad), and with K-split pairs the exchange buffer of partial scores
-constexpr int split_lds_bytes(int nbuf, int waves, bool ksplit) {
+// (one 16-row block of 16 heads = 1 KiB per wave, head group and row block)
+constexpr int split_lds_bytes(int nbuf, int waves, int gpw, bool ksplit) {
   return nbuf * kTileRows * kRow * 2 + (kListCap + (nbuf > 2 ? kTileRows * nbuf : 0)) * 4 +
-         (ksplit ? waves * (kTileRows / 16) * 64 * 16 : 0);
+         (ksplit ? waves * gpw * (kTileRows / 16) * 64 * 16 : 0);
 }
 constexpr int kCuLdsBytes = 160 * 1024;
 
@@ -806,28 +821,28 @@ static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t 
 }
 
 // Per head class.  Up to 32 heads: 4 waves, two tile buffers, two workgroups
-// per CU.  More heads (64-head blocks): 8 waves in K-split pairs (each pair
-// shares 16 heads: one wave takes the even K-steps of QK^T and the first 256
-// V columns, the other the odd K-steps and the last 256), three tile buffers,
-// one workgroup per CU.  The pairs halve the registers a wave needs, so that
-// two waves share each SIMD and each wave can keep its LDS operand reads in
-// flight together (a 4-wave 64-head workgroup spends most of a tile waiting
-// on one LDS read after another).
-constexpr int kNbufSmall = 2, kNbufLarge = 3;
-static_assert(kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, false) == 2, "two small workgroups per CU");
-static_assert(kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, true) == 1, "one large workgroup per CU");
+// per CU.  More heads (64-head blocks): 8 waves in K-split pairs, each pair
+// sharing one 16-head group: one wave takes the even K-steps of QK^T and the
+// first 256 V columns, the other the odd K-steps and the last 256.  Three
+// tile buffers, one workgroup per CU, two waves per SIMD.  (Two head groups
+// per wave halve the LDS reads per head but need about 480 registers, one
+// wave per SIMD: measured 20% slower, the LDS latency is no longer hidden.)
+constexpr int kNbufSmall = 2, kNbufLarge = 3, kGpwLarge = 1;
+static_assert(kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 1, false) == 2, "two small workgroups per CU");
+static_assert(kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, kGpwLarge, true) == 1,
+              "one large workgroup per CU");
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
   if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, kNbufSmall, false>(p, 1, st);
   if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, kNbufSmall, false>(p, 1, st);
-  return launch_split_t<4, 2, 1, 32, kNbufLarge, true>(p, (p.heads + 63) / 64, st);
+  return launch_split_t<4, 2, kGpwLarge, 32, kNbufLarge, true>(p, (p.heads + 63) / 64, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }
 
 int split_blocks_per_cu(int heads) {
-  return heads <= 32 ? kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, false)
-                     : kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, true);
+  return heads <= 32 ? kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 1, false)
+                     : kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, kGpwLarge, true);
 }
 
 template <int SG, int PER>

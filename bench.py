@@ -19,7 +19,11 @@ Timing protocol
   * roofline: gathered-KV bytes of one split launch (valid list entries x
     1152 B) / the split kernel's mean duration, against 8 TB/s HBM3E;
   * cpu_baseline: the fp64 oracle, as is, on the host cores, over a bounded
-    sample of the same workload, scaled to steps/s.
+    sample of the same workload, scaled to steps/s;
+  * nsplit_sweep: steps/s and the split kernel's gathered-KV rate of the same
+    workload at each NSPLIT of its sweep (the planner's marked), and, beside
+    a batch-1 workload, the same figures for the batch-64 workload at the
+    planner's NSPLIT ("secondary").
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -70,7 +74,9 @@ def parse():
     ap.add_argument("--warm", action="store_true", help="no input rotation (cache-resident figure)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline (0 = skip)")
-    ap.add_argument("--kernel-steps", type=int, default=512, help="steps of the per-kernel event loop")
+    ap.add_argument("--kernel-steps", type=int, default=512, help="launches per per-kernel timing")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the NSPLIT sweep and the secondary batch-64 figure")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -91,6 +97,118 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "launches": 3}), flush=True)
 
 
+SWEEPS = {"tiny": [1, 4], "long": [1, 16, 64, 128], "spec": [16, 64], "batched": [1, 2, 4, 8, 16],
+          "ragged": [1, 2, 4]}
+
+
+class Workload:
+    """Device-resident inputs of one workload plus its rotation of
+    (cache, index set) pairs, and the timing helpers over them."""
+
+    def __init__(self, name, spec_ctx, warm, dev):
+        import numpy as np
+        import torch
+
+        import sparse_mla_decode_amd as smla
+        import workloads as wl
+
+        self.smla, self.torch, self.name, self.dev = smla, torch, name, dev
+        inp = wl.workload(name, spec_ctx=spec_ctx, with_kv=False)
+        self.inp = inp
+        self.B, self.Lq, self.H, self.K = inp.batch, inp.q_len, inp.heads, inp.topk
+        self.T = self.B * self.Lq
+        if warm:
+            self.n_caches, self.sets = 1, [inp.idx]
+        else:
+            self.n_caches, self.sets = wl.rotation(inp)
+        self.q = wl.bits_to_torch(inp.q).to(dev)
+        self.caches = [wl.device_pool(inp.kv_rows, (inp.pool_seed or 0) + 1000 * c, dev)
+                       for c in range(self.n_caches)]
+        self.idx_sets = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in self.sets]
+        self.out = torch.empty((self.B, self.Lq, self.H, 512), dtype=torch.bfloat16, device=dev)
+        self.lse = torch.empty((self.B, self.Lq, self.H), dtype=torch.float32, device=dev)
+        self.n_rot = self.n_caches * len(self.sets)
+        self.valid_rows = [int((x >= 0).sum()) for x in self.sets]  # every set points inside its cache
+        self.mean_kv_bytes = sum(self.valid_rows[(i // self.n_caches) % len(self.sets)] * ROW_BYTES
+                                 for i in range(self.n_rot)) / self.n_rot
+        self.stream = torch.cuda.Stream()
+        self.ws = {}
+        torch.cuda.synchronize()
+
+    def plan(self):
+        return self.smla.smla_plan_nsplit(self.B, self.Lq, self.H, self.K)
+
+    def workspace(self, nsplit):
+        if nsplit not in self.ws:
+            self.ws[nsplit] = self.smla.workspace(self.B, self.Lq, self.H, nsplit, self.dev)
+        return self.ws[nsplit]
+
+    def _args(self, i):
+        return self.caches[i % self.n_caches], self.idx_sets[(i // self.n_caches) % len(self.sets)]
+
+    def step_fn(self, nsplit):
+        ws = self.workspace(nsplit)
+
+        def f(i, stream=None):
+            c, ix = self._args(i)
+            self.smla.smla_decode(self.q, c, ix, self.out, self.lse, self.inp.scale, nsplit, ws, stream)
+        return f
+
+    def split_fn(self, nsplit):
+        ws = self.workspace(nsplit)
+
+        def f(i):
+            c, ix = self._args(i)
+            self.smla.smla_split(self.q, c, ix, self.out, self.lse, self.inp.scale, nsplit, ws)
+        return f
+
+    def combine_fn(self, nsplit):
+        part = self.smla.partials_view(self.workspace(nsplit), self.B, self.Lq, self.H, nsplit)
+
+        def f(i):
+            self.smla.smla_combine(part[0], part[1], self.out, self.lse)
+        return f
+
+    def graph_of(self, fn):
+        """One rotation cycle of fn(i) captured in a HIP graph."""
+        torch = self.torch
+        torch.cuda.synchronize()
+        self.stream.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(self.stream):
+            with torch.cuda.graph(g, stream=self.stream):
+                for i in range(self.n_rot):
+                    fn(i)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        return g
+
+    def time_graph(self, g, min_launches):
+        """Mean microseconds per captured call over whole-cycle replays."""
+        torch = self.torch
+        reps = max(1, -(-min_launches // self.n_rot))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(reps):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / (reps * self.n_rot), reps * self.n_rot
+
+    def summary(self, nsplit, steps, kernel_steps):
+        """Steps/s and the split kernel's time and gathered-KV rate at nsplit."""
+        step_us, n = self.time_graph(self.graph_of(self.step_fn(nsplit)), steps)
+        split_us, _ = self.time_graph(self.graph_of(self.split_fn(nsplit)), kernel_steps)
+        return {"nsplit": nsplit, "us_per_step": round(step_us, 3), "steps_per_s": round(1e6 / step_us, 2),
+                "gathered_kv_gbps_per_step": round(self.mean_kv_bytes / (step_us * 1e-6) / 1e9, 2),
+                "split_us": round(split_us, 3),
+                "split_kv_gbps": round(self.mean_kv_bytes / (split_us * 1e-6) / 1e9, 2),
+                "split_roofline_frac": round(self.mean_kv_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                "steps_timed": n}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -106,112 +224,37 @@ def main():
         copy_calibration()
         return
 
-    import sparse_mla_decode_amd as smla
-    import workloads as wl
-
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_setup = time.time()
-    inp = wl.workload(args.workload, spec_ctx=args.spec_ctx, with_kv=False)
-    B, Lq, H, K = inp.batch, inp.q_len, inp.heads, inp.topk
-    T = B * Lq
-    if args.warm:
-        n_caches, sets = 1, [inp.idx]
-    else:
-        n_caches, sets = wl.rotation(inp)
-    log(f"[bench] workload={args.workload} B={B} Lq={Lq} H={H} K={K} kv_rows={inp.kv_rows} "
-        f"caches={n_caches} index_sets={len(sets)}")
+    w = Workload(args.workload, args.spec_ctx, args.warm, dev)
+    B, Lq, H, K, T = w.B, w.Lq, w.H, w.K, w.T
+    log(f"[bench] workload={args.workload} B={B} Lq={Lq} H={H} K={K} kv_rows={w.inp.kv_rows} "
+        f"caches={w.n_caches} index_sets={len(w.sets)}")
+    nsplit = args.nsplit if args.nsplit > 0 else w.plan()
+    step = w.step_fn(nsplit)
+    log(f"[bench] setup {time.time() - t_setup:.1f}s nsplit={nsplit} rotation={w.n_rot} steps")
 
-    q = wl.bits_to_torch(inp.q).to(dev)
-    caches = [wl.device_pool(inp.kv_rows, (inp.pool_seed or 0) + 1000 * c, dev) for c in range(n_caches)]
-    idx_sets = [torch.from_numpy(np.ascontiguousarray(s)).to(dev) for s in sets]
-    nsplit = args.nsplit if args.nsplit > 0 else smla.smla_plan_nsplit(B, Lq, H, K)
-    ws = smla.workspace(B, Lq, H, nsplit, dev)
-    out = torch.empty((B, Lq, H, 512), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((B, Lq, H), dtype=torch.float32, device=dev)
-    n_rot = n_caches * len(sets)
-    valid_rows = [int((s >= 0).sum()) for s in sets]   # every index set points inside its cache
-    kv_bytes_step = [v * ROW_BYTES for v in valid_rows]
-
-    def step(i, stream=None):
-        c = caches[i % n_caches]
-        ix = idx_sets[(i // n_caches) % len(sets)]
-        smla.smla_decode(q, c, ix, out, lse, inp.scale, nsplit, ws, stream)
-
-    torch.cuda.synchronize()
-    log(f"[bench] setup {time.time() - t_setup:.1f}s nsplit={nsplit} rotation={n_rot} steps")
-
-    # ---- warm-up (eager), then capture one rotation cycle in a HIP graph
+    # ---- warm-up (eager), then the timed region: K steps from replays of a
+    # HIP graph holding one rotation cycle
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    g_stream = torch.cuda.Stream()
-    g_stream.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(g_stream):
-        with torch.cuda.graph(graph, stream=g_stream):
-            for i in range(n_rot):
-                step(i)
-    torch.cuda.synchronize()
-    graph.replay()
-    torch.cuda.synchronize()
-
-    # ---- timed region: K steps from graph replays (whole rotation cycles)
-    reps = max(1, -(-args.steps // n_rot))
-    steps = reps * n_rot
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        graph.replay()
-    t1.record()
-    torch.cuda.synchronize()
-    ms_total = t0.elapsed_time(t1)
-    ms_per_step = ms_total / steps
-    steps_per_s = 1000.0 / ms_per_step
-    mean_kv_bytes = sum(kv_bytes_step[(i // n_caches) % len(sets)] for i in range(n_rot)) / n_rot
-    log(f"[bench] graph: {steps} steps in {ms_total:.3f} ms -> {ms_per_step * 1e3:.2f} us/step")
+    graph = w.graph_of(step)
+    us_per_step, steps = w.time_graph(graph, args.steps)
+    ms_per_step = us_per_step * 1e-3
+    steps_per_s = 1e6 / us_per_step
+    log(f"[bench] graph: {steps} steps -> {us_per_step:.2f} us/step")
 
     # ---- per-kernel durations (a): each kernel alone, one rotation cycle of
     # back-to-back launches per HIP graph, timed with events around replays
-    def graph_of(fn):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.stream(g_stream):
-            with torch.cuda.graph(g, stream=g_stream):
-                for i in range(n_rot):
-                    fn(i)
-        return g
-
-    def split_only(i):
-        c = caches[i % n_caches]
-        ix = idx_sets[(i // n_caches) % len(sets)]
-        smla.smla_split(q, c, ix, out, lse, inp.scale, nsplit, ws)
-
-    part = smla.partials_view(ws, B, Lq, H, nsplit) if nsplit > 1 else None
-
-    def combine_only(i):
-        smla.smla_combine(part[0], part[1], out, lse)
-
-    def time_graph(g, reps):
-        g.replay()
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for _ in range(reps):
-            g.replay()
-        b.record()
-        torch.cuda.synchronize()
-        return 1e3 * a.elapsed_time(b) / (reps * n_rot)
-
-    kreps = max(1, -(-args.kernel_steps // n_rot))
-    split_us = time_graph(graph_of(split_only), kreps)
-    comb_us = time_graph(graph_of(combine_only), kreps) if nsplit > 1 else 0.0
-    kv_split = mean_kv_bytes
+    split_only, combine_only = w.split_fn(nsplit), w.combine_fn(nsplit) if nsplit > 1 else None
+    split_us, _ = w.time_graph(w.graph_of(split_only), args.kernel_steps)
+    comb_us = w.time_graph(w.graph_of(combine_only), args.kernel_steps)[0] if nsplit > 1 else 0.0
 
     # ---- per-kernel durations (b), diagnostic: events bracketing each eager
     # launch, queued behind a spin kernel so host enqueue time cannot leak in
-    ks = min(args.kernel_steps, 4 * n_rot)
+    ks = min(args.kernel_steps, 4 * w.n_rot)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(ks)]
     torch.cuda.synchronize()
     torch.cuda._sleep(200_000_000)
@@ -229,13 +272,34 @@ def main():
     log(f"[bench] kernels (graph, per launch): split {split_us:.2f} us, combine {comb_us:.2f} us; "
         f"(event-bracketed: split {ev_split_us:.2f} us, combine {ev_comb_us:.2f} us, eager step {eager_us:.2f} us)")
 
-    flops = T * H * K * 2 * (576 + 512) * (valid_rows[0] / max(1, T * K))
+    kv_split = w.mean_kv_bytes
+    flops = T * H * K * 2 * (576 + 512) * (w.valid_rows[0] / max(1, T * K))
     achieved = kv_split / (split_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         rec = json.load(open(TRAFFIC_FILE)).get(args.workload if args.workload != "spec" else f"spec{args.spec_ctx}")
         if rec and rec.get("kernel_sha") == kernel_sha() and rec.get("nsplit") == nsplit and not args.warm:
             traffic = rec.get("bytes_per_launch")
+
+    # ---- NSPLIT sweep of the same workload, and the batch-64 workload at the
+    # planner's NSPLIT beside a batch-1 headline (graph timing only)
+    sweep = []
+    if not args.no_sweep:
+        for ns in SWEEPS[args.workload] + ([] if nsplit in SWEEPS[args.workload] else [nsplit]):
+            sweep.append(dict(w.summary(ns, min(args.steps, 1024), min(args.kernel_steps, 512)),
+                              planner=(ns == w.plan())))
+            log(f"[bench] sweep nsplit={ns}: {sweep[-1]['us_per_step']:.2f} us/step, "
+                f"split {sweep[-1]['split_us']:.2f} us")
+    secondary = {}
+    if not args.no_sweep and args.workload in ("long", "tiny", "spec"):
+        w2 = Workload("batched", args.spec_ctx, args.warm, dev)
+        ns2 = w2.plan()
+        secondary["batched"] = dict(w2.summary(ns2, 512, 256), planner=True,
+                                    workload="batched: " + DESCRIPTIONS["batched"])
+        log(f"[bench] batched (planner nsplit={ns2}): {secondary['batched']['us_per_step']:.2f} us/step, "
+            f"split {secondary['batched']['split_us']:.2f} us")
+        del w2
+        torch.cuda.empty_cache()
 
     result = {
         "metric": METRIC,
@@ -252,13 +316,13 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": f"{args.workload}: " + DESCRIPTIONS[args.workload].format(ctx=args.spec_ctx),
-            "batch": B, "q_len": Lq, "heads": H, "topk": K, "kv_rows": inp.kv_rows,
+            "batch": B, "q_len": Lq, "heads": H, "topk": K, "kv_rows": w.inp.kv_rows,
             "nsplit": nsplit, "nsplit_from": "planner" if args.nsplit == 0 else "argument",
             "cache_state": "warm (no rotation)" if args.warm else
-                           f"cold: rotation over {n_caches} caches x {len(sets)} disjoint index sets",
+                           f"cold: rotation over {w.n_caches} caches x {len(w.sets)} disjoint index sets",
             "timing": "HIP graph replay of whole rotation cycles",
         },
-        "gathered_kv_gbps_per_step": round(mean_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "gathered_kv_gbps_per_step": round(w.mean_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "kernels_us": {"split": round(split_us, 3), "combine": round(comb_us, 3),
                        "method": "graph of back-to-back launches of one kernel, events around replays",
                        "event_bracketed_split": round(ev_split_us, 3),
@@ -279,8 +343,12 @@ def main():
                  "frac": round(flops / (split_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
         "kernel_sha": kernel_sha(),
     }
+    if sweep:
+        result["nsplit_sweep"] = sweep
+    if secondary:
+        result["secondary"] = secondary
     if args.cpu_seconds > 0:
-        result["cpu_baseline"] = cpu_baseline(inp, caches[0], torch.from_numpy(sets[0]), args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w.inp, w.caches[0], torch.from_numpy(w.sets[0]), args.cpu_seconds)
     print(json.dumps(result), flush=True)
 
 

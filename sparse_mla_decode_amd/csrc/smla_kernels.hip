@@ -650,94 +650,80 @@ constexpr int kCombC4 = kCombCols / 4;       // 4-float lanes per split group
 
 template <int SG, int PER>
 __global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) {
-  constexpr int NT = kCombC4 * SG;
-  __shared__ float w_s[kMaxNsplit];
-  __shared__ float red[2][(NT + 63) / 64];
   __shared__ floatx4 acc_s[SG][kCombC4];
+  __shared__ float m_s[SG], w_s[SG];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
   const int quarter = blockIdx.x & 3;
   const int th_id = blockIdx.x >> 2;          // token * heads + head
   const int tok = th_id / p.heads;
   const int h = th_id % p.heads;
   const int S = p.nsplit;
   const float* lse_in = p.part_lse + (int64_t)tok * S * p.heads + h;
-
-  // this thread's first round of partial-O loads goes out before the LSE
-  // pass, so the two memory latencies overlap
   const int c4 = tid % kCombC4;
   const int sg = tid / kCombC4;
   const int col = quarter * kCombCols + c4 * 4;
   const float* o_in = p.part_o + ((int64_t)tok * S * p.heads + h) * kDV + col;
   const int64_t stride = (int64_t)p.heads * kDV;
-  floatx4 v[PER];
-  auto load_round = [&](int s0) __attribute__((always_inline)) {
+
+  // Each thread merges its own splits (sg, sg + SG, ...) with a running
+  // maximum, its O slices and LSE values of a round loaded together:
+  // (m, w, acc) = (max LSE, sum exp(LSE - m), sum exp(LSE - m) O).
+  float m = -__builtin_inff(), w = 0.f;
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = sg; s0 < S; s0 += SG * PER) {
+    floatx4 v[PER];
+    float l[PER];
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
       const int s = s0 + u * SG;
       v[u] = s < S ? *(const floatx4*)(o_in + s * stride) : floatx4{0.f, 0.f, 0.f, 0.f};
+      l[u] = s < S ? lse_in[(int64_t)s * p.heads] : -__builtin_inff();
     }
-  };
-  load_round(sg);
-
-  // M = max_s LSE_s and W = sum_s exp(LSE_s - M), both block-wide
-  float mx = -__builtin_inff();
-  for (int s = tid; s < S; s += NT) mx = fmaxf(mx, lse_in[(int64_t)s * p.heads]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  if (lane == 0) red[0][wave] = mx;
-  __syncthreads();
-  mx = red[0][0];
-#pragma unroll
-  for (int w = 1; w < (NT + 63) / 64; ++w) mx = fmaxf(mx, red[0][w]);
-  float ws = 0.f;
-  for (int s = tid; s < S; s += NT) {
-    const float l = lse_in[(int64_t)s * p.heads];
-    const float w = (mx == -__builtin_inff() || l == -__builtin_inff())
-                        ? 0.f
-                        : __builtin_amdgcn_exp2f((l - mx) * kLog2e);
-    w_s[s] = w;
-    ws += w;
-  }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ws += __shfl_xor(ws, o, 64);
-  if (lane == 0) red[1][wave] = ws;
-  __syncthreads();
-  float wsum = 0.f;
-#pragma unroll
-  for (int w = 0; w < (NT + 63) / 64; ++w) wsum += red[1][w];
-
-  // sum_s w_s O_s over this thread's splits, PER loads in flight at a time
-  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int s0 = sg;;) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
-      const int s = s0 + u * SG;
-      const float w = s < S ? w_s[s] : 0.f;
-      // a zero weight (empty split) contributes nothing, whatever its slot holds
-      if (w != 0.f) acc += w * v[u];
-    }
-    s0 += SG * PER;
-    if (s0 >= S) break;
-    load_round(s0);
-  }
-  if (SG > 1) {
-    acc_s[sg][c4] = acc;
-    __syncthreads();
-    if (sg == 0) {
-#pragma unroll
-      for (int i = 1; i < SG; ++i) acc += acc_s[i][c4];
+      // an empty split (LSE = -inf) contributes nothing, whatever its slot holds
+      if (l[u] == -__builtin_inff()) continue;
+      if (l[u] > m) {
+        const float r = __builtin_amdgcn_exp2f((m - l[u]) * kLog2e);  // 0 while m = -inf
+        acc *= r;
+        w *= r;
+        m = l[u];
+      }
+      const float e = __builtin_amdgcn_exp2f((l[u] - m) * kLog2e);
+      acc += e * v[u];
+      w += e;
     }
   }
+  // merge the SG groups: M = max m_g, O = sum f_g acc_g / sum f_g w_g with
+  // f_g = exp(m_g - M), LSE = M + ln sum f_g w_g
+  acc_s[sg][c4] = acc;
+  if (c4 == 0) {
+    m_s[sg] = m;
+    w_s[sg] = w;
+  }
+  __syncthreads();
   if (sg != 0) return;
-  const bool any = wsum > 0.f;
-  const float inv = any ? 1.f / wsum : 0.f;
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int i = 0; i < SG; ++i) M = fmaxf(M, m_s[i]);
+  floatx4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (M != -__builtin_inff()) {
+#pragma unroll
+    for (int i = 0; i < SG; ++i) {
+      if (m_s[i] == -__builtin_inff()) continue;
+      const float f = __builtin_amdgcn_exp2f((m_s[i] - M) * kLog2e);
+      num += f * acc_s[i][c4];
+      den += f * w_s[i];
+    }
+  }
+  const bool any = den > 0.f;
+  const float inv = any ? 1.f / den : 0.f;
   const int64_t th = (int64_t)tok * p.heads + h;
   *(u32x2*)(p.out + th * kDV + col) =
-      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
-  if (tid == 0 && quarter == 0) p.lse[th] = any ? mx + __logf(wsum) : -__builtin_inff();
+      u32x2{pack_bf16x2(num[0] * inv, num[1] * inv), pack_bf16x2(num[2] * inv, num[3] * inv)};
+  if (tid == 0 && quarter == 0) p.lse[th] = any ? M + __logf(den) : -__builtin_inff();
 }
 
 // Combine for many (token, head) pairs: one thread per 4 output columns of
@@ -762,28 +748,33 @@ __global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineP
   const float* o_in = p.part_o + (tok * S * p.heads + h) * kDV + c4 * 4;
   const int64_t stride = (int64_t)p.heads * kDV;
 
+  // a round: CH splits' O slices and LSE values, all loads in flight together
   floatx4 v[CH];
+  float l[CH];
   auto load_round = [&](int s0) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
       const int s = s0 + u;
       v[u] = s < S ? *(const floatx4*)(o_in + s * stride) : floatx4{0.f, 0.f, 0.f, 0.f};
+      l[u] = s < S ? lse_in[(int64_t)s * p.heads] : -__builtin_inff();
     }
   };
-  load_round(0);  // in flight while the LSE values are read
-
+  load_round(0);
   float mx = -__builtin_inff();
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lse_in[(int64_t)s * p.heads]);
+  if (S <= CH) {  // one round holds every split: a single memory round trip
+#pragma unroll
+    for (int u = 0; u < CH; ++u) mx = fmaxf(mx, l[u]);
+  } else {
+    for (int s = 0; s < S; ++s) mx = fmaxf(mx, lse_in[(int64_t)s * p.heads]);
+  }
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   for (int s0 = 0;;) {
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int s = s0 + u;
-      const float l = s < S ? lse_in[(int64_t)s * p.heads] : -__builtin_inff();
-      const float w = (mx == -__builtin_inff() || l == -__builtin_inff())
+      const float w = (mx == -__builtin_inff() || l[u] == -__builtin_inff())
                           ? 0.f
-                          : __builtin_amdgcn_exp2f((l - mx) * kLog2e);
+                          : __builtin_amdgcn_exp2f((l[u] - mx) * kLog2e);
       wsum += w;
       // a zero weight (empty split) contributes nothing, whatever its slot holds
       if (w != 0.f) acc += w * v[u];
@@ -857,14 +848,21 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t st) {
   const int64_t pairs = (int64_t)p.tokens * p.heads;
   if (pairs >= kWideMinPairs) {
     const int64_t nwg = (pairs + kWidePairs - 1) / kWidePairs;
-    hipLaunchKernelGGL((combine_wide_kernel<8>), dim3((unsigned)nwg), dim3(128 * kWidePairs), 0,
-                       st, p);
+    // rounds of 4 splits when that covers them all (fewer registers, so every
+    // workgroup of a large grid is resident at once), else of 8
+    if (p.nsplit <= 4)
+      hipLaunchKernelGGL((combine_wide_kernel<4>), dim3((unsigned)nwg), dim3(128 * kWidePairs), 0,
+                         st, p);
+    else
+      hipLaunchKernelGGL((combine_wide_kernel<8>), dim3((unsigned)nwg), dim3(128 * kWidePairs), 0,
+                         st, p);
     return hipGetLastError();
   }
   // few pairs: the splits of one pair are spread over the waves of a
-  // workgroup (split groups x loads in flight per thread, sized so one pass
+  // workgroup (split groups x loads in flight per thread, sized so one round
   // covers up to 128 splits)
-  if (p.nsplit > 32) return launch_combine_t<16, 8>(p, st);
+  if (p.nsplit > 64) return launch_combine_t<16, 8>(p, st);
+  if (p.nsplit > 32) return launch_combine_t<16, 4>(p, st);
   if (p.nsplit > 8) return launch_combine_t<8, 4>(p, st);
   return launch_combine_t<4, 2>(p, st);
 }

@@ -52,6 +52,7 @@ DESCRIPTIONS = {
     "batched": "batch 64, q_len 1, 64 heads, top-2048 per sequence, 32768-token contexts in a paged pool of 32768 x 64-token pages",
     "spec": "batch 1, q_len 9 (9 verify tokens with their own lists), 8 heads, top-2048 of a {ctx}-row cache",
     "ragged": "batch 128, q_len 1, 128 heads, top-2048 per sequence, contexts uniform in [2048, 131072], paged 64-token pages",
+    "verify": "dense verify: batch 1, q_len 9, 8 heads, every row of a {ctx}-row cache (no list)",
 }
 
 
@@ -68,7 +69,10 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2048)
     ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default="long", choices=["tiny", "long", "batched", "spec", "ragged"])
+    ap.add_argument("--workload", default="long",
+                    choices=["tiny", "long", "batched", "spec", "ragged", "verify"])
+    ap.add_argument("--mode", default="rows", choices=["rows", "paged"],
+                    help="paged: positions + page tables mapped in the kernel (batched, ragged)")
     ap.add_argument("--spec-ctx", type=int, default=65536)
     ap.add_argument("--nsplit", type=int, default=0, help="0 = the planner's choice")
     ap.add_argument("--warm", action="store_true", help="no input rotation (cache-resident figure)")
@@ -98,14 +102,14 @@ def copy_calibration():
 
 
 SWEEPS = {"tiny": [1, 4], "long": [1, 16, 64, 128], "spec": [16, 64], "batched": [1, 2, 4, 8, 16],
-          "ragged": [1, 2, 4]}
+          "ragged": [1, 2, 4], "verify": [16, 64]}
 
 
 class Workload:
     """Device-resident inputs of one workload plus its rotation of
     (cache, index set) pairs, and the timing helpers over them."""
 
-    def __init__(self, name, spec_ctx, warm, dev):
+    def __init__(self, name, spec_ctx, warm, dev, mode="rows"):
         import numpy as np
         import torch
 
@@ -117,14 +121,31 @@ class Workload:
         self.inp = inp
         self.B, self.Lq, self.H, self.K = inp.batch, inp.q_len, inp.heads, inp.topk
         self.T = self.B * self.Lq
+        self.kind = "dense" if inp.dense else mode
+        if self.kind == "paged" and inp.pos is None:
+            raise SystemExit(f"--mode paged needs a paged workload (batched, ragged), not {name}")
+        self.pos_sets = None
         if warm:
             self.n_caches, self.sets = 1, [inp.idx]
+            self.pos_sets = [inp.pos] if self.kind == "paged" else None
+        elif self.kind == "dense":
+            # no list to vary: rotate over caches whose rows together exceed 512 MB
+            self.sets = [inp.idx]
+            self.n_caches = max(1, -(-(512 << 20) // (inp.kv_rows * ROW_BYTES)))
+        elif self.kind == "paged":
+            self.n_caches, self.sets, self.pos_sets = wl.rotation(inp, positions=True)
         else:
             self.n_caches, self.sets = wl.rotation(inp)
         self.q = wl.bits_to_torch(inp.q).to(dev)
         self.caches = [wl.device_pool(inp.kv_rows, (inp.pool_seed or 0) + 1000 * c, dev)
                        for c in range(self.n_caches)]
         self.idx_sets = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in self.sets]
+        if self.kind == "paged":
+            self.pos_dev = [torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in self.pos_sets]
+            self.table = torch.from_numpy(wl.block_table(inp)).to(dev)
+        if self.kind == "dense":
+            self.ctx_len = torch.tensor(inp.ctx, dtype=torch.int32, device=dev)
+            self.max_ctx = int(inp.ctx.max())
         self.out = torch.empty((self.B, self.Lq, self.H, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((self.B, self.Lq, self.H), dtype=torch.float32, device=dev)
         self.n_rot = self.n_caches * len(self.sets)
@@ -136,6 +157,8 @@ class Workload:
         torch.cuda.synchronize()
 
     def plan(self):
+        if self.kind == "dense":
+            return self.smla.smla_plan_nsplit_dense(self.B, self.Lq, self.H, self.K)
         return self.smla.smla_plan_nsplit(self.B, self.Lq, self.H, self.K)
 
     def workspace(self, nsplit):
@@ -148,11 +171,23 @@ class Workload:
 
     def step_fn(self, nsplit):
         ws = self.workspace(nsplit)
+        scale = self.inp.scale
 
-        def f(i, stream=None):
+        def rows(i, stream=None):
             c, ix = self._args(i)
-            self.smla.smla_decode(self.q, c, ix, self.out, self.lse, self.inp.scale, nsplit, ws, stream)
-        return f
+            self.smla.smla_decode(self.q, c, ix, self.out, self.lse, scale, nsplit, ws, stream)
+
+        def paged(i, stream=None):
+            c = self.caches[i % self.n_caches]
+            pos = self.pos_dev[(i // self.n_caches) % len(self.sets)]
+            self.smla.smla_decode_paged(self.q, c, self.table, 64, pos, self.out, self.lse, scale,
+                                        nsplit, ws, stream)
+
+        def dense(i, stream=None):
+            c = self.caches[i % self.n_caches]
+            self.smla.smla_decode_dense(self.q, c, self.ctx_len, self.max_ctx, self.out, self.lse,
+                                        scale, nsplit, workspace_t=ws, stream=stream)
+        return {"rows": rows, "paged": paged, "dense": dense}[self.kind]
 
     def split_fn(self, nsplit):
         ws = self.workspace(nsplit)
@@ -197,10 +232,19 @@ class Workload:
         torch.cuda.synchronize()
         return 1e3 * a.elapsed_time(b) / (reps * self.n_rot), reps * self.n_rot
 
+    def split_time(self, nsplit, kernel_steps, step_us):
+        """The split kernel's time per launch: a graph of split-only launches
+        (lists of rows), or for the paged and dense entry points, which have
+        no split-only call, the step minus a graph of combine-only launches."""
+        if self.kind == "rows":
+            return self.time_graph(self.graph_of(self.split_fn(nsplit)), kernel_steps)[0]
+        comb = self.time_graph(self.graph_of(self.combine_fn(nsplit)), kernel_steps)[0] if nsplit > 1 else 0.0
+        return step_us - comb
+
     def summary(self, nsplit, steps, kernel_steps):
         """Steps/s and the split kernel's time and gathered-KV rate at nsplit."""
         step_us, n = self.time_graph(self.graph_of(self.step_fn(nsplit)), steps)
-        split_us, _ = self.time_graph(self.graph_of(self.split_fn(nsplit)), kernel_steps)
+        split_us = self.split_time(nsplit, kernel_steps, step_us)
         return {"nsplit": nsplit, "us_per_step": round(step_us, 3), "steps_per_s": round(1e6 / step_us, 2),
                 "gathered_kv_gbps_per_step": round(self.mean_kv_bytes / (step_us * 1e-6) / 1e9, 2),
                 "split_us": round(split_us, 3),
@@ -227,11 +271,12 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t_setup = time.time()
-    w = Workload(args.workload, args.spec_ctx, args.warm, dev)
+    w = Workload(args.workload, args.spec_ctx, args.warm, dev, args.mode)
     B, Lq, H, K, T = w.B, w.Lq, w.H, w.K, w.T
     log(f"[bench] workload={args.workload} B={B} Lq={Lq} H={H} K={K} kv_rows={w.inp.kv_rows} "
         f"caches={w.n_caches} index_sets={len(w.sets)}")
     nsplit = args.nsplit if args.nsplit > 0 else w.plan()
+    rows_mode = w.kind == "rows"
     step = w.step_fn(nsplit)
     log(f"[bench] setup {time.time() - t_setup:.1f}s nsplit={nsplit} rotation={w.n_rot} steps")
 
@@ -248,9 +293,10 @@ def main():
 
     # ---- per-kernel durations (a): each kernel alone, one rotation cycle of
     # back-to-back launches per HIP graph, timed with events around replays
-    split_only, combine_only = w.split_fn(nsplit), w.combine_fn(nsplit) if nsplit > 1 else None
-    split_us, _ = w.time_graph(w.graph_of(split_only), args.kernel_steps)
+    combine_only = w.combine_fn(nsplit) if nsplit > 1 else None
     comb_us = w.time_graph(w.graph_of(combine_only), args.kernel_steps)[0] if nsplit > 1 else 0.0
+    split_us = w.split_time(nsplit, args.kernel_steps, us_per_step)
+    split_only = w.split_fn(nsplit) if rows_mode else step
 
     # ---- per-kernel durations (b), diagnostic: events bracketing each eager
     # launch, queued behind a spin kernel so host enqueue time cannot leak in
@@ -262,7 +308,7 @@ def main():
         ev[i][0].record()
         split_only(i)
         ev[i][1].record()
-        if nsplit > 1:
+        if nsplit > 1 and rows_mode:
             combine_only(i)
         ev[i][2].record()
     torch.cuda.synchronize()
@@ -277,7 +323,9 @@ def main():
     achieved = kv_split / (split_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE)).get(args.workload if args.workload != "spec" else f"spec{args.spec_ctx}")
+        key = args.workload + (str(args.spec_ctx) if args.workload in ("spec", "verify") else "") + \
+            ("_paged" if w.kind == "paged" else "")
+        rec = json.load(open(TRAFFIC_FILE)).get(key)
         if rec and rec.get("kernel_sha") == kernel_sha() and rec.get("nsplit") == nsplit and not args.warm:
             traffic = rec.get("bytes_per_launch")
 
@@ -291,7 +339,7 @@ def main():
             log(f"[bench] sweep nsplit={ns}: {sweep[-1]['us_per_step']:.2f} us/step, "
                 f"split {sweep[-1]['split_us']:.2f} us")
     secondary = {}
-    if not args.no_sweep and args.workload in ("long", "tiny", "spec"):
+    if not args.no_sweep and args.workload in ("long", "tiny", "spec") and w.kind == "rows":
         w2 = Workload("batched", args.spec_ctx, args.warm, dev)
         ns2 = w2.plan()
         secondary["batched"] = dict(w2.summary(ns2, 512, 256), planner=True,
@@ -315,7 +363,10 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: " + DESCRIPTIONS[args.workload].format(ctx=args.spec_ctx),
+            "workload": f"{args.workload}: " + DESCRIPTIONS[args.workload].format(ctx=args.spec_ctx)
+                        + ("; positions mapped through page tables in the kernel" if w.kind == "paged" else ""),
+            "entry_point": {"rows": "smla_decode", "paged": "smla_decode_paged",
+                            "dense": "smla_decode_dense"}[w.kind],
             "batch": B, "q_len": Lq, "heads": H, "topk": K, "kv_rows": w.inp.kv_rows,
             "nsplit": nsplit, "nsplit_from": "planner" if args.nsplit == 0 else "argument",
             "cache_state": "warm (no rotation)" if args.warm else
@@ -324,7 +375,9 @@ def main():
         },
         "gathered_kv_gbps_per_step": round(w.mean_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "kernels_us": {"split": round(split_us, 3), "combine": round(comb_us, 3),
-                       "method": "graph of back-to-back launches of one kernel, events around replays",
+                       "method": ("graph of back-to-back launches of one kernel, events around replays"
+                                  if rows_mode else
+                                  "split = graph step minus a graph of combine-only launches"),
                        "event_bracketed_split": round(ev_split_us, 3),
                        "event_bracketed_combine": round(ev_comb_us, 3),
                        "eager_step": round(eager_us, 3)},

@@ -118,6 +118,63 @@ int smla_decode(const void *q, const void *kv_cache, const int32_t *topk_idx, vo
                 int64_t kv_rows, void *workspace, size_t workspace_bytes, void *hip_stream);
 
 /*
+ * smla_decode over a paged cache, with the page-table lookup done in the
+ * kernel ("The Occupancy Hypothesis", "The Road to This Experiment": the
+ * serving cache is reached through per-sequence page tables).
+ *   block_table [batch, max_pages] int32: page ids of each sequence's pages
+ *     in order; a page id < 0 marks no page.  Required (non-NULL).
+ *   page_size: tokens per page (>= 1); the cache holds page id p's token t at
+ *     row p * page_size + t.
+ *   topk_pos [batch, q_len, topk] int32: positions within the token's own
+ *     sequence (not rows).  Position x maps to row
+ *     block_table[b][x / page_size] * page_size + x % page_size.
+ * A position that is < 0 or beyond the table (x / page_size >= max_pages), a
+ * missing page, or a row outside [0, kv_rows) carries zero weight, like -1 in
+ * smla_decode.  Results equal smla_decode's on the translated rows, bit for
+ * bit.  Rows must fit in int32.  Other arguments, the workspace and the
+ * errors as smla_decode.
+ */
+int smla_decode_paged(const void *q, const void *kv_cache, const int32_t *block_table,
+                      int max_pages, int page_size, const int32_t *topk_pos, void *out,
+                      float *lse, float scale, int nsplit, int batch, int q_len, int heads,
+                      int topk, int64_t kv_rows, void *workspace, size_t workspace_bytes,
+                      void *hip_stream);
+
+/*
+ * Dense KV-split decode: every query token of sequence b attends to all
+ * positions 0 .. ctx_len[b]-1 of its sequence, split into NSPLIT contiguous
+ * slices ("The Occupancy Hypothesis", "The Occupancy Insight" and "The
+ * Broader Context": the verify kernel splits the whole context, flash-decode
+ * style, partial + reduce).  There is no list: the implicit list of a token
+ * is 0 .. max_ctx-1, and entries at or beyond ctx_len[b] are masked.
+ *   ctx_len [batch] int32 (>= 0; values above max_ctx are attended only up to
+ *     max_ctx);  max_ctx: the longest context, the implicit list length
+ *     (plays topk's part for the planner and the workspace).
+ *   block_table / max_pages / page_size: as smla_decode_paged, or block_table
+ *     NULL for a flat cache in which position x is row x.
+ * Results equal smla_decode with topk_idx[b, i, :] = the rows of positions
+ * 0 .. ctx_len[b]-1 (then -1).  Since the q_len tokens of a sequence share
+ * those positions, for long contexts (max_ctx >= 8192, q_len > 1, q_len*heads
+ * <= SMLA_MAX_HEADS) the call treats them as q_len*heads heads of one token
+ * (q, out and lse are laid out alike either way): each context row is then
+ * gathered once per head block, not once per token.  NSPLIT 0 asks
+ * smla_plan_nsplit_dense; the workspace size is the same for either view.
+ * Errors as smla_decode (SMLA_ERR_NULL if ctx_len is NULL).
+ */
+/*
+ * NSPLIT the planner picks for smla_decode_dense of this shape: the
+ * smla_plan_nsplit rule applied to the shape the call runs as (folded or
+ * not, see smla_decode_dense).  Same returns as smla_plan_nsplit.
+ */
+int smla_plan_nsplit_dense(int batch, int q_len, int heads, int max_ctx);
+
+int smla_decode_dense(const void *q, const void *kv_cache, const int32_t *block_table,
+                      int max_pages, int page_size, const int32_t *ctx_len, int max_ctx,
+                      void *out, float *lse, float scale, int nsplit, int batch, int q_len,
+                      int heads, int64_t kv_rows, void *workspace, size_t workspace_bytes,
+                      void *hip_stream);
+
+/*
  * The split kernel alone ("The Split-K Imperative": each block computes a
  * partial attention output over its slice of the list).  With NSPLIT > 1 it
  * writes part_o / part_lse into the workspace (layout above; an empty slice

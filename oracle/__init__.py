@@ -15,7 +15,11 @@ Page citations (by title and section):
            Blackwell MLA Decode" -- "The Split-K Imperative".
   [NSPLIT] "The Occupancy Hypothesis: How One Kernel Parameter Unlocked 1.8x
            Decode Speedup on Blackwell" -- "The Occupancy Insight",
-           "The Broader Context".
+           "The Broader Context", "The Road to This Experiment".
+
+Paged and dense calls (``rows_of_positions``, ``dense_positions``) are
+defined as a plain decode over the rows their positions name, so the oracle
+for them is the index map below followed by ``decode``.
 """
 from __future__ import annotations
 
@@ -182,3 +186,47 @@ def combine(part_o, part_lse):
 
 def weights(q_row, kv, idx_row, scale: float):
     return default().weights(q_row, kv, idx_row, scale)
+
+
+def rows_of_positions(block_table, page_size: int, pos, kv_rows: int) -> np.ndarray:
+    """Cache rows of positions in paged sequences ([NSPLIT] "The Road to This
+    Experiment": the cache is reached through per-sequence page tables).
+
+    block_table [B, P] int: page ids of sequence b's pages in order (< 0: no
+    page), or None for a flat cache (position = row).  pos [B, Lq, K] int.
+    Position x of sequence b is row block_table[b, x // page_size] *
+    page_size + x % page_size.  Returns int32 rows of pos's shape, -1 for a
+    position < 0 or beyond the table, a missing page, or a row outside
+    [0, kv_rows).
+    """
+    pos = np.asarray(pos, np.int64)
+    out = np.full(pos.shape, -1, np.int64)
+    for b in range(pos.shape[0]):
+        for i in range(pos.shape[1]):
+            for k in range(pos.shape[2]):
+                x = int(pos[b, i, k])
+                if x < 0:
+                    continue
+                if block_table is None:
+                    row = x
+                else:
+                    page_i, offset = divmod(x, page_size)
+                    if page_i >= block_table.shape[1] or block_table[b, page_i] < 0:
+                        continue
+                    row = int(block_table[b, page_i]) * page_size + offset
+                if row < kv_rows:
+                    out[b, i, k] = row
+    return out.astype(np.int32)
+
+
+def dense_positions(ctx_len, max_ctx: int, q_len: int) -> np.ndarray:
+    """The implicit list of a dense call ([NSPLIT] "The Occupancy Insight",
+    "The Broader Context": the verify kernel splits the whole context): every
+    token of sequence b takes positions 0 .. ctx_len[b]-1, then -1 up to
+    max_ctx entries.  Returns int32 [B, q_len, max_ctx]."""
+    ctx_len = np.asarray(ctx_len, np.int64)
+    out = np.full((len(ctx_len), q_len, max_ctx), -1, np.int64)
+    for b, c in enumerate(ctx_len):
+        n = min(int(c), max_ctx)
+        out[b, :, :n] = np.arange(n)
+    return out.astype(np.int32)

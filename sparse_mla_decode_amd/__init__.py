@@ -3,11 +3,13 @@ top-k list on MI355X (gfx950).
 
 Argument marshalling only: every step of the computation runs in the HIP
 kernels behind the C ABI (include/smla.h).  torch supplies device memory and
-the stream; there is no CPU fallback, and importing this package without the
-built library raises.
+the stream; there is no CPU fallback.  The library is loaded on first use
+(so that the package's build module can run before it exists): any call
+without the built library raises ImportError.
 
 Functions carry the C names: smla_plan_nsplit, smla_plan_nsplit_cus,
-smla_workspace_bytes, smla_workspace_lse_offset, smla_decode, smla_split,
+smla_workspace_bytes, smla_workspace_lse_offset, smla_decode,
+smla_decode_paged, smla_decode_dense, smla_plan_nsplit_dense, smla_split,
 smla_combine, smla_status_str.
 """
 from __future__ import annotations
@@ -54,6 +56,14 @@ def _load() -> ctypes.CDLL:
     lib.smla_decode.restype = i32
     lib.smla_split.argtypes = call
     lib.smla_split.restype = i32
+    lib.smla_decode_paged.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, f32, i32, i32, i32, i32,
+                                      i32, i64, vp, sz, vp]
+    lib.smla_decode_paged.restype = i32
+    lib.smla_decode_dense.argtypes = [vp, vp, vp, i32, i32, vp, i32, vp, vp, f32, i32, i32, i32,
+                                      i32, i64, vp, sz, vp]
+    lib.smla_decode_dense.restype = i32
+    lib.smla_plan_nsplit_dense.argtypes = [i32, i32, i32, i32]
+    lib.smla_plan_nsplit_dense.restype = i32
     lib.smla_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
     lib.smla_combine.restype = i32
     lib.smla_status_str.argtypes = [i32]
@@ -61,34 +71,47 @@ def _load() -> ctypes.CDLL:
     return lib
 
 
-_lib = _load()
-lib = _lib  # the raw ctypes handle (tests call the C ABI through it)
+_handle = None
+
+
+def _lib_handle() -> ctypes.CDLL:
+    global _handle
+    if _handle is None:
+        _handle = _load()
+    return _handle
+
+
+def __getattr__(name):
+    # `lib`: the raw ctypes handle (tests call the C ABI through it)
+    if name == "lib":
+        return _lib_handle()
+    raise AttributeError(f"module {__name__!r} has no attribute {name!r}")
 
 
 def smla_status_str(status: int) -> str:
-    return _lib.smla_status_str(int(status)).decode()
+    return _lib_handle().smla_status_str(int(status)).decode()
 
 
 def smla_plan_nsplit(batch: int, q_len: int, heads: int, topk: int) -> int:
-    r = _lib.smla_plan_nsplit(batch, q_len, heads, topk)
+    r = _lib_handle().smla_plan_nsplit(batch, q_len, heads, topk)
     if r < 1:
         raise SmlaError(r, "smla_plan_nsplit")
     return r
 
 
 def smla_plan_nsplit_cus(cus: int, batch: int, q_len: int, heads: int, topk: int) -> int:
-    r = _lib.smla_plan_nsplit_cus(cus, batch, q_len, heads, topk)
+    r = _lib_handle().smla_plan_nsplit_cus(cus, batch, q_len, heads, topk)
     if r < 1:
         raise SmlaError(r, "smla_plan_nsplit_cus")
     return r
 
 
 def smla_workspace_bytes(batch: int, q_len: int, heads: int, nsplit: int) -> int:
-    return int(_lib.smla_workspace_bytes(batch, q_len, heads, nsplit))
+    return int(_lib_handle().smla_workspace_bytes(batch, q_len, heads, nsplit))
 
 
 def smla_workspace_lse_offset(batch: int, q_len: int, heads: int, nsplit: int) -> int:
-    return int(_lib.smla_workspace_lse_offset(batch, q_len, heads, nsplit))
+    return int(_lib_handle().smla_workspace_lse_offset(batch, q_len, heads, nsplit))
 
 
 def _ptr(t):
@@ -152,7 +175,7 @@ def smla_decode(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int = 0,
     nsplit 0 asks the planner.  A workspace is allocated when none is given
     and NSPLIT > 1.  Returns the NSPLIT used.
     """
-    return _call(_lib.smla_decode, "smla_decode", q, kv_cache, topk_idx, out, lse, scale, nsplit,
+    return _call(_lib_handle().smla_decode, "smla_decode", q, kv_cache, topk_idx, out, lse, scale, nsplit,
                  workspace_t, stream)[0]
 
 
@@ -160,8 +183,80 @@ def smla_split(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int,
                workspace_t=None, stream=None):
     """Split kernel alone.  Returns (nsplit, workspace) -- the partials live in
     the workspace (see partials_view) when NSPLIT > 1."""
-    return _call(_lib.smla_split, "smla_split", q, kv_cache, topk_idx, out, lse, scale, nsplit,
+    return _call(_lib_handle().smla_split, "smla_split", q, kv_cache, topk_idx, out, lse, scale, nsplit,
                  workspace_t, stream)
+
+
+def _check_table(block_table, what):
+    if block_table is None:
+        return 0
+    if block_table.dtype != torch.int32 or not block_table.is_contiguous() or block_table.dim() != 2:
+        raise ValueError(f"{what}: block_table must be a contiguous int32 [batch, max_pages] tensor")
+    return block_table.shape[1]
+
+
+def smla_decode_paged(q, kv_cache, block_table, page_size: int, topk_pos, out, lse, scale: float,
+                      nsplit: int = 0, workspace_t=None, stream=None) -> int:
+    """smla_decode with topk_pos [B, Lq, K] holding positions in each
+    sequence, mapped to cache rows through block_table [B, max_pages] inside
+    the kernel.  Returns the NSPLIT used."""
+    _check_tensors(q, kv_cache, topk_pos, out, lse)
+    b, lq, h, k = _shape(q, topk_pos)
+    max_pages = _check_table(block_table, "smla_decode_paged")
+    if block_table is None or block_table.shape[0] != b:
+        raise ValueError("smla_decode_paged: block_table must be [batch, max_pages]")
+    if nsplit == 0 and b * lq > 0:
+        nsplit = smla_plan_nsplit(b, lq, h, k)
+    ws = workspace_t
+    if ws is None and nsplit > 1:
+        ws = workspace(b, lq, h, nsplit, q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = _lib_handle().smla_decode_paged(_ptr(q), _ptr(kv_cache), _ptr(block_table), max_pages, page_size,
+                                _ptr(topk_pos), _ptr(out), _ptr(lse), float(scale), int(nsplit),
+                                b, lq, h, k, kv_cache.shape[0], _ptr(ws), ws_bytes, _stream(stream))
+    if rc != 0:
+        raise SmlaError(rc, "smla_decode_paged")
+    return nsplit
+
+
+def smla_plan_nsplit_dense(batch: int, q_len: int, heads: int, max_ctx: int) -> int:
+    r = _lib_handle().smla_plan_nsplit_dense(batch, q_len, heads, max_ctx)
+    if r < 1:
+        raise SmlaError(r, "smla_plan_nsplit_dense")
+    return r
+
+
+def dense_folds(q_len: int, heads: int, max_ctx: int) -> bool:
+    """Whether smla_decode_dense runs a sequence's tokens as heads of one
+    token (the rule stated in include/smla.h)."""
+    return q_len > 1 and q_len * heads <= 4096 and max_ctx >= 8192
+
+
+def smla_decode_dense(q, kv_cache, ctx_len, max_ctx: int, out, lse, scale: float, nsplit: int = 0,
+                      block_table=None, page_size: int = 1, workspace_t=None, stream=None) -> int:
+    """Dense KV-split decode: each token of sequence b attends to positions
+    0 .. ctx_len[b]-1 (rows through block_table when given, else position =
+    row).  Returns the NSPLIT used."""
+    _check_tensors(q, kv_cache, None, out, lse)
+    if q.dim() != 4 or q.shape[-1] != ROW:
+        raise ValueError(f"q must be [batch, q_len, heads, {ROW}], got {tuple(q.shape)}")
+    b, lq, h, _ = q.shape
+    if ctx_len.dtype != torch.int32 or ctx_len.shape != (b,) or not ctx_len.is_contiguous():
+        raise ValueError("smla_decode_dense: ctx_len must be a contiguous int32 [batch] tensor")
+    max_pages = _check_table(block_table, "smla_decode_dense")
+    if nsplit == 0 and b * lq > 0:
+        nsplit = smla_plan_nsplit_dense(b, lq, h, max_ctx)
+    ws = workspace_t
+    if ws is None and nsplit > 1:
+        ws = workspace(b, lq, h, nsplit, q.device)
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
+    rc = _lib_handle().smla_decode_dense(_ptr(q), _ptr(kv_cache), _ptr(block_table), max_pages, page_size,
+                                _ptr(ctx_len), int(max_ctx), _ptr(out), _ptr(lse), float(scale),
+                                int(nsplit), b, lq, h, kv_cache.shape[0], _ptr(ws), ws_bytes,
+                                _stream(stream))
+    if rc != 0:
+        raise SmlaError(rc, "smla_decode_dense")
+    return nsplit
 
 
 def partials_view(ws: torch.Tensor, batch: int, q_len: int, heads: int, nsplit: int):
@@ -184,7 +279,7 @@ def smla_combine(part_o: torch.Tensor, part_lse: torch.Tensor, out: torch.Tensor
     t, s, h = part_lse.shape
     if tuple(part_o.shape) != (t, s, h, DV):
         raise ValueError(f"part_o must be [{t}, {s}, {h}, {DV}], got {tuple(part_o.shape)}")
-    rc = _lib.smla_combine(_ptr(part_o), _ptr(part_lse), _ptr(out), _ptr(lse), t, h, s,
+    rc = _lib_handle().smla_combine(_ptr(part_o), _ptr(part_lse), _ptr(out), _ptr(lse), t, h, s,
                            _stream(stream))
     if rc != 0:
         raise SmlaError(rc, "smla_combine")

@@ -65,11 +65,34 @@ size_t ws_bytes(int64_t tokens, int heads, int nsplit) {
   return lse_offset(tokens, heads, nsplit) + (size_t)tokens * nsplit * heads * sizeof(float);
 }
 
-// Shared by smla_decode (combine = true) and smla_split (combine = false).
-int run(const void* q, const void* kv, const int32_t* idx, void* out, float* lse, float scale,
+// Where a call's rows come from (smla::RowSource and its tables).
+struct Source {
+  int src = smla::kSrcRows;
+  const int32_t* idx = nullptr;    // rows or positions [T, topk]
+  const int32_t* table = nullptr;  // [batch, max_pages] or null
+  const int32_t* ctx = nullptr;    // [batch] (dense)
+  int max_pages = 0, page_size = 1;
+};
+
+// A dense call's q_len tokens attend to the same positions, so they can be
+// folded into the head dimension: q [B, q_len, H, 576] is q [B, 1, q_len*H,
+// 576] byte for byte (out and lse likewise), and each context row is then
+// gathered once per head block rather than once per token.  Folding moves the
+// call to the larger head-block kernel, whose start-up costs more, so it pays
+// only for long contexts (measured for 9 tokens x 8 heads: 18.9 vs 22.0 us at
+// 4096 positions unfolded vs folded, 33.8 vs 29.1 at 16384, 93 vs 48 at 65536).
+constexpr int kDenseFoldMinCtx = 8192;
+bool dense_folds(int q_len, int heads, int max_ctx) {
+  return q_len > 1 && (int64_t)q_len * heads <= SMLA_MAX_HEADS && max_ctx >= kDenseFoldMinCtx;
+}
+
+// Shared by every decode entry point (combine = true) and smla_split
+// (combine = false).  topk is the list length (the longest context when dense).
+int run(const void* q, const void* kv, const Source& so, void* out, float* lse, float scale,
         int nsplit, int batch, int q_len, int heads, int topk, int64_t kv_rows, void* ws,
         size_t ws_size, void* stream, bool combine) {
   if (!dims_ok(batch, q_len, heads, topk) || kv_rows < 0) return SMLA_ERR_DIM;
+  if (so.table && (so.page_size < 1 || so.max_pages < 0)) return SMLA_ERR_DIM;
   if (nsplit < 0 || nsplit > SMLA_MAX_NSPLIT) return SMLA_ERR_NSPLIT;
   const int64_t tokens = (int64_t)batch * q_len;
   if (tokens == 0) return SMLA_OK;  // nothing to compute, nothing written
@@ -84,9 +107,14 @@ int run(const void* q, const void* kv, const int32_t* idx, void* out, float* lse
   const bool partials = nsplit > 1;
   const bool writes_out = !partials || combine;
 
-  if (!q || (topk > 0 && !idx) || (kv_rows > 0 && !kv)) return SMLA_ERR_NULL;
+  const bool lists = so.src != smla::kSrcDense;
+  if (!q || (lists && topk > 0 && !so.idx) || (kv_rows > 0 && !kv)) return SMLA_ERR_NULL;
+  if (so.src == smla::kSrcPositions && !so.table) return SMLA_ERR_NULL;
+  if (so.src == smla::kSrcDense && !so.ctx) return SMLA_ERR_NULL;
   if (writes_out && (!out || !lse)) return SMLA_ERR_NULL;
-  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(idx, 4)) return SMLA_ERR_ALIGN;
+  if (!aligned(q, 16) || !aligned(kv, 16) || !aligned(so.idx, 4) || !aligned(so.table, 4) ||
+      !aligned(so.ctx, 4))
+    return SMLA_ERR_ALIGN;
   if (writes_out && (!aligned(out, 16) || !aligned(lse, 4))) return SMLA_ERR_ALIGN;
   if (partials) {
     if (!ws || ws_size < ws_bytes(tokens, heads, nsplit)) return SMLA_ERR_WORKSPACE;
@@ -100,7 +128,13 @@ int run(const void* q, const void* kv, const int32_t* idx, void* out, float* lse
   smla::SplitParams sp;
   sp.q = (const uint16_t*)q;
   sp.kv = (const uint16_t*)kv;
-  sp.idx = idx;
+  sp.idx = so.idx;
+  sp.src = so.src;
+  sp.table = so.src == smla::kSrcRows ? nullptr : so.table;
+  sp.ctx = so.ctx;
+  sp.max_pages = so.max_pages;
+  sp.page_size = so.page_size;
+  sp.q_len = q_len;
   sp.out = (uint16_t*)out;
   sp.lse = lse;
   sp.part_o = partials ? (float*)ws : nullptr;
@@ -182,15 +216,58 @@ SMLA_API int smla_decode(const void* q, const void* kv_cache, const int32_t* top
                          float* lse, float scale, int nsplit, int batch, int q_len, int heads,
                          int topk, int64_t kv_rows, void* workspace, size_t workspace_bytes,
                          void* hip_stream) {
-  return run(q, kv_cache, topk_idx, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
+  Source so;
+  so.idx = topk_idx;
+  return run(q, kv_cache, so, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
              workspace, workspace_bytes, hip_stream, true);
+}
+
+SMLA_API int smla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
+                               int max_pages, int page_size, const int32_t* topk_pos, void* out,
+                               float* lse, float scale, int nsplit, int batch, int q_len,
+                               int heads, int topk, int64_t kv_rows, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  Source so;
+  so.src = smla::kSrcPositions;
+  so.idx = topk_pos;
+  so.table = block_table;
+  so.max_pages = max_pages;
+  so.page_size = page_size;
+  return run(q, kv_cache, so, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
+             workspace, workspace_bytes, hip_stream, true);
+}
+
+SMLA_API int smla_decode_dense(const void* q, const void* kv_cache, const int32_t* block_table,
+                               int max_pages, int page_size, const int32_t* ctx_len, int max_ctx,
+                               void* out, float* lse, float scale, int nsplit, int batch,
+                               int q_len, int heads, int64_t kv_rows, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  Source so;
+  so.src = smla::kSrcDense;
+  so.table = block_table;
+  so.ctx = ctx_len;
+  so.max_pages = block_table ? max_pages : 0;
+  so.page_size = page_size;
+  if (dense_folds(q_len, heads, max_ctx))
+    return run(q, kv_cache, so, out, lse, scale, nsplit, batch, 1, q_len * heads, max_ctx,
+               kv_rows, workspace, workspace_bytes, hip_stream, true);
+  return run(q, kv_cache, so, out, lse, scale, nsplit, batch, q_len, heads, max_ctx, kv_rows,
+             workspace, workspace_bytes, hip_stream, true);
+}
+
+SMLA_API int smla_plan_nsplit_dense(int batch, int q_len, int heads, int max_ctx) {
+  if (!dims_ok(batch, q_len, heads, max_ctx)) return SMLA_ERR_DIM;
+  if (dense_folds(q_len, heads, max_ctx)) return smla_plan_nsplit(batch, 1, q_len * heads, max_ctx);
+  return smla_plan_nsplit(batch, q_len, heads, max_ctx);
 }
 
 SMLA_API int smla_split(const void* q, const void* kv_cache, const int32_t* topk_idx, void* out,
                         float* lse, float scale, int nsplit, int batch, int q_len, int heads,
                         int topk, int64_t kv_rows, void* workspace, size_t workspace_bytes,
                         void* hip_stream) {
-  return run(q, kv_cache, topk_idx, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
+  Source so;
+  so.idx = topk_idx;
+  return run(q, kv_cache, so, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
              workspace, workspace_bytes, hip_stream, false);
 }
 

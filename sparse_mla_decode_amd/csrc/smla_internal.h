@@ -21,10 +21,24 @@ constexpr int kTileRows = 32;
 // list entries a split workgroup stages in LDS at a time
 constexpr int kListCap = 2048;
 
+// Where the rows of a token's list come from.
+enum RowSource : int {
+  kSrcRows = 0,       // idx holds cache rows
+  kSrcPositions = 1,  // idx holds positions in the token's sequence, mapped to
+                      // rows through the sequence's page table
+  kSrcDense = 2,      // no list: entry e is position e of the sequence (e <
+                      // ctx[b]), mapped through the page table if there is one
+};
+
 struct SplitParams {
   const uint16_t* q;    // [T, H, 576] bf16 bits
   const uint16_t* kv;   // [kv_rows, 576]
-  const int32_t* idx;   // [T, topk]
+  const int32_t* idx;   // [T, topk] (rows or positions; unused when dense)
+  int src;              // RowSource
+  const int32_t* table; // [batch, max_pages] page ids (-1 = none), or null:
+                        // positions are rows
+  const int32_t* ctx;   // [batch] context lengths (dense)
+  int max_pages, page_size, q_len;
   uint16_t* out;        // [T, H, 512] bf16 (nsplit == 1)
   float* lse;           // [T, H]            (nsplit == 1)
   float* part_o;        // [T, S, H, 512]    (nsplit > 1)

@@ -275,12 +275,31 @@ void split_kernel(SplitParams p) {
   // before q, so that the tile loads can start as soon as the list is in
   const int lo = min(split * p.per_split, p.topk);
   const int hi = min(lo + p.per_split, p.topk);
-  const int32_t* idx_row = p.idx + (int64_t)tok * p.topk;
+  const int32_t* idx_row = p.idx ? p.idx + (int64_t)tok * p.topk : nullptr;
+  // the row of list entry e, or -1: straight from the list, or a position of
+  // the token's sequence mapped through its page table (row = page id *
+  // page_size + offset in the page); a position outside the table, a missing
+  // page or a row outside the cache is masked like -1
+  const int seq = tok / p.q_len;
+  int ctx_seq = 0;
+  if (p.src == kSrcDense) ctx_seq = p.ctx[seq];
+  const int32_t* tab = p.table ? p.table + (int64_t)seq * p.max_pages : nullptr;
+  auto entry = [&](int e) __attribute__((always_inline)) -> int32_t {
+    if (p.src == kSrcRows) return idx_row[e];
+    const int32_t pos = p.src == kSrcDense ? (e < ctx_seq ? e : -1) : idx_row[e];
+    if (!tab || pos < 0) return pos;
+    const int pg_i = pos / p.page_size;
+    if (pg_i >= p.max_pages) return -1;
+    const int32_t pg = tab[pg_i];
+    if (pg < 0) return -1;
+    const int64_t row = (int64_t)pg * p.page_size + (pos - pg_i * p.page_size);
+    return row < p.kv_rows && row <= 0x7fffffff ? (int32_t)row : -1;
+  };
   constexpr int LI = kListCap / NT;
   int lv[LI];
   auto load_list = [&](int clo, int n_ent) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < LI; ++u) lv[u] = idx_row[clo + min(u * NT + tid, n_ent - 1)];
+    for (int u = 0; u < LI; ++u) lv[u] = entry(clo + min(u * NT + tid, n_ent - 1));
   };
   if (lo < hi) load_list(lo, min(hi - lo, kListCap));
 

@@ -23,6 +23,7 @@ HEADER = os.path.join(ROOT, "include", "smla.h")
 @pytest.fixture(scope="module")
 def smla():
     import sparse_mla_decode_amd as m
+    assert m.lib is not None  # the library loads (lazily) and binds every declared symbol
     return m
 
 
@@ -35,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["smla_plan_nsplit", "smla_plan_nsplit_cus", "smla_workspace_bytes",
-                            "smla_workspace_lse_offset", "smla_decode", "smla_split",
+                            "smla_workspace_lse_offset", "smla_decode", "smla_decode_paged",
+                            "smla_decode_dense", "smla_plan_nsplit_dense", "smla_split",
                             "smla_combine", "smla_status_str"]), names
 
 
@@ -208,6 +210,56 @@ def test_combine_arguments(smla):
     assert f(*ok, 1, 8, 1025, vp(0)) == -3
     assert f(vp(0x10004), *ok[1:], 1, 8, 4, vp(0)) == -5
     assert f(*ok, 0, 8, 4, vp(0)) == 0
+
+
+def _paged(smla, **kw):
+    a = dict(q=0x10000, kv=0x20000, table=0x70000, max_pages=16, page=64, pos=0x30000, out=0x40000,
+             lse=0x50000, scale=0.1, nsplit=1, batch=1, q_len=1, heads=8, topk=128, kv_rows=1024,
+             ws=0, ws_bytes=0, stream=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return smla.lib.smla_decode_paged(vp(a["q"]), vp(a["kv"]), vp(a["table"]), a["max_pages"],
+                                      a["page"], vp(a["pos"]), vp(a["out"]), vp(a["lse"]), a["scale"],
+                                      a["nsplit"], a["batch"], a["q_len"], a["heads"], a["topk"],
+                                      a["kv_rows"], vp(a["ws"]), a["ws_bytes"], vp(a["stream"]))
+
+
+def _dense(smla, **kw):
+    a = dict(q=0x10000, kv=0x20000, table=0, max_pages=0, page=1, ctx=0x30000, max_ctx=4096,
+             out=0x40000, lse=0x50000, scale=0.1, nsplit=1, batch=1, q_len=9, heads=8,
+             kv_rows=4096, ws=0, ws_bytes=0, stream=0)
+    a.update(kw)
+    vp = ctypes.c_void_p
+    return smla.lib.smla_decode_dense(vp(a["q"]), vp(a["kv"]), vp(a["table"]), a["max_pages"],
+                                      a["page"], vp(a["ctx"]), a["max_ctx"], vp(a["out"]),
+                                      vp(a["lse"]), a["scale"], a["nsplit"], a["batch"], a["q_len"],
+                                      a["heads"], a["kv_rows"], vp(a["ws"]), a["ws_bytes"],
+                                      vp(a["stream"]))
+
+
+def test_paged_arguments(smla):
+    # fake pointers: every call must fail validation and launch nothing
+    assert _paged(smla, table=0) == -1          # the page table is required
+    assert _paged(smla, pos=0) == -1
+    assert _paged(smla, page=0) == -2
+    assert _paged(smla, max_pages=-1) == -2
+    assert _paged(smla, table=0x70002) == -5
+    assert _paged(smla, pos=0x30002) == -5
+    assert _paged(smla, nsplit=2000) == -3
+    assert _paged(smla, nsplit=4) == -4          # no workspace
+    assert _paged(smla, q=0, kv=0, pos=0, table=0, out=0, lse=0, batch=0) == 0
+
+
+def test_dense_arguments(smla):
+    assert _dense(smla, ctx=0) == -1            # context lengths are required
+    assert _dense(smla, q=0) == -1
+    assert _dense(smla, ctx=0x30002) == -5
+    assert _dense(smla, max_ctx=-1) == -2
+    assert _dense(smla, table=0x70000, max_pages=4, page=0) == -2
+    assert _dense(smla, table=0x70000, max_pages=-4, page=64) == -2
+    assert _dense(smla, nsplit=4) == -4
+    # a flat cache needs no table; zero tokens launch nothing
+    assert _dense(smla, q=0, kv=0, ctx=0, out=0, lse=0, batch=0) == 0
 
 
 def test_planner_path_without_device(smla):

@@ -297,3 +297,50 @@ def test_mutants_are_caught(name):
             except (AssertionError, RuntimeError, FloatingPointError, ValueError):
                 caught.append(pin.__name__)
         assert caught, f"no pin catches mutant {name}"
+
+
+# ------------------------------------------------------ paged and dense maps
+
+def test_pin_rows_of_positions_worked_example():
+    # sequence 0 owns pages 3, 0, 2 (in that order), 4 tokens per page; page
+    # slot 3 of sequence 1 is missing.  Position 5 is page 1 (id 0), offset 1
+    # -> row 1; position 9 is page 2 (id 2), offset 1 -> row 9; position 12 is
+    # page 3, beyond sequence 0's three pages -> masked; position 3 of
+    # sequence 1 is its page 0 (id 1), offset 3 -> row 7; its position 13 is
+    # page 3, id -1 -> masked.  With a 12-row cache, position 0 of sequence 0
+    # (page id 3, offset 0 = row 12) and position 8 of sequence 1 (page id 3,
+    # offset 0 = row 12) fall outside the cache -> masked.
+    table = np.array([[3, 0, 2, -1], [1, 2, 3, -1]], np.int32)
+    pos = np.array([[[0, 5, 9, 12, -1]], [[3, 13, 8, -7, 4]]], np.int32)
+    got = oracle.rows_of_positions(table, 4, pos, kv_rows=12)
+    assert got[0, 0].tolist() == [-1, 1, 9, -1, -1]
+    assert got[1, 0].tolist() == [7, -1, -1, -1, 8]
+    got16 = oracle.rows_of_positions(table, 4, pos, kv_rows=16)
+    assert got16[0, 0].tolist() == [12, 1, 9, -1, -1]
+    assert got16[1, 0].tolist() == [7, -1, 12, -1, 8]
+
+
+def test_pin_rows_of_positions_identity_and_bijection():
+    rng = np.random.default_rng(7)
+    P, page = 6, 8
+    ident = np.tile(np.arange(P, dtype=np.int32), (2, 1))
+    pos = rng.integers(-3, P * page + 5, size=(2, 3, 40)).astype(np.int32)
+    rows = oracle.rows_of_positions(ident, page, pos, kv_rows=P * page)
+    inside = (pos >= 0) & (pos < P * page)
+    assert (rows[inside] == pos[inside]).all() and (rows[~inside] == -1).all()
+    # a permuted table maps the sequence's positions one-to-one onto its pages' rows
+    perm = rng.permutation(P).astype(np.int32)[None, :]
+    allpos = np.arange(P * page, dtype=np.int32)[None, None, :]
+    r = oracle.rows_of_positions(perm, page, allpos, kv_rows=P * page)
+    assert sorted(r.ravel().tolist()) == list(range(P * page))
+    # flat cache: positions are rows, clipped at kv_rows
+    flat = oracle.rows_of_positions(None, page, pos, kv_rows=20)
+    assert ((flat == pos) | (flat == -1)).all() and (flat[(pos >= 0) & (pos < 20)] >= 0).all()
+
+
+def test_pin_dense_positions():
+    d = oracle.dense_positions([3, 0, 7], max_ctx=5, q_len=2)
+    assert d.shape == (3, 2, 5)
+    assert d[0, 1].tolist() == [0, 1, 2, -1, -1]
+    assert d[1, 0].tolist() == [-1] * 5
+    assert d[2, 0].tolist() == [0, 1, 2, 3, 4]

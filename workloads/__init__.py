@@ -73,6 +73,8 @@ class Inputs:
     pool_seed: Optional[int] = None
     ctx: Optional[np.ndarray] = None          # per-sequence context lengths
     page_table: Optional[list] = None         # per-sequence physical page ids
+    pos: Optional[np.ndarray] = None          # [B, Lq, K] positions behind idx (paged, dense)
+    dense: bool = False                       # the list is every position of the context
 
     @property
     def batch(self): return self.q.shape[0]
@@ -125,22 +127,75 @@ def paged_inputs(name: str, seed: int, heads: int, topk: int, ctx: np.ndarray,
         off += pages[b]
     rng = np.random.default_rng(seed + SUB_IDX)
     idx = np.empty((batch, q_len, topk), np.int32)
+    pos_all = np.empty((batch, q_len, topk), np.int32)
     for b in range(batch):
         for i in range(q_len):
             pos = sample_topk(rng, int(ctx[b]), topk).astype(np.int64)
-            phys = np.where(pos >= 0, table[b][np.maximum(pos, 0) // PAGE] * PAGE + np.maximum(pos, 0) % PAGE, -1)
-            idx[b, i] = phys.astype(np.int32)
+            pos_all[b, i] = pos
+            idx[b, i] = physical_rows(table[b], pos)
     kv_rows = total_pages * PAGE
     q = normal_bf16(np.random.default_rng(seed + SUB_Q), (batch, q_len, heads, D))
     kv = normal_bf16(np.random.default_rng(seed + SUB_KV), (kv_rows, D)) if with_kv else None
     return Inputs(name, q, kv, idx, kv_rows, pool_seed=None if with_kv else seed + SUB_KV,
-                  ctx=ctx, page_table=table)
+                  ctx=ctx, page_table=table, pos=pos_all)
+
+
+def physical_rows(pages: np.ndarray, pos: np.ndarray) -> np.ndarray:
+    """Rows of one sequence's positions in the pool (input construction: the
+    harness's own page bookkeeping, -1 stays -1)."""
+    pos = np.asarray(pos, np.int64)
+    out = np.full(pos.shape, -1, np.int64)
+    ok = pos >= 0
+    if ok.any():
+        out[ok] = np.asarray(pages, np.int64)[pos[ok] // PAGE] * PAGE + pos[ok] % PAGE
+    return out.astype(np.int32)
+
+
+def block_table(inp: Inputs) -> np.ndarray:
+    """The paged workload's page tables as one int32 [B, max_pages] array,
+    padded with -1 (no page)."""
+    width = max(len(t) for t in inp.page_table)
+    out = np.full((len(inp.page_table), width), -1, np.int32)
+    for b, t in enumerate(inp.page_table):
+        out[b, : len(t)] = t
+    return out
+
+
+def dense_inputs(name: str, seed: int, batch: int, q_len: int, heads: int, ctx,
+                 paged: bool, with_kv: bool = True) -> Inputs:
+    """Dense verify inputs: every token of sequence b attends to all ctx[b]
+    positions of its context.  Flat (paged=False): one cache whose first
+    ctx[b] rows are sequence b's context.  Paged: a permuted pool of 64-token
+    pages as in paged_inputs.  idx holds the rows of positions 0..ctx[b]-1
+    (then -1) up to max(ctx) entries, pos the positions themselves."""
+    ctx = np.asarray(ctx, np.int64)
+    max_ctx = int(ctx.max()) if len(ctx) else 0
+    pos = np.full((batch, q_len, max_ctx), -1, np.int32)
+    for b in range(batch):
+        pos[b, :, : ctx[b]] = np.arange(ctx[b])
+    if paged:
+        pages = (ctx + PAGE - 1) // PAGE
+        perm = np.random.default_rng(seed + SUB_PAGES).permutation(int(pages.sum())).astype(np.int64)
+        table, off = [], 0
+        for b in range(batch):
+            table.append(perm[off: off + pages[b]])
+            off += pages[b]
+        kv_rows = int(pages.sum()) * PAGE
+        idx = np.stack([np.stack([physical_rows(table[b], pos[b, i]) for i in range(q_len)])
+                        for b in range(batch)]).astype(np.int32)
+    else:
+        table, kv_rows, idx = None, max_ctx, pos.copy()
+    q = normal_bf16(np.random.default_rng(seed + SUB_Q), (batch, q_len, heads, D))
+    kv = normal_bf16(np.random.default_rng(seed + SUB_KV), (kv_rows, D)) if with_kv else None
+    return Inputs(name, q, kv, idx, kv_rows, pool_seed=None if with_kv else seed + SUB_KV,
+                  ctx=ctx, page_table=table, pos=pos, dense=True)
 
 
 # The five workload shapes: (1) tiny, (2) single request at long context,
 # (3) batched decode over a paged pool, (4) speculative-verify shape (9 query
-# tokens, each with its own list), (5) large ragged batch over a paged pool.
-WORKLOADS = ("tiny", "long", "batched", "spec", "ragged")
+# tokens, each with its own list), (5) large ragged batch over a paged pool;
+# and the dense verify shape: 9 query tokens over the whole context.
+WORKLOADS = ("tiny", "long", "batched", "spec", "ragged", "verify")
 
 
 def workload(name: str, *, spec_ctx: int = 65536, with_kv: Optional[bool] = None,
@@ -164,6 +219,9 @@ def workload(name: str, *, spec_ctx: int = 65536, with_kv: Optional[bool] = None
     if name == "spec":
         return flat_inputs(f"spec{spec_ctx}", 4000, 1, 9, 8, spec_ctx, 2048,
                            with_kv=True if with_kv is None else with_kv)
+    if name == "verify":
+        return dense_inputs(f"verify{spec_ctx}", 6000, 1, 9, 8, [spec_ctx], paged=False,
+                            with_kv=True if with_kv is None else with_kv)
     if name == "ragged":
         rng = np.random.default_rng(5000 + SUB_CTX)
         ctx = rng.integers(2048, 131072, size=128, endpoint=True).astype(np.int64)
@@ -180,7 +238,8 @@ def _first_sequences(inp: Inputs, b: int) -> Inputs:
         return inp
     return dataclasses.replace(inp, q=inp.q[:b], idx=inp.idx[:b],
                                ctx=None if inp.ctx is None else inp.ctx[:b],
-                               page_table=None if inp.page_table is None else inp.page_table[:b])
+                               page_table=None if inp.page_table is None else inp.page_table[:b],
+                               pos=None if inp.pos is None else inp.pos[:b])
 
 
 def device_pool(kv_rows: int, seed: int, device, chunk_rows: int = 1 << 18):
@@ -262,7 +321,7 @@ def oracle_view(inp: Inputs, kv_dev=None, seqs=None):
 
 # ------------------------------------------------------------ bench rotation
 
-def rotation(inp: Inputs, min_bytes: int = 512 << 20, seed: int = 77):
+def rotation(inp: Inputs, min_bytes: int = 512 << 20, seed: int = 77, positions: bool = False):
     """Input sets for timing with cold caches.
 
     Successive timed steps cycle through (cache, index set) pairs whose
@@ -274,7 +333,8 @@ def rotation(inp: Inputs, min_bytes: int = 512 << 20, seed: int = 77):
 
     Returns (n_caches, sets): step i uses cache i % n_caches and
     sets[(i // n_caches) % len(sets)], each set an int32 [B, Lq, K] array.
-    Paged workloads use their one pool (n_caches == 1).
+    Paged workloads use their one pool (n_caches == 1); with positions=True
+    they return (1, sets, position_sets), the positions behind each set.
     """
     rng = np.random.default_rng(seed)
     B, Lq, K = inp.idx.shape
@@ -298,9 +358,10 @@ def rotation(inp: Inputs, min_bytes: int = 512 << 20, seed: int = 77):
     valid = int((inp.idx >= 0).sum())
     need = -(-min_bytes // max(1, valid * ROW_BYTES))
     n_sets = max(1, min(need, int(max(1, (ctx // K).min()))))
-    sets = []
+    sets, pos_sets = [], []
     for s in range(n_sets):
         idx = np.empty((B, Lq, K), np.int32)
+        pset = np.empty((B, Lq, K), np.int32)
         for b in range(B):
             perm = rng.permutation(int(ctx[b]))
             for i in range(Lq):
@@ -309,11 +370,11 @@ def rotation(inp: Inputs, min_bytes: int = 512 << 20, seed: int = 77):
                     pos = perm[j * K:(j + 1) * K].astype(np.int64)
                 else:
                     pos = sample_topk(rng, int(ctx[b]), K).astype(np.int64)
-                page = inp.page_table[b]
-                safe = np.maximum(pos, 0)
-                idx[b, i] = np.where(pos >= 0, page[safe // PAGE] * PAGE + safe % PAGE, -1)
+                pset[b, i] = pos
+                idx[b, i] = physical_rows(inp.page_table[b], pos)
         sets.append(idx)
-    return 1, sets
+        pos_sets.append(pset)
+    return (1, sets, pos_sets) if positions else (1, sets)
 
 
 def edge_inputs(seed: int = 4242, kv_rows: int = 4096, heads: int = 16, topk: int = 300) -> Inputs:

@@ -150,6 +150,10 @@ class Workload:
         self.lse = torch.empty((self.B, self.Lq, self.H), dtype=torch.float32, device=dev)
         self.n_rot = self.n_caches * len(self.sets)
         self.valid_rows = [int((x >= 0).sum()) for x in self.sets]  # every set points inside its cache
+        if self.kind == "dense":
+            # every query token of a sequence attends to the same context rows:
+            # count each context row once (per query token it would exceed HBM)
+            self.valid_rows = [int(np.minimum(inp.ctx, inp.idx.shape[-1]).sum())]
         self.mean_kv_bytes = sum(self.valid_rows[(i // self.n_caches) % len(self.sets)] * ROW_BYTES
                                  for i in range(self.n_rot)) / self.n_rot
         self.stream = torch.cuda.Stream()
@@ -319,7 +323,7 @@ def main():
         f"(event-bracketed: split {ev_split_us:.2f} us, combine {ev_comb_us:.2f} us, eager step {eager_us:.2f} us)")
 
     kv_split = w.mean_kv_bytes
-    flops = T * H * K * 2 * (576 + 512) * (w.valid_rows[0] / max(1, T * K))
+    flops = T * H * K * 2 * (576 + 512) * (int((w.sets[0] >= 0).sum()) / max(1, T * K))
     achieved = kv_split / (split_us * 1e-6) / 1e9
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
@@ -390,6 +394,8 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "bytes_per_launch": int(kv_split),
+            "bytes": ("context rows x 1152 B, each row once (all query tokens share them)"
+                      if w.kind == "dense" else "valid list entries x 1152 B"),
         },
         "mfma": {"achieved_tflops": round(flops / (split_us * 1e-6) / 1e12, 3),
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,

@@ -202,7 +202,7 @@ __device__ __forceinline__ void dma_tile(const u32x4* src, uint8_t* lds,
 // Keeps a value in its registers up to this point.
 __device__ __forceinline__ void keep_live(uint64_t v) { asm volatile("" ::"v"(v)); }
 
-template <int HG, int NCS, int GPW, int TR, int NBUF, bool KSPLIT>
+template <int HG, int NCS, int GPW, int TR, int NBUF, bool KSPLIT, int SRC>
 __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
 __attribute__((amdgpu_waves_per_eu(GPW == 1 && (NBUF == 2 || KSPLIT) ? 2 : 1)))
 void split_kernel(SplitParams p) {
@@ -280,13 +280,15 @@ void split_kernel(SplitParams p) {
   // the token's sequence mapped through its page table (row = page id *
   // page_size + offset in the page); a position outside the table, a missing
   // page or a row outside the cache is masked like -1
-  const int seq = tok / p.q_len;
+  // (SRC, the row source, is a template argument: a plain list of rows
+  // compiles to nothing but the list load)
+  const int seq = SRC == kSrcRows ? 0 : tok / p.q_len;
   int ctx_seq = 0;
-  if (p.src == kSrcDense) ctx_seq = p.ctx[seq];
-  const int32_t* tab = p.table ? p.table + (int64_t)seq * p.max_pages : nullptr;
+  if (SRC == kSrcDense) ctx_seq = p.ctx[seq];
+  const int32_t* tab = SRC != kSrcRows && p.table ? p.table + (int64_t)seq * p.max_pages : nullptr;
   auto entry = [&](int e) __attribute__((always_inline)) -> int32_t {
-    if (p.src == kSrcRows) return idx_row[e];
-    const int32_t pos = p.src == kSrcDense ? (e < ctx_seq ? e : -1) : idx_row[e];
+    if constexpr (SRC == kSrcRows) return idx_row[e];
+    const int32_t pos = SRC == kSrcDense ? (e < ctx_seq ? e : -1) : idx_row[e];
     if (!tab || pos < 0) return pos;
     const int pg_i = pos / p.page_size;
     if (pg_i >= p.max_pages) return -1;
@@ -825,8 +827,20 @@ template <int HG, int NCS, int GPW, int TR, int NBUF, bool KSPLIT>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
   static_assert(TR == kTileRows, "the planner's tile");
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
-  hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF, KSPLIT>), dim3((unsigned)nwg),
-                     dim3(64 * (HG / GPW) * NCS), 0, st, p);
+  const dim3 grid((unsigned)nwg), block(64 * (HG / GPW) * NCS);
+  switch (p.src) {
+    case kSrcPositions:
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF, KSPLIT, kSrcPositions>), grid, block,
+                         0, st, p);
+      break;
+    case kSrcDense:
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF, KSPLIT, kSrcDense>), grid, block, 0,
+                         st, p);
+      break;
+    default:
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF, KSPLIT, kSrcRows>), grid, block, 0,
+                         st, p);
+  }
   return hipGetLastError();
 }
 

@@ -20,6 +20,9 @@ constexpr float kRescaleLog2 = 8.0f;
 constexpr int kTileRows = 32;
 // list entries a split workgroup stages in LDS at a time
 constexpr int kListCap = 2048;
+// ... per configuration: the K-split workgroup whose 4 waves share one head
+// group (column quarters) stages half as many, so that two fit a CU's LDS
+constexpr int split_list_cap(int ncs, bool ksplit) { return ksplit && ncs == 4 ? 1024 : kListCap; }
 
 // Where the rows of a token's list come from.
 enum RowSource : int {

@@ -207,7 +207,7 @@ __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
 __attribute__((amdgpu_waves_per_eu(GPW == 1 && (NBUF == 2 || KSPLIT) ? 2 : 1)))
 void split_kernel(SplitParams p) {
   static_assert(HG % GPW == 0, "whole head groups per wave");
-  static_assert(!KSPLIT || NCS == 2, "K-split pairs the two column halves");
+  static_assert(!KSPLIT || NCS % 2 == 0, "K-split pairs waves of opposite parity");
   constexpr int NT = 64 * (HG / GPW) * NCS;
   // waves that issue the tile loads: all of them, or half of them when the
   // tile's wave loads do not split evenly (36 per 32-row tile: not over 8)
@@ -227,6 +227,13 @@ void split_kernel(SplitParams p) {
   // with always-issued refills the tile count of a chunk is rounded up to a
   // multiple of NBUF; the list's tail pad (all -1) covers those tiles
   constexpr int kListPad = NBUF > 2 ? TR * NBUF : 0;
+  // list entries staged at a time (the K-split 16-head workgroup stages
+  // 1024 so that two of them fit a CU's LDS)
+  constexpr int LCAP = split_list_cap(NCS, KSPLIT);
+  // K-split: one slot of partial scores per (head group, K parity); the
+  // waves of a head group with cs < 2 write them, every wave reads the other
+  // parity's slot
+  constexpr int kXsSlots = KSPLIT ? (NT / 64 / NCS) * 2 : 1;
 
   // One __shared__ object per buffer: each access below names its buffer at
   // compile time, which lets the compiler see that a read of one buffer does
@@ -236,9 +243,9 @@ void split_kernel(SplitParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[NBUF > 2 ? kTileBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t tb3[NBUF > 3 ? kTileBytes : 16];
-  __shared__ __attribute__((aligned(16))) int list_s[kListCap + kListPad];
-  // partial S^T of every wave (K-split pairs exchange them), [wave][rb][lane]
-  __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? (NT / 64) * GPW * RB * 64 : 1];
+  __shared__ __attribute__((aligned(16))) int list_s[LCAP + kListPad];
+  // partial S^T per (head group, parity) slot: [slot][gi][rb][lane]
+  __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? kXsSlots * GPW * RB * 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -297,13 +304,13 @@ void split_kernel(SplitParams p) {
     const int64_t row = (int64_t)pg * p.page_size + (pos - pg_i * p.page_size);
     return row < p.kv_rows && row <= 0x7fffffff ? (int32_t)row : -1;
   };
-  constexpr int LI = kListCap / NT;
+  constexpr int LI = LCAP / NT;
   int lv[LI];
   auto load_list = [&](int clo, int n_ent) __attribute__((always_inline)) {
 #pragma unroll
     for (int u = 0; u < LI; ++u) lv[u] = entry(clo + min(u * NT + tid, n_ent - 1));
   };
-  if (lo < hi) load_list(lo, min(hi - lo, kListCap));
+  if (lo < hi) load_list(lo, min(hi - lo, LCAP));
 
   // with K-split pairs wave half cs holds K-steps 2k + cs
   bf16x8 qb[GPW][KSW];
@@ -312,7 +319,7 @@ void split_kernel(SplitParams p) {
     const u32x4* qrow = h_ok[gi]
                             ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + h[gi]) * kRow) + g
                             : g_zero_row + g;
-    if (KSPLIT) qrow += 4 * cs;
+    if (KSPLIT) qrow += 4 * (cs & 1);
 #pragma unroll
     for (int k = 0; k < KSW; ++k)
       qb[gi][k] = __builtin_bit_cast(bf16x8, qrow[k * 4 * (KSPLIT ? 2 : 1)]);
@@ -323,8 +330,8 @@ void split_kernel(SplitParams p) {
   const int hq = hsw(l16);
   const int qk_even = l16 * 128 + (g ^ hq) * 16;
   const int qk_odd = l16 * 128 + ((g ^ hq) ^ 4) * 16;
-  // K-split: K-step 2k + cs is block k, in-block half cs
-  const int qk_half = cs ? qk_odd : qk_even;
+  // K-split: K-step 2k + par is block k, in-block half par (par = cs & 1)
+  const int qk_half = (cs & 1) ? qk_odd : qk_even;
   // V^T transpose read: source lane (e, s') of group g reads row 4g + e
   // (+16 for slots 4-7, +32 per PV K-step), columns 16*cb + 4s' .. +3 =
   // granule 2cb + b0 (b0 = s' >> 1) at byte 8*b1 (b1 = s' & 1); in-block
@@ -373,7 +380,7 @@ void split_kernel(SplitParams p) {
   // known to be complete.
   static_assert(DP == 1, "one row per lane per tile");
   auto issue = [&](uint8_t* buf, int t, int ntiles) __attribute__((always_inline)) -> uint64_t {
-    const int e = min(t * TR + dma_row[0], kListCap - 1);  // inside list_s
+    const int e = min(t * TR + dma_row[0], LCAP - 1);  // inside list_s
     const int32_t r = t < ntiles ? list_s[e] : -1;
     const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
     const u32x4* src = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran[0];
@@ -413,19 +420,21 @@ void split_kernel(SplitParams p) {
       // exchange the half sums with the partner wave (same heads, other
       // parity); own + partner is the same sum in both waves (addition
       // commutes), so both hold bitwise the same scores
+      const int par = cs & 1;
+      const int my_slot = (wave / NCS) * 2 + par, other_slot = my_slot ^ 1;
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb) {
           sacc[gi][rb] = acc2[0][gi][rb] + acc2[1][gi][rb];
-          xs[((wave * GPW + gi) * RB + rb) * 64 + lane] = sacc[gi][rb];
+          if (cs < 2) xs[((my_slot * GPW + gi) * RB + rb) * 64 + lane] = sacc[gi][rb];
         }
       barrier_lds();
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi)
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
-          sacc[gi][rb] += xs[(((wave ^ 1) * GPW + gi) * RB + rb) * 64 + lane];
+          sacc[gi][rb] += xs[((other_slot * GPW + gi) * RB + rb) * 64 + lane];
     } else {
 #pragma unroll
       for (int gi = 0; gi < GPW; ++gi)
@@ -564,16 +573,16 @@ void split_kernel(SplitParams p) {
       list_s[e] = (e < n_ent && (uint32_t)lv[u] < kv32) ? lv[u] : -1;
     }
     static_assert(kListPad <= NT, "one pad entry per thread at most");
-    if (kListPad > 0 && tid < kListPad) list_s[kListCap + tid] = -1;
+    if (kListPad > 0 && tid < kListPad) list_s[LCAP + tid] = -1;
     barrier_lds();
   };
-  if (lo < hi) store_list(min(hi - lo, kListCap));
+  if (lo < hi) store_list(min(hi - lo, LCAP));
   auto buf = [&](auto bconst) __attribute__((always_inline)) -> uint8_t* {
     constexpr int b = decltype(bconst)::value;
     return b == 0 ? tb0 : b == 1 ? tb1 : b == 2 ? tb2 : tb3;
   };
-  for (int clo = lo; clo < hi; clo += kListCap) {
-    const int n_ent = min(hi - clo, kListCap);
+  for (int clo = lo; clo < hi; clo += LCAP) {
+    const int n_ent = min(hi - clo, LCAP);
     const int ntiles = (n_ent + TR - 1) / TR;
     // With two buffers the refill of the next tile is skipped past the
     // last tile.  With more, every step issues one refill (a tile past the
@@ -621,10 +630,10 @@ void split_kernel(SplitParams p) {
 #pragma unroll
     for (int b = 0; b < NBUF; ++b) keep_live(addr[b]);
     barrier_raw();  // list_s and the buffers are reused by the next chunk
-    const int nxt = clo + kListCap;
+    const int nxt = clo + LCAP;
     if (nxt < hi) {
-      load_list(nxt, min(hi - nxt, kListCap));
-      store_list(min(hi - nxt, kListCap));
+      load_list(nxt, min(hi - nxt, LCAP));
+      store_list(min(hi - nxt, LCAP));
     }
   }
 
@@ -815,11 +824,12 @@ __global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineP
 // launchers
 // ---------------------------------------------------------------------------
 // LDS of one split workgroup: NBUF tile buffers, the staged index list (with
-// its pad), and with K-split pairs the exchange buffer of partial scores
-// (one 16-row block of 16 heads = 1 KiB per wave, head group and row block)
-constexpr int split_lds_bytes(int nbuf, int waves, int gpw, bool ksplit) {
-  return nbuf * kTileRows * kRow * 2 + (kListCap + (nbuf > 2 ? kTileRows * nbuf : 0)) * 4 +
-         (ksplit ? waves * gpw * (kTileRows / 16) * 64 * 16 : 0);
+// its pad), and with K-split pairs the exchange slots of partial scores (one
+// 16-row block of 16 heads = 1 KiB per slot, head group and row block)
+constexpr int split_lds_bytes(int nbuf, int waves, int ncs, int gpw, bool ksplit) {
+  return nbuf * kTileRows * kRow * 2 +
+         (split_list_cap(ncs, ksplit) + (nbuf > 2 ? kTileRows * nbuf : 0)) * 4 +
+         (ksplit ? (waves / ncs) * 2 * gpw * (kTileRows / 16) * 64 * 16 : 0);
 }
 constexpr int kCuLdsBytes = 160 * 1024;
 
@@ -844,20 +854,27 @@ static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t 
   return hipGetLastError();
 }
 
-// Per head class.  Up to 32 heads: 4 waves, two tile buffers, two workgroups
-// per CU.  More heads (64-head blocks): 8 waves in K-split pairs, each pair
-// sharing one 16-head group: one wave takes the even K-steps of QK^T and the
-// first 256 V columns, the other the odd K-steps and the last 256.  Three
-// tile buffers, one workgroup per CU, two waves per SIMD.  (Two head groups
-// per wave halve the LDS reads per head but need about 480 registers, one
-// wave per SIMD: measured 20% slower, the LDS latency is no longer hidden.)
+// Per head class:
+//  * up to 16 heads: 4 waves sharing one 16-head group, each with a quarter
+//    of the 512 V columns, in K-split pairs (even / odd K-steps of QK^T);
+//    two tile buffers, two workgroups per CU;
+//  * up to 32 heads: 4 waves = 2 head groups x 2 column halves, each wave
+//    all of QK^T; two tile buffers, two workgroups per CU;
+//  * more (64-head blocks): 8 waves = 4 head groups x 2 column halves in
+//    K-split pairs; three tile buffers, one workgroup per CU, two waves per
+//    SIMD.  (Two head groups per wave halve the LDS reads per head but need
+//    about 480 registers, one wave per SIMD: measured 20% slower, the LDS
+//    latency is no longer hidden.)
 constexpr int kNbufSmall = 2, kNbufLarge = 3, kGpwLarge = 1;
-static_assert(kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 1, false) == 2, "two small workgroups per CU");
-static_assert(kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, kGpwLarge, true) == 1,
+static_assert(kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 4, 1, true) == 2,
+              "two 16-head workgroups per CU");
+static_assert(kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 2, 1, false) == 2,
+              "two 32-head workgroups per CU");
+static_assert(kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, 2, kGpwLarge, true) == 1,
               "one large workgroup per CU");
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
-  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, kNbufSmall, false>(p, 1, st);
+  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, kNbufSmall, true>(p, 1, st);
   if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, kNbufSmall, false>(p, 1, st);
   return launch_split_t<4, 2, kGpwLarge, 32, kNbufLarge, true>(p, (p.heads + 63) / 64, st);
 }
@@ -865,8 +882,9 @@ hipError_t launch_split(const SplitParams& p, hipStream_t st) {
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }
 
 int split_blocks_per_cu(int heads) {
-  return heads <= 32 ? kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 1, false)
-                     : kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, kGpwLarge, true);
+  if (heads <= 16) return kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 4, 1, true);
+  if (heads <= 32) return kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 2, 1, false);
+  return kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, 2, kGpwLarge, true);
 }
 
 template <int SG, int PER>

@@ -11,13 +11,17 @@ Timing protocol
     (cache, index set) pairs whose distinct gathered rows exceed 512 MB (2x
     the Infinity Cache), so every step gathers rows from HBM (--warm turns the
     rotation off: a cache-resident figure, never an HBM one);
-  * steps/s: W warm-up steps, then K steps replayed from a HIP graph that
-    holds one rotation cycle, bracketed by device synchronisation;
+  * steps/s: W warm-up steps, then untimed replays of a HIP graph that holds
+    one rotation cycle for at least --settle seconds (the GPU's clocks ramp
+    up under load over tens of milliseconds), then K steps replayed from that
+    graph, bracketed by device synchronisation;
   * per-kernel durations: an eager loop with HIP events recorded around each
     launch on the launch stream, queued behind a spin kernel so that host
     enqueue time cannot leak into the measured intervals;
   * roofline: gathered-KV bytes of one split launch (valid list entries x
     1152 B) / the split kernel's mean duration, against 8 TB/s HBM3E;
+  * single_launch: the same step through smla_decode_fused, the merge inside
+    the split launch (list workloads, when the shape allows it);
   * cpu_baseline: the fp64 oracle, as is, on the host cores, over a bounded
     sample of the same workload, scaled to steps/s;
   * nsplit_sweep: steps/s and the split kernel's gathered-KV rate of the same
@@ -79,6 +83,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="CPU time budget of the oracle baseline (0 = skip)")
     ap.add_argument("--kernel-steps", type=int, default=512, help="launches per per-kernel timing")
+    ap.add_argument("--settle", type=float, default=0.3,
+                    help="seconds of untimed graph replays before the timed steps")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the NSPLIT sweep and the secondary batch-64 figure")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -193,6 +199,18 @@ class Workload:
                                         scale, nsplit, workspace_t=ws, stream=stream)
         return {"rows": rows, "paged": paged, "dense": dense}[self.kind]
 
+    def fused_in_launch(self, nsplit):
+        return (self.kind == "rows" and nsplit > 1
+                and self.smla.smla_fused_in_launch(self.B, self.Lq, self.H, nsplit))
+
+    def fused_fn(self, nsplit):
+        ws = self.workspace(nsplit)
+
+        def f(i):
+            c, ix = self._args(i)
+            self.smla.smla_decode_fused(self.q, c, ix, self.out, self.lse, self.inp.scale, nsplit, ws)
+        return f
+
     def split_fn(self, nsplit):
         ws = self.workspace(nsplit)
 
@@ -290,6 +308,11 @@ def main():
         step(i)
     torch.cuda.synchronize()
     graph = w.graph_of(step)
+    t_settle = time.time()
+    while time.time() - t_settle < args.settle:
+        for _ in range(max(1, 64 // w.n_rot)):
+            graph.replay()
+        torch.cuda.synchronize()
     us_per_step, steps = w.time_graph(graph, args.steps)
     ms_per_step = us_per_step * 1e-3
     steps_per_s = 1e6 / us_per_step
@@ -301,6 +324,13 @@ def main():
     comb_us = w.time_graph(w.graph_of(combine_only), args.kernel_steps)[0] if nsplit > 1 else 0.0
     split_us = w.split_time(nsplit, args.kernel_steps, us_per_step)
     split_only = w.split_fn(nsplit) if rows_mode else step
+    single_launch = None
+    if w.fused_in_launch(nsplit):
+        fused_us = w.time_graph(w.graph_of(w.fused_fn(nsplit)), args.steps)[0]
+        single_launch = {"us_per_step": round(fused_us, 3), "steps_per_s": round(1e6 / fused_us, 2),
+                         "entry_point": "smla_decode_fused",
+                         "method": "graph replay of smla_decode_fused steps (one kernel per step)"}
+        log(f"[bench] single launch (smla_decode_fused): {fused_us:.2f} us/step")
 
     # ---- per-kernel durations (b), diagnostic: events bracketing each eager
     # launch, queued behind a spin kernel so host enqueue time cannot leak in
@@ -375,7 +405,7 @@ def main():
             "nsplit": nsplit, "nsplit_from": "planner" if args.nsplit == 0 else "argument",
             "cache_state": "warm (no rotation)" if args.warm else
                            f"cold: rotation over {w.n_caches} caches x {len(w.sets)} disjoint index sets",
-            "timing": "HIP graph replay of whole rotation cycles",
+            "timing": f"HIP graph replay of whole rotation cycles, after {args.settle:g} s of untimed replays",
         },
         "gathered_kv_gbps_per_step": round(w.mean_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
         "kernels_us": {"split": round(split_us, 3), "combine": round(comb_us, 3),
@@ -402,6 +432,8 @@ def main():
                  "frac": round(flops / (split_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
         "kernel_sha": kernel_sha(),
     }
+    if single_launch:
+        result["single_launch"] = single_launch
     if sweep:
         result["nsplit_sweep"] = sweep
     if secondary:

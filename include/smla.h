@@ -30,20 +30,28 @@
  *   topk_idx   [batch, q_len, topk]         int32 physical row indices
  *   out        [batch, q_len, heads, 512]   bf16
  *   lse        [batch, q_len, heads]        fp32
- *   workspace  part_o [T, NSPLIT, heads, 512] fp32, then (at byte offset
- *              smla_workspace_lse_offset) part_lse [T, NSPLIT, heads] fp32,
- *              T = batch * q_len.
+ *   workspace  SMLA_WS_SYNC_BYTES of synchronisation words (below), then
+ *              part_o [T, NSPLIT, heads, 512] fp32 at byte offset
+ *              SMLA_WS_SYNC_BYTES, then part_lse [T, NSPLIT, heads] fp32 at
+ *              byte offset smla_workspace_lse_offset; T = batch * q_len.
+ *              The first SMLA_WS_SYNC_BYTES must be zero before the
+ *              workspace's first decode call; every decode call leaves them
+ *              zero again, whatever its shape, so a workspace zeroed once
+ *              serves any sequence of calls.  smla_split and smla_combine do
+ *              not touch them.
  * q, kv_cache, out and workspace must be 16-byte aligned; topk_idx and lse
  * 4-byte aligned.
  *
  * Ownership and execution.  The caller owns every buffer, including the
  * workspace; the library allocates no device memory and keeps no per-call
- * state (its only global is a per-device cache of the CU count).  Work is
+ * state (its globals are a per-device cache of the CU count and the
+ * smla_set_merge_polls setting).  Work is
  * enqueued on `hip_stream` (a hipStream_t; NULL = the legacy default stream)
  * and the call returns without waiting for it: buffers must stay alive and
  * unmodified until the stream has passed the call.  The calls never
  * synchronise the host, so they can be captured into a HIP graph.  Calls on
- * different streams that share a workspace race.
+ * different streams that share a workspace race (the synchronisation words
+ * included: such calls may also wait out their bounded polls, below).
  *
  * Errors.  Every entry point returns SMLA_OK (0) or a negative smla_status.
  * Arguments are validated before anything is enqueued; on an error nothing is
@@ -78,6 +86,8 @@ enum smla_status {
 #define SMLA_MAX_NSPLIT 1024  /* largest NSPLIT accepted */
 #define SMLA_MAX_HEADS 4096   /* largest head count accepted */
 #define SMLA_MAX_TOPK (1 << 24)
+#define SMLA_WS_SYNC_BYTES 16384  /* head of every workspace: single-launch combine words */
+#define SMLA_FUSED_MAX_NSPLIT 64  /* largest NSPLIT merged inside the split launch */
 
 /*
  * NSPLIT the planner picks for a call of this shape on the current device
@@ -106,8 +116,26 @@ size_t smla_workspace_bytes(int batch, int q_len, int heads, int nsplit);
 size_t smla_workspace_lse_offset(int batch, int q_len, int heads, int nsplit);
 
 /*
+ * 1 if smla_decode_fused with this shape and an explicit nsplit merges the
+ * partials inside the split launch (the conditions stated there), 0 if it
+ * launches the combine kernel too (or nsplit == 1: no merge at all), or a
+ * negative smla_status.  Uses the current device's CU count.
+ */
+int smla_fused_in_launch(int batch, int q_len, int heads, int nsplit);
+
+/*
+ * Bound on the polls (each a short sleep and one device-scope load) of a
+ * workgroup that waits for the other partials of its unit in the
+ * single-launch merge of smla_decode_fused; default 2048.  0 = never wait: the last workgroup to
+ * arrive merges the whole unit (same results, bit for bit).  Process-wide;
+ * applies to calls made after it.  Returns the previous value, or
+ * SMLA_ERR_DIM if polls < 0.
+ */
+int smla_set_merge_polls(int polls);
+
+/*
  * Full decode: the split kernel over every (token, split) and, when
- * NSPLIT > 1, the combine kernel.  nsplit == 0 asks the planner
+ * NSPLIT > 1, the combine kernel (smla_combine).  nsplit == 0 asks the planner
  * (smla_plan_nsplit); size the workspace with smla_workspace_bytes for the
  * NSPLIT actually used.  nsplit > topk is allowed (surplus splits are empty).
  * batch == 0, q_len == 0 or topk == 0 are valid: the first two launch
@@ -116,6 +144,30 @@ size_t smla_workspace_lse_offset(int batch, int q_len, int heads, int nsplit);
 int smla_decode(const void *q, const void *kv_cache, const int32_t *topk_idx, void *out,
                 float *lse, float scale, int nsplit, int batch, int q_len, int heads, int topk,
                 int64_t kv_rows, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * smla_decode with the log-sum-exp merge inside the split launch (one kernel
+ * instead of two; "The Split-K Imperative": the partials of the slices are
+ * merged by log-sum-exp), when 2 <= NSPLIT <= SMLA_FUSED_MAX_NSPLIT,
+ * tokens * head blocks <= SMLA_WS_SYNC_BYTES / 16 (head blocks of 16, 32 or
+ * 64 heads, by head count) and the grid fits the device's resident
+ * workgroups (smla_fused_in_launch); otherwise exactly smla_decode.  The
+ * NSPLIT workgroups of a (token, head block) write their partials with
+ * device-coherent stores and take tickets on counters in the workspace's
+ * synchronisation words; those that see every partial written merge one
+ * slice of the output each, and the last to arrive merges the slices of any
+ * that stopped waiting (each waits a bounded number of polls,
+ * smla_set_merge_polls), so no wait is unbounded even on a shared device.
+ * Same arithmetic as smla_combine; the merge order within a slice is fixed,
+ * so results repeat bit for bit.  On MI355X this form is slower than the two
+ * launches of smla_decode (its cross-XCD handoffs cost more than a kernel
+ * boundary); it serves callers that need a single launch.  Arguments,
+ * workspace size and errors as smla_decode.
+ */
+int smla_decode_fused(const void *q, const void *kv_cache, const int32_t *topk_idx, void *out,
+                      float *lse, float scale, int nsplit, int batch, int q_len, int heads,
+                      int topk, int64_t kv_rows, void *workspace, size_t workspace_bytes,
+                      void *hip_stream);
 
 /*
  * smla_decode over a paged cache, with the page-table lookup done in the

@@ -8,9 +8,9 @@ the stream; there is no CPU fallback.  The library is loaded on first use
 without the built library raises ImportError.
 
 Functions carry the C names: smla_plan_nsplit, smla_plan_nsplit_cus,
-smla_workspace_bytes, smla_workspace_lse_offset, smla_decode,
-smla_decode_paged, smla_decode_dense, smla_plan_nsplit_dense, smla_split,
-smla_combine, smla_status_str.
+smla_workspace_bytes, smla_workspace_lse_offset, smla_decode, smla_decode_fused,
+smla_fused_in_launch, smla_set_merge_polls, smla_decode_paged, smla_decode_dense,
+smla_plan_nsplit_dense, smla_split, smla_combine, smla_status_str.
 """
 from __future__ import annotations
 
@@ -51,9 +51,15 @@ def _load() -> ctypes.CDLL:
     lib.smla_workspace_bytes.restype = sz
     lib.smla_workspace_lse_offset.argtypes = [i32, i32, i32, i32]
     lib.smla_workspace_lse_offset.restype = sz
+    lib.smla_fused_in_launch.argtypes = [i32, i32, i32, i32]
+    lib.smla_fused_in_launch.restype = i32
+    lib.smla_set_merge_polls.argtypes = [i32]
+    lib.smla_set_merge_polls.restype = i32
     call = [vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i64, vp, sz, vp]
     lib.smla_decode.argtypes = call
     lib.smla_decode.restype = i32
+    lib.smla_decode_fused.argtypes = call
+    lib.smla_decode_fused.restype = i32
     lib.smla_split.argtypes = call
     lib.smla_split.restype = i32
     lib.smla_decode_paged.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, f32, i32, i32, i32, i32,
@@ -114,6 +120,23 @@ def smla_workspace_lse_offset(batch: int, q_len: int, heads: int, nsplit: int) -
     return int(_lib_handle().smla_workspace_lse_offset(batch, q_len, heads, nsplit))
 
 
+def smla_set_merge_polls(polls: int) -> int:
+    """Bound on a waiting workgroup's polls in the single-launch merge
+    (0 = the last arriver merges the whole unit).  Returns the previous value."""
+    r = _lib_handle().smla_set_merge_polls(polls)
+    if r < 0:
+        raise SmlaError(r, "smla_set_merge_polls")
+    return r
+
+
+def smla_fused_in_launch(batch: int, q_len: int, heads: int, nsplit: int) -> bool:
+    """Whether smla_decode_fused of this shape merges inside the split launch."""
+    r = _lib_handle().smla_fused_in_launch(batch, q_len, heads, nsplit)
+    if r < 0:
+        raise SmlaError(r, "smla_fused_in_launch")
+    return bool(r)
+
+
 def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -147,10 +170,18 @@ def _check_tensors(q, kv_cache, topk_idx, out, lse):
         raise ValueError(f"kv_cache must be [rows, {ROW}], got {tuple(kv_cache.shape)}")
 
 
+WS_SYNC_BYTES = 16384  # SMLA_WS_SYNC_BYTES: the workspace's synchronisation words
+
+
 def workspace(batch: int, q_len: int, heads: int, nsplit: int, device) -> torch.Tensor | None:
-    """A workspace tensor of the size the call needs (None when nsplit <= 1)."""
+    """A workspace tensor of the size the call needs (None when nsplit <= 1),
+    its synchronisation words zeroed as the library requires."""
     n = smla_workspace_bytes(batch, q_len, heads, nsplit)
-    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+    if not n:
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    ws[:WS_SYNC_BYTES].zero_()
+    return ws
 
 
 def _call(fn, name, q, kv_cache, topk_idx, out, lse, scale, nsplit, ws, stream):
@@ -177,6 +208,16 @@ def smla_decode(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int = 0,
     """
     return _call(_lib_handle().smla_decode, "smla_decode", q, kv_cache, topk_idx, out, lse, scale, nsplit,
                  workspace_t, stream)[0]
+
+
+def smla_decode_fused(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int = 0,
+                      workspace_t=None, stream=None) -> int:
+    """smla_decode with the merge inside the split launch when the shape
+    allows it (smla_fused_in_launch), else exactly smla_decode.  A given
+    workspace must have its first WS_SYNC_BYTES zero (workspace() does that);
+    the call leaves them zero.  Returns the NSPLIT used."""
+    return _call(_lib_handle().smla_decode_fused, "smla_decode_fused", q, kv_cache, topk_idx, out, lse,
+                 scale, nsplit, workspace_t, stream)[0]
 
 
 def smla_split(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int,
@@ -264,7 +305,7 @@ def partials_view(ws: torch.Tensor, batch: int, q_len: int, heads: int, nsplit: 
     t = batch * q_len
     n_o = t * nsplit * heads * DV
     off = smla_workspace_lse_offset(batch, q_len, heads, nsplit)
-    part_o = ws[: n_o * 4].view(torch.float32).view(t, nsplit, heads, DV)
+    part_o = ws[WS_SYNC_BYTES: WS_SYNC_BYTES + n_o * 4].view(torch.float32).view(t, nsplit, heads, DV)
     part_lse = ws[off: off + t * nsplit * heads * 4].view(torch.float32).view(t, nsplit, heads)
     return part_o, part_lse
 

@@ -21,6 +21,11 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
 
 // CU count of the current device, queried once per device.
+// bound on the polls of a workgroup waiting for its unit's partials in the
+// single-launch merge (each poll: a short sleep and one device-scope load)
+constexpr int kDefaultMergePolls = 2048;
+std::atomic<int> g_merge_polls{kDefaultMergePolls};
+
 int device_cus(int* cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
@@ -56,8 +61,11 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// workspace: [0, SMLA_WS_SYNC_BYTES) single-launch combine words, then part_o,
+// then part_lse
 size_t lse_offset(int64_t tokens, int heads, int nsplit) {
-  return round_up((size_t)tokens * nsplit * heads * SMLA_DV * sizeof(float), 256);
+  return SMLA_WS_SYNC_BYTES +
+         round_up((size_t)tokens * nsplit * heads * SMLA_DV * sizeof(float), 256);
 }
 
 size_t ws_bytes(int64_t tokens, int heads, int nsplit) {
@@ -86,11 +94,28 @@ bool dense_folds(int q_len, int heads, int max_ctx) {
   return q_len > 1 && (int64_t)q_len * heads <= SMLA_MAX_HEADS && max_ctx >= kDenseFoldMinCtx;
 }
 
+// Whether a decode call with NSPLIT > 1 merges inside the split launch: its
+// (token, head block) units fit the workspace's sync words, NSPLIT fits the
+// 64-bit claim mask, and the grid fits the device's resident workgroups.
+int single_launch(int64_t tokens, int heads, int nsplit, int* single) {
+  *single = 0;
+  if (nsplit < 2 || nsplit > SMLA_FUSED_MAX_NSPLIT) return SMLA_OK;
+  int cus = 0;
+  const int rc = device_cus(&cus);
+  if (rc != SMLA_OK) return rc;
+  const int hpb = smla::split_heads_per_block(heads);
+  const int64_t units = tokens * ((heads + hpb - 1) / hpb);
+  *single = units <= SMLA_WS_SYNC_BYTES / 16 &&
+            nsplit * units <= (int64_t)cus * smla::split_blocks_per_cu(heads);
+  return SMLA_OK;
+}
+
 // Shared by every decode entry point (combine = true) and smla_split
-// (combine = false).  topk is the list length (the longest context when dense).
+// (combine = false); fused: merge inside the split launch when single_launch
+// allows it.  topk is the list length (the longest context when dense).
 int run(const void* q, const void* kv, const Source& so, void* out, float* lse, float scale,
         int nsplit, int batch, int q_len, int heads, int topk, int64_t kv_rows, void* ws,
-        size_t ws_size, void* stream, bool combine) {
+        size_t ws_size, void* stream, bool combine, bool fused = false) {
   if (!dims_ok(batch, q_len, heads, topk) || kv_rows < 0) return SMLA_ERR_DIM;
   if (so.table && (so.page_size < 1 || so.max_pages < 0)) return SMLA_ERR_DIM;
   if (nsplit < 0 || nsplit > SMLA_MAX_NSPLIT) return SMLA_ERR_NSPLIT;
@@ -137,7 +162,7 @@ int run(const void* q, const void* kv, const Source& so, void* out, float* lse, 
   sp.q_len = q_len;
   sp.out = (uint16_t*)out;
   sp.lse = lse;
-  sp.part_o = partials ? (float*)ws : nullptr;
+  sp.part_o = partials ? (float*)((char*)ws + SMLA_WS_SYNC_BYTES) : nullptr;
   sp.part_lse = partials ? (float*)((char*)ws + lse_offset(tokens, heads, nsplit)) : nullptr;
   sp.kv_rows = kv_rows;
   sp.tokens = (int)tokens;
@@ -146,11 +171,22 @@ int run(const void* q, const void* kv, const Source& so, void* out, float* lse, 
   sp.nsplit = nsplit;
   sp.per_split = topk == 0 ? 0 : (topk + nsplit - 1) / nsplit;
   sp.scale_log2 = scale * smla::kLog2e;
+  // the merge runs inside the split launch when the unit's workgroups can all
+  // be resident at once (so none waits on one that has not started) and the
+  // unit count and NSPLIT fit the workspace's sync words; else a second launch
+  sp.sync = nullptr;
+  if (partials && combine && fused) {
+    int single = 0;
+    const int rc = single_launch(tokens, heads, nsplit, &single);
+    if (rc != SMLA_OK) return rc;
+    if (single) sp.sync = (uint32_t*)ws;
+  }
+  sp.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
   if (smla::launch_split(sp, st) != hipSuccess) {
     (void)hipGetLastError();
     return SMLA_ERR_LAUNCH;
   }
-  if (partials && combine) {
+  if (partials && combine && !sp.sync) {
     smla::CombineParams cp;
     cp.part_o = sp.part_o;
     cp.part_lse = sp.part_lse;
@@ -207,6 +243,19 @@ SMLA_API size_t smla_workspace_bytes(int batch, int q_len, int heads, int nsplit
   return ws_bytes((int64_t)batch * q_len, heads, nsplit);
 }
 
+SMLA_API int smla_set_merge_polls(int polls) {
+  if (polls < 0) return SMLA_ERR_DIM;
+  return g_merge_polls.exchange(polls, std::memory_order_relaxed);
+}
+
+SMLA_API int smla_fused_in_launch(int batch, int q_len, int heads, int nsplit) {
+  if (batch < 0 || q_len < 0 || heads < 1 || heads > SMLA_MAX_HEADS) return SMLA_ERR_DIM;
+  if (nsplit < 1 || nsplit > SMLA_MAX_NSPLIT) return SMLA_ERR_NSPLIT;
+  int single = 0;
+  const int rc = single_launch((int64_t)batch * q_len, heads, nsplit, &single);
+  return rc != SMLA_OK ? rc : single;
+}
+
 SMLA_API size_t smla_workspace_lse_offset(int batch, int q_len, int heads, int nsplit) {
   if (batch < 0 || q_len < 0 || heads < 1 || nsplit < 1) return 0;
   return lse_offset((int64_t)batch * q_len, heads, nsplit);
@@ -220,6 +269,16 @@ SMLA_API int smla_decode(const void* q, const void* kv_cache, const int32_t* top
   so.idx = topk_idx;
   return run(q, kv_cache, so, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
              workspace, workspace_bytes, hip_stream, true);
+}
+
+SMLA_API int smla_decode_fused(const void* q, const void* kv_cache, const int32_t* topk_idx,
+                               void* out, float* lse, float scale, int nsplit, int batch,
+                               int q_len, int heads, int topk, int64_t kv_rows, void* workspace,
+                               size_t workspace_bytes, void* hip_stream) {
+  Source so;
+  so.idx = topk_idx;
+  return run(q, kv_cache, so, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
+             workspace, workspace_bytes, hip_stream, true, true);
 }
 
 SMLA_API int smla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,

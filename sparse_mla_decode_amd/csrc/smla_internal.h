@@ -46,6 +46,9 @@ struct SplitParams {
   float* lse;           // [T, H]            (nsplit == 1)
   float* part_o;        // [T, S, H, 512]    (nsplit > 1)
   float* part_lse;      // [T, S, H]         (nsplit > 1)
+  uint32_t* sync;       // [units][4] single-launch combine words (zero between
+                        // calls), or null: partials only
+  int merge_polls;      // bound on a waiting workgroup's polls (single launch)
   int64_t kv_rows;
   int tokens, heads, topk, nsplit, per_split;
   float scale_log2;     // scale * log2(e): scores are kept in base 2

@@ -146,14 +146,204 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
 
 
 // ---------------------------------------------------------------------------
+// Single-launch combine ([SPLITK] "The Split-K Imperative": the partials of
+// the NSPLIT slices are merged by log-sum-exp; here the split workgroups do
+// it themselves instead of a second launch).  The NSPLIT workgroups of a
+// unit (token, head block) share four words in the caller's workspace,
+// zero between calls: arrive, depart and a 64-bit claim mask.
+//   1. Each workgroup writes its partial with device-coherent stores, waits
+//      until they have completed, and takes an arrival ticket.
+//   2. A workgroup waits, with a bounded number of polls, until all NSPLIT
+//      tickets are out (the last arriver does not wait), then claims its
+//      own slice of the unit's output (claim bit = its split index) and
+//      merges it from the NSPLIT partials.
+//   3. The last arriver then claims every slice still unclaimed and merges
+//      those too: slices of workgroups that gave up waiting (which happens
+//      only if the unit's workgroups are not resident together), so every
+//      slice is merged exactly once and no wait is unbounded.
+//   4. The last workgroup to depart clears the four words for the next call.
+// A slice is a contiguous range of the unit's (head, 4-column) quads; its
+// merge is the combine kernel's arithmetic: a running maximum over the
+// splits' LSE, weights exp(LSE_s - max), empty splits (LSE = -inf) weight 0.
+// The partials travel between XCDs, whose L2 caches are not coherent with
+// each other for ordinary accesses: they are written and read with
+// agent-scope atomic accesses (8 bytes each), which the L2 keeps coherent,
+// so no cache-wide writeback or invalidate is needed (those serialise per
+// XCD and cost more than the merge itself).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_agent(float* p, floatx4 v) {
+  const u32x4 u = __builtin_bit_cast(u32x4, v);
+  uint64_t* q = (uint64_t*)p;
+  __hip_atomic_store(q, (uint64_t)u[0] | ((uint64_t)u[1] << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(q + 1, (uint64_t)u[2] | ((uint64_t)u[3] << 32), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ floatx4 ld_agent(const float* p) {
+  uint64_t* q = (uint64_t*)const_cast<float*>(p);
+  const uint64_t a = __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t b = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return floatx4{__uint_as_float((uint32_t)a), __uint_as_float((uint32_t)(a >> 32)),
+                 __uint_as_float((uint32_t)b), __uint_as_float((uint32_t)(b >> 32))};
+}
+__device__ __forceinline__ float ld_agent1(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Merge slice c of unit (tok, heads h0 .. h0+hv-1) into out / lse; NT
+// threads, LDS scratch of NT * 24 bytes at `lds`.
+template <int NT>
+__device__ __forceinline__ void merge_slice(const SplitParams& p, int tok, int h0, int hv, int c,
+                                            uint8_t* lds) {
+  const int tid = threadIdx.x, S = p.nsplit;
+  const int Q = hv * (kDV / 4);
+  const int qlo = (int)((int64_t)c * Q / S), qhi = (int)((int64_t)(c + 1) * Q / S);
+  const int P = qhi - qlo;
+  if (P <= 0) return;  // uniform
+  // G thread groups share the splits of a quad when the slice is small
+  int G = 1;
+  while (2 * G * P <= NT && 2 * G <= S) G *= 2;
+  const int TPG = NT / G, grp = tid / TPG, lt = tid % TPG;
+  const int64_t stride = (int64_t)p.heads * kDV;
+  floatx4* acc_s = (floatx4*)lds;
+  float* m_s = (float*)(lds + NT * 16);
+  float* w_s = m_s + NT;
+  for (int base = 0; base < P; base += TPG) {
+    const int qi = base + lt;
+    const bool act = qi < P;
+    const int q = qlo + (act ? qi : P - 1);
+    const int h = h0 + q / (kDV / 4), col = (q % (kDV / 4)) * 4;
+    const float* lse_in = p.part_lse + (int64_t)tok * S * p.heads + h;
+    const float* o_in = p.part_o + ((int64_t)tok * S * p.heads + h) * kDV + col;
+    float m = -__builtin_inff(), w = 0.f;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+    constexpr int PER = 4;
+    for (int s0 = grp; s0 < S; s0 += G * PER) {
+      floatx4 v[PER];
+      float l[PER];
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int sp = s0 + u * G;
+        v[u] = sp < S ? ld_agent(o_in + sp * stride) : floatx4{0.f, 0.f, 0.f, 0.f};
+        l[u] = sp < S ? ld_agent1(lse_in + (int64_t)sp * p.heads) : -__builtin_inff();
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        if (l[u] == -__builtin_inff()) continue;
+        if (l[u] > m) {
+          const float r = __builtin_amdgcn_exp2f((m - l[u]) * kLog2e);  // 0 while m = -inf
+          acc *= r;
+          w *= r;
+          m = l[u];
+        }
+        const float e = __builtin_amdgcn_exp2f((l[u] - m) * kLog2e);
+        acc += e * v[u];
+        w += e;
+      }
+    }
+    if (G > 1) {  // merge the groups: M = max m_g, weights exp(m_g - M)
+      acc_s[tid] = acc;
+      m_s[tid] = m;
+      w_s[tid] = w;
+      __syncthreads();
+      if (grp == 0) {
+        float M = -__builtin_inff();
+        for (int g2 = 0; g2 < G; ++g2) M = fmaxf(M, m_s[lt + g2 * TPG]);
+        acc = floatx4{0.f, 0.f, 0.f, 0.f};
+        w = 0.f;
+        if (M != -__builtin_inff()) {
+          for (int g2 = 0; g2 < G; ++g2) {
+            const float mg = m_s[lt + g2 * TPG];
+            if (mg == -__builtin_inff()) continue;
+            const float f = __builtin_amdgcn_exp2f((mg - M) * kLog2e);
+            acc += f * acc_s[lt + g2 * TPG];
+            w += f * w_s[lt + g2 * TPG];
+          }
+        }
+        m = M;
+      }
+      __syncthreads();
+    }
+    if (grp == 0 && act) {
+      const bool any = w > 0.f;
+      const float inv = any ? 1.f / w : 0.f;
+      const int64_t th = (int64_t)tok * p.heads + h;
+      *(u32x2*)(p.out + th * kDV + col) =
+          u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+      if (col == 0) p.lse[th] = any ? m + __logf(w) : -__builtin_inff();
+    }
+  }
+}
+
+// Steps 1-4 above for split `split` of unit `unit`; lds: NT * 24 bytes of
+// merge scratch, bc: 16 bytes for broadcasts (both free LDS).
+template <int NT>
+__device__ __forceinline__ void fused_combine(const SplitParams& p, int unit, int tok, int h0, int hv,
+                                              int split, uint8_t* lds, uint32_t* bc) {
+  const int tid = threadIdx.x;
+  const uint32_t S = (uint32_t)p.nsplit;
+  uint32_t* sy = p.sync + 4 * (int64_t)unit;  // arrive, depart, claim (2 words)
+  // 1. every wave's partial stores have completed before the ticket is taken
+  wait_vmcnt<0>();
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t t = __hip_atomic_fetch_add(sy, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool ready = t == S - 1;
+    for (int i = 0; !ready && i < p.merge_polls; ++i) {
+      __builtin_amdgcn_s_sleep(4);
+      ready = __hip_atomic_load(sy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S;
+    }
+    uint32_t own = 0;
+    if (ready) {
+      const uint32_t bit = 1u << (split & 31);
+      own = (__hip_atomic_fetch_or(sy + 2 + (split >> 5), bit, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) & bit) == 0;
+    }
+    bc[0] = own;
+    bc[1] = t == S - 1;
+  }
+  __syncthreads();
+  const bool own = bc[0] != 0, last = bc[1] != 0;
+  // 2. this workgroup's own slice
+  if (own) merge_slice<NT>(p, tok, h0, hv, split, lds);
+  // 3. the last arriver takes every slice nobody has claimed yet
+  if (last) {
+    if (tid == 0) {
+      const uint32_t all0 = S >= 32 ? 0xffffffffu : (1u << S) - 1;
+      const uint32_t all1 = S >= 64 ? 0xffffffffu : S > 32 ? (1u << (S - 32)) - 1 : 0u;
+      const uint32_t o0 =
+          __hip_atomic_fetch_or(sy + 2, all0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t o1 = all1 ? __hip_atomic_fetch_or(sy + 3, all1, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT)
+                               : 0u;
+      bc[2] = all0 & ~o0;
+      bc[3] = all1 & ~o1;
+    }
+    __syncthreads();
+    uint64_t todo = (uint64_t)bc[2] | ((uint64_t)bc[3] << 32);
+    while (todo) {  // uniform
+      merge_slice<NT>(p, tok, h0, hv, __builtin_ctzll(todo), lds);
+      todo &= todo - 1;
+    }
+  }
+  // 4. depart; the last one out clears the words (no workgroup of this call
+  // reads them any more; the next call is ordered after this one)
+  if (tid == 0 &&
+      __hip_atomic_fetch_add(sy + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) __hip_atomic_store(sy + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Split kernel.  HG head groups of 16 per workgroup; each wave owns GPW
 // head groups and one of NCS column slices of the 512 value columns.  Every
 // wave computes S for its head groups; the PV work and the O accumulators
 // are divided among the NCS waves that share head groups.  With GPW = 2 a
 // wave feeds every LDS operand read (a K-tile of QK^T, a V^T block of PV) to
 // two MFMAs, one per head group, halving LDS traffic per head; it then needs
-// about 460 registers and runs one wave per SIMD.  TR rows per tile, NBUF
-// tile buffers: NBUF-1 tiles are in flight while one is computed.
+// about 460 registers and runs one wave per SIMD.  TR rows per tile, two
+// tile buffers: one tile is in flight while the other is computed.
 // ---------------------------------------------------------------------------
 // The dispatcher hands workgroup i to XCD i % kXcds (round robin over the
 // eight XCDs, each with its own L2).  This renumbering gives every XCD a
@@ -202,9 +392,9 @@ __device__ __forceinline__ void dma_tile(const u32x4* src, uint8_t* lds,
 // Keeps a value in its registers up to this point.
 __device__ __forceinline__ void keep_live(uint64_t v) { asm volatile("" ::"v"(v)); }
 
-template <int HG, int NCS, int GPW, int TR, int NBUF, bool KSPLIT, int SRC>
+template <int HG, int NCS, int GPW, int TR, bool KSPLIT, int SRC>
 __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
-__attribute__((amdgpu_waves_per_eu(GPW == 1 && (NBUF == 2 || KSPLIT) ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(GPW == 1 ? 2 : 1)))
 void split_kernel(SplitParams p) {
   static_assert(HG % GPW == 0, "whole head groups per wave");
   static_assert(!KSPLIT || NCS % 2 == 0, "K-split pairs waves of opposite parity");
@@ -222,11 +412,7 @@ void split_kernel(SplitParams p) {
   // QK^T K-steps per wave: all 18, or with K-split pairs the 9 of one parity
   constexpr int KSW = KSPLIT ? kKSteps / 2 : kKSteps;
   static_assert(TR * kRowGran % NTD == 0, "tile must split evenly over the loading threads");
-  static_assert(TR % 32 == 0 && NBUF >= 2 && NBUF <= 4, "tile shape");
-  static_assert(L * (NBUF - 2) < 64, "vmcnt range");
-  // with always-issued refills the tile count of a chunk is rounded up to a
-  // multiple of NBUF; the list's tail pad (all -1) covers those tiles
-  constexpr int kListPad = NBUF > 2 ? TR * NBUF : 0;
+  static_assert(TR % 32 == 0, "tile shape");
   // list entries staged at a time (the K-split 16-head workgroup stages
   // 1024 so that two of them fit a CU's LDS)
   constexpr int LCAP = split_list_cap(NCS, KSPLIT);
@@ -241,9 +427,7 @@ void split_kernel(SplitParams p) {
   // for every outstanding load before each LDS read).
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t tb2[NBUF > 2 ? kTileBytes : 16];
-  __shared__ __attribute__((aligned(16))) uint8_t tb3[NBUF > 3 ? kTileBytes : 16];
-  __shared__ __attribute__((aligned(16))) int list_s[LCAP + kListPad];
+  __shared__ __attribute__((aligned(16))) int list_s[LCAP];
   // partial S^T per (head group, parity) slot: [slot][gi][rb][lane]
   __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? kXsSlots * GPW * RB * 64 : 1];
 
@@ -374,14 +558,12 @@ void split_kernel(SplitParams p) {
   }
 
   // LDS-DMA loads of tile t (list entries t*TR.. of the staged chunk); a
-  // masked entry, one past the chunk or a tile past the last (t >= ntiles)
-  // loads the zero row.  The L loads of a lane share one 64-bit address (see
+  // masked entry or one past the chunk loads the zero row.  The L loads of a lane share one 64-bit address (see
   // dma_tile), returned so that the caller keeps it live until the loads are
   // known to be complete.
   static_assert(DP == 1, "one row per lane per tile");
-  auto issue = [&](uint8_t* buf, int t, int ntiles) __attribute__((always_inline)) -> uint64_t {
-    const int e = min(t * TR + dma_row[0], LCAP - 1);  // inside list_s
-    const int32_t r = t < ntiles ? list_s[e] : -1;
+  auto issue = [&](uint8_t* buf, int t) __attribute__((always_inline)) -> uint64_t {
+    const int32_t r = list_s[t * TR + dma_row[0]];  // t * TR + TR <= LCAP
     const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
     const u32x4* src = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran[0];
     if (wave < DW)
@@ -572,63 +754,36 @@ void split_kernel(SplitParams p) {
       const int e = u * NT + tid;
       list_s[e] = (e < n_ent && (uint32_t)lv[u] < kv32) ? lv[u] : -1;
     }
-    static_assert(kListPad <= NT, "one pad entry per thread at most");
-    if (kListPad > 0 && tid < kListPad) list_s[LCAP + tid] = -1;
     barrier_lds();
   };
   if (lo < hi) store_list(min(hi - lo, LCAP));
   auto buf = [&](auto bconst) __attribute__((always_inline)) -> uint8_t* {
     constexpr int b = decltype(bconst)::value;
-    return b == 0 ? tb0 : b == 1 ? tb1 : b == 2 ? tb2 : tb3;
+    return b == 0 ? tb0 : tb1;
   };
   for (int clo = lo; clo < hi; clo += LCAP) {
     const int n_ent = min(hi - clo, LCAP);
     const int ntiles = (n_ent + TR - 1) / TR;
-    // With two buffers the refill of the next tile is skipped past the
-    // last tile.  With more, every step issues one refill (a tile past the
-    // last loads the zero row): the number of loads in flight is then the
-    // same at every wait, and no branch joins paths with different loads
-    // outstanding, which would make the compiler wait for all of them.
-    constexpr bool kAlwaysIssue = NBUF > 2;
-    uint64_t addr[NBUF] = {};  // per buffer: the address its last loads read
-    addr[0] = issue(tb0, 0, ntiles);
-    if constexpr (NBUF > 2) addr[1] = issue(tb1, 1, ntiles);
-    if constexpr (NBUF > 3) addr[2] = issue(tb2, 2, ntiles);
+    // double buffering: tile n+1 loads while tile n is computed
+    uint64_t addr[2] = {};  // per buffer: the address its last loads read
+    addr[0] = issue(tb0, 0);
     // one pipeline step on buffer b (a compile-time constant)
     auto step = [&](auto bconst, int n) __attribute__((always_inline)) {
       constexpr int b = decltype(bconst)::value;
-      // tile n landed; tiles n+1 .. n+NBUF-2 may still be in flight
-      if constexpr (kAlwaysIssue) wait_vmcnt<L * (NBUF - 2)>();
-      else wait_vmcnt<0>();
-      keep_live(addr[b]);  // tile n's loads are done: its address may go
+      wait_vmcnt<0>();     // tile n landed
+      keep_live(addr[b]);  // its loads are done: their address may go
       barrier_raw();
-      // refill the buffer every wave finished with in the previous step
-      constexpr int bn = (b + NBUF - 1) % NBUF;
-      if (kAlwaysIssue || n + NBUF - 1 < ntiles)
-        addr[bn] = issue(buf(std::integral_constant<int, bn>{}), n + NBUF - 1, ntiles);
+      // refill the other buffer, which every wave finished with in the
+      // previous step
+      if (n + 1 < ntiles) addr[b ^ 1] = issue(buf(std::integral_constant<int, b ^ 1>{}), n + 1);
       compute(buf(bconst), n);
     };
-    if constexpr (kAlwaysIssue) {
-      // all NBUF steps of a round unconditionally (a skipped step would again
-      // join paths with different loads outstanding): the tile count is
-      // rounded up to a multiple of NBUF, and a tile past the last holds
-      // only masked entries (-1 in list_s, zero rows in the buffer), which
-      // leave m, l and O unchanged
-      for (int n0 = 0; n0 < ntiles; n0 += NBUF) {
-        step(std::integral_constant<int, 0>{}, n0);
-        step(std::integral_constant<int, 1>{}, n0 + 1);
-        step(std::integral_constant<int, 2>{}, n0 + 2);
-        if constexpr (NBUF > 3) step(std::integral_constant<int, 3>{}, n0 + 3);
-      }
-    } else {
-      for (int n0 = 0; n0 < ntiles; n0 += NBUF) {
-        step(std::integral_constant<int, 0>{}, n0);
-        if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
-      }
+    for (int n0 = 0; n0 < ntiles; n0 += 2) {
+      step(std::integral_constant<int, 0>{}, n0);
+      if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
     }
-    if constexpr (kAlwaysIssue) wait_vmcnt<0>();  // the refills past the last tile
-#pragma unroll
-    for (int b = 0; b < NBUF; ++b) keep_live(addr[b]);
+    keep_live(addr[0]);
+    keep_live(addr[1]);
     barrier_raw();  // list_s and the buffers are reused by the next chunk
     const int nxt = clo + LCAP;
     if (nxt < hi) {
@@ -658,14 +813,25 @@ void split_kernel(SplitParams p) {
     } else {
       const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + h[gi];
       float* orow = p.part_o + slot * kDV;
+      if (p.sync) {  // read by other workgroups in this launch: coherent stores
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int c0 = (cs * CB + cb) * 16 + 4 * g;
-        *(floatx4*)(orow + c0) = oacc[gi][cb] * inv;
+        for (int cb = 0; cb < CB; ++cb) st_agent(orow + (cs * CB + cb) * 16 + 4 * g, oacc[gi][cb] * inv);
+        if (g == 0 && cs == 0)
+          __hip_atomic_store(p.part_lse + slot, lse_v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+#pragma unroll
+        for (int cb = 0; cb < CB; ++cb) {
+          const int c0 = (cs * CB + cb) * 16 + 4 * g;
+          *(floatx4*)(orow + c0) = oacc[gi][cb] * inv;
+        }
+        if (g == 0 && cs == 0) p.part_lse[slot] = lse_v;
       }
-      if (g == 0 && cs == 0) p.part_lse[slot] = lse_v;
     }
   }
+  if (p.sync && p.nsplit > 1)  // single launch: merge the unit's partials here
+    fused_combine<NT>(p, rest, tok, hblk * kHeadsPerBlock,
+                      min(kHeadsPerBlock, p.heads - hblk * kHeadsPerBlock), split, tb0,
+                      (uint32_t*)tb1);
 }
 
 // ---------------------------------------------------------------------------
@@ -823,68 +989,67 @@ __global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineP
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// LDS of one split workgroup: NBUF tile buffers, the staged index list (with
-// its pad), and with K-split pairs the exchange slots of partial scores (one
-// 16-row block of 16 heads = 1 KiB per slot, head group and row block)
-constexpr int split_lds_bytes(int nbuf, int waves, int ncs, int gpw, bool ksplit) {
-  return nbuf * kTileRows * kRow * 2 +
-         (split_list_cap(ncs, ksplit) + (nbuf > 2 ? kTileRows * nbuf : 0)) * 4 +
+// LDS of one split workgroup: two tile buffers, the staged index list, and
+// with K-split pairs the exchange slots of partial scores (one 16-row block
+// of 16 heads = 1 KiB per slot, head group and row block)
+constexpr int split_lds_bytes(int waves, int ncs, int gpw, bool ksplit) {
+  return 2 * kTileRows * kRow * 2 + split_list_cap(ncs, ksplit) * 4 +
          (ksplit ? (waves / ncs) * 2 * gpw * (kTileRows / 16) * 64 * 16 : 0);
 }
 constexpr int kCuLdsBytes = 160 * 1024;
 
-template <int HG, int NCS, int GPW, int TR, int NBUF, bool KSPLIT>
+template <int HG, int NCS, int GPW, int TR, bool KSPLIT>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
   static_assert(TR == kTileRows, "the planner's tile");
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
   const dim3 grid((unsigned)nwg), block(64 * (HG / GPW) * NCS);
   switch (p.src) {
     case kSrcPositions:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF, KSPLIT, kSrcPositions>), grid, block,
-                         0, st, p);
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KSPLIT, kSrcPositions>), grid, block, 0,
+                         st, p);
       break;
     case kSrcDense:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF, KSPLIT, kSrcDense>), grid, block, 0,
-                         st, p);
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KSPLIT, kSrcDense>), grid, block, 0, st,
+                         p);
       break;
     default:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, NBUF, KSPLIT, kSrcRows>), grid, block, 0,
-                         st, p);
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KSPLIT, kSrcRows>), grid, block, 0, st,
+                         p);
   }
   return hipGetLastError();
 }
 
-// Per head class:
+// Per head class (all with two tile buffers):
 //  * up to 16 heads: 4 waves sharing one 16-head group, each with a quarter
 //    of the 512 V columns, in K-split pairs (even / odd K-steps of QK^T);
-//    two tile buffers, two workgroups per CU;
+//    two workgroups per CU;
 //  * up to 32 heads: 4 waves = 2 head groups x 2 column halves, each wave
-//    all of QK^T; two tile buffers, two workgroups per CU;
+//    all of QK^T; two workgroups per CU;
 //  * more (64-head blocks): 8 waves = 4 head groups x 2 column halves in
-//    K-split pairs; three tile buffers, one workgroup per CU, two waves per
-//    SIMD.  (Two head groups per wave halve the LDS reads per head but need
-//    about 480 registers, one wave per SIMD: measured 20% slower, the LDS
-//    latency is no longer hidden.)
-constexpr int kNbufSmall = 2, kNbufLarge = 3, kGpwLarge = 1;
-static_assert(kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 4, 1, true) == 2,
-              "two 16-head workgroups per CU");
-static_assert(kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 2, 1, false) == 2,
-              "two 32-head workgroups per CU");
-static_assert(kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, 2, kGpwLarge, true) == 1,
-              "one large workgroup per CU");
+//    K-split pairs; one workgroup per CU (its registers allow two waves per
+//    SIMD, i.e. 8 waves per CU).  Two head groups per wave would halve the
+//    LDS reads per head but need about 480 registers, one wave per SIMD:
+//    measured 20% slower, the LDS latency is no longer hidden.  A third tile
+//    buffer (two tiles in flight) measured 13% slower: it gained nothing in
+//    overlap and its always-issued refills round the tile count up.
+constexpr int kGpwLarge = 1;
+static_assert(kCuLdsBytes / split_lds_bytes(4, 4, 1, true) == 2, "two 16-head workgroups per CU");
+static_assert(kCuLdsBytes / split_lds_bytes(4, 2, 1, false) == 2, "two 32-head workgroups per CU");
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
-  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, kNbufSmall, true>(p, 1, st);
-  if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, kNbufSmall, false>(p, 1, st);
-  return launch_split_t<4, 2, kGpwLarge, 32, kNbufLarge, true>(p, (p.heads + 63) / 64, st);
+  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, true>(p, 1, st);
+  if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, false>(p, 1, st);
+  return launch_split_t<4, 2, kGpwLarge, 32, true>(p, (p.heads + 63) / 64, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }
 
+// workgroups of the head class resident per CU: LDS bounds the 4-wave
+// classes at two; the 8-wave class at 2 waves per SIMD is one per CU
 int split_blocks_per_cu(int heads) {
-  if (heads <= 16) return kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 4, 1, true);
-  if (heads <= 32) return kCuLdsBytes / split_lds_bytes(kNbufSmall, 4, 2, 1, false);
-  return kCuLdsBytes / split_lds_bytes(kNbufLarge, 8, 2, kGpwLarge, true);
+  if (heads <= 16) return kCuLdsBytes / split_lds_bytes(4, 4, 1, true);
+  if (heads <= 32) return kCuLdsBytes / split_lds_bytes(4, 2, 1, false);
+  return 1;
 }
 
 template <int SG, int PER>

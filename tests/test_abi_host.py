@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["smla_plan_nsplit", "smla_plan_nsplit_cus", "smla_workspace_bytes",
-                            "smla_workspace_lse_offset", "smla_decode", "smla_decode_paged",
+                            "smla_workspace_lse_offset", "smla_fused_in_launch", "smla_set_merge_polls",
+                            "smla_decode", "smla_decode_fused", "smla_decode_paged",
                             "smla_decode_dense", "smla_plan_nsplit_dense", "smla_split",
                             "smla_combine", "smla_status_str"]), names
 
@@ -141,10 +142,29 @@ def test_planner_degenerate(smla):
 def test_workspace_layout(smla, b, lq, h, s):
     t = b * lq
     o_bytes = t * s * h * 512 * 4
-    off = -(-o_bytes // 256) * 256
+    off = 16384 + -(-o_bytes // 256) * 256  # sync words, then part_o
     assert smla.smla_workspace_lse_offset(b, lq, h, s) == off
     want = 0 if s <= 1 else off + t * s * h * 4
     assert smla.smla_workspace_bytes(b, lq, h, s) == want
+
+
+def test_single_launch_query(smla):
+    """When smla_decode_fused merges inside the split launch; the answers that
+    need no device (NSPLIT 1 has no merge, NSPLIT above 64 exceeds the claim
+    mask) and the argument errors."""
+    q = smla.lib.smla_fused_in_launch
+    assert q(1, 1, 8, 1) == 0
+    assert q(1, 1, 8, 65) == 0 and q(4, 1, 128, 1024) == 0
+    assert q(1, 1, 0, 4) == -2 and q(-1, 1, 8, 4) == -2 and q(1, 1, 5000, 4) == -2
+    assert q(1, 1, 8, 0) == -3 and q(1, 1, 8, 1025) == -3
+
+
+def test_merge_polls_setting(smla):
+    prev = smla.lib.smla_set_merge_polls(7)
+    assert prev >= 0
+    assert smla.lib.smla_set_merge_polls(prev) == 7
+    assert smla.lib.smla_set_merge_polls(-1) == -2
+    assert smla.lib.smla_set_merge_polls(prev) == prev
 
 
 # ----------------------------------------------------------- argument errors
@@ -161,7 +181,7 @@ def _call(smla, fn="smla_decode", **kw):
              vp(a["ws"]), a["ws_bytes"], vp(a["stream"]))
 
 
-@pytest.mark.parametrize("fn", ["smla_decode", "smla_split"])
+@pytest.mark.parametrize("fn", ["smla_decode", "smla_decode_fused", "smla_split"])
 def test_invalid_arguments_rejected_before_launch(smla, fn):
     # pointers are fake: each call must fail validation and touch nothing
     assert _call(smla, fn, q=0) == -1
@@ -269,3 +289,6 @@ def test_planner_path_without_device(smla):
     # nsplit == 0 consults the device's CU count: no device -> SMLA_ERR_DEVICE
     assert _call(smla, "smla_decode", nsplit=0) == -6
     assert smla.lib.smla_plan_nsplit(1, 1, 8, 2048) == -6
+    assert smla.lib.smla_fused_in_launch(1, 1, 8, 4) == -6
+    # a valid fused call with NSPLIT > 1 asks the device whether to merge in-launch
+    assert _call(smla, "smla_decode_fused", nsplit=4, ws=0x60000, ws_bytes=1 << 24) == -6

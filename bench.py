@@ -21,7 +21,8 @@ Timing protocol
   * roofline: gathered-KV bytes of one split launch (valid list entries x
     1152 B) / the split kernel's mean duration, against 8 TB/s HBM3E;
   * single_launch: the same step through smla_decode_fused, the merge inside
-    the split launch (list workloads, when the shape allows it);
+    the split launch (list workloads, when the shape allows it; skipped with
+    --no-sweep, so that a profiled run holds only the two-launch kernels);
   * cpu_baseline: the fp64 oracle, as is, on the host cores, over a bounded
     sample of the same workload, scaled to steps/s;
   * nsplit_sweep: steps/s and the split kernel's gathered-KV rate of the same
@@ -86,7 +87,7 @@ def parse():
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed graph replays before the timed steps")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the NSPLIT sweep and the secondary batch-64 figure")
+                    help="skip the NSPLIT sweep, the single-launch figure and the secondary batch-64 figure")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -263,9 +264,19 @@ class Workload:
         comb = self.time_graph(self.graph_of(self.combine_fn(nsplit)), kernel_steps)[0] if nsplit > 1 else 0.0
         return step_us - comb
 
-    def summary(self, nsplit, steps, kernel_steps):
+    def settle(self, g, seconds):
+        """Untimed replays of graph g for `seconds` (clocks ramp up under load)."""
+        t0 = time.time()
+        while time.time() - t0 < seconds:
+            for _ in range(max(1, 64 // self.n_rot)):
+                g.replay()
+            self.torch.cuda.synchronize()
+
+    def summary(self, nsplit, steps, kernel_steps, settle=0.1):
         """Steps/s and the split kernel's time and gathered-KV rate at nsplit."""
-        step_us, n = self.time_graph(self.graph_of(self.step_fn(nsplit)), steps)
+        g = self.graph_of(self.step_fn(nsplit))
+        self.settle(g, settle)
+        step_us, n = self.time_graph(g, steps)
         split_us = self.split_time(nsplit, kernel_steps, step_us)
         return {"nsplit": nsplit, "us_per_step": round(step_us, 3), "steps_per_s": round(1e6 / step_us, 2),
                 "gathered_kv_gbps_per_step": round(self.mean_kv_bytes / (step_us * 1e-6) / 1e9, 2),
@@ -308,11 +319,7 @@ def main():
         step(i)
     torch.cuda.synchronize()
     graph = w.graph_of(step)
-    t_settle = time.time()
-    while time.time() - t_settle < args.settle:
-        for _ in range(max(1, 64 // w.n_rot)):
-            graph.replay()
-        torch.cuda.synchronize()
+    w.settle(graph, args.settle)
     us_per_step, steps = w.time_graph(graph, args.steps)
     ms_per_step = us_per_step * 1e-3
     steps_per_s = 1e6 / us_per_step
@@ -325,7 +332,7 @@ def main():
     split_us = w.split_time(nsplit, args.kernel_steps, us_per_step)
     split_only = w.split_fn(nsplit) if rows_mode else step
     single_launch = None
-    if w.fused_in_launch(nsplit):
+    if not args.no_sweep and w.fused_in_launch(nsplit):
         fused_us = w.time_graph(w.graph_of(w.fused_fn(nsplit)), args.steps)[0]
         single_launch = {"us_per_step": round(fused_us, 3), "steps_per_s": round(1e6 / fused_us, 2),
                          "entry_point": "smla_decode_fused",

@@ -250,6 +250,27 @@ int smla_split(const void *q, const void *kv_cache, const int32_t *topk_idx, voi
 int smla_combine(const float *part_o, const float *part_lse, void *out, float *lse, int tokens,
                  int heads, int nsplit, void *hip_stream);
 
+/*
+ * Top-k producer, the step before the path ("The Negative Result That
+ * Refined the Hunt", section "The Context": an indexer selects the candidate
+ * positions; "The Moment of Truth", section "The Split-K Imperative": the
+ * top-k set is the set of candidate tokens retrieved from the cache).  The
+ * pages give no indexer math: the scores are an input.  For every row (b, t)
+ * of scores [batch, q_len, max_ctx] fp32 (row stride max_ctx), with
+ * n = min(max(ctx_len[b], 0), max_ctx) (ctx_len NULL: n = max_ctx), writes to
+ * out_pos [batch, q_len, topk] int32 the positions of the topk largest
+ * scores among positions 0 .. n-1, in ascending position order; when
+ * n <= topk, positions 0 .. n-1 followed by -1.  Ranking: the IEEE total
+ * order of the fp32 bit patterns (-NaN < -inf < ... < -0 < +0 < ... < +inf <
+ * +NaN), equal values ranking the lower position first, so the selected set
+ * is unique.  The output is the topk_pos of smla_decode_paged (or, for a flat
+ * cache where positions are rows, the topk_idx of smla_decode).  scores,
+ * ctx_len and out_pos 4-byte aligned; scores may be NULL when max_ctx == 0.
+ * batch, q_len or topk 0 launch nothing.  Errors as smla_decode.
+ */
+int smla_topk(const float *scores, const int32_t *ctx_len, int batch, int q_len, int max_ctx,
+              int topk, int32_t *out_pos, void *hip_stream);
+
 /* Static description of a status code (never NULL). */
 const char *smla_status_str(int status);
 

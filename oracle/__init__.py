@@ -17,9 +17,13 @@ Page citations (by title and section):
            Decode Speedup on Blackwell" -- "The Occupancy Insight",
            "The Broader Context", "The Road to This Experiment".
 
+  [BISECT] "The Negative Result That Refined the Hunt: Disabling the MMA
+           FlashMLA Kernel" -- "The Context".
+
 Paged and dense calls (``rows_of_positions``, ``dense_positions``) are
 defined as a plain decode over the rows their positions name, so the oracle
-for them is the index map below followed by ``decode``.
+for them is the index map below followed by ``decode``.  The top-k producer
+(``topk_positions``) is a selection, defined by a sort.
 """
 from __future__ import annotations
 
@@ -229,4 +233,39 @@ def dense_positions(ctx_len, max_ctx: int, q_len: int) -> np.ndarray:
     for b, c in enumerate(ctx_len):
         n = min(int(c), max_ctx)
         out[b, :, :n] = np.arange(n)
+    return out.astype(np.int32)
+
+
+def score_keys(scores) -> np.ndarray:
+    """Rank keys of fp32 scores: the IEEE total order of their bit patterns
+    as unsigned 32-bit integers (a negative value's bits all flipped, any
+    other value's sign bit set), so -NaN < -inf < ... < -0 < +0 < ... <
+    +inf < +NaN.  Returns uint64 (no wrap in later arithmetic)."""
+    u = np.ascontiguousarray(scores, dtype=np.float32).view(np.uint32)
+    neg = (u >> np.uint32(31)) == 1
+    return np.where(neg, ~u, u | np.uint32(0x80000000)).astype(np.uint64)
+
+
+def topk_positions(scores, ctx_len, topk: int) -> np.ndarray:
+    """The top-k producer ([BISECT] "The Context": an indexer picks the
+    candidate positions; [SPLITK] "The Split-K Imperative": the top-k set is
+    the candidate tokens retrieved from the cache).  The pages give no
+    indexer math, so the scores are an input.
+
+    scores [B, Lq, M] fp32; ctx_len [B] int or None (M).  For row (b, t) with
+    n = min(max(ctx_len[b], 0), M): sort positions 0..n-1 by rank key
+    descending, ties by position ascending; take the first topk; return them
+    in ascending position order, -1 after the last when n < topk.
+    Returns int32 [B, Lq, topk]."""
+    scores = np.asarray(scores, dtype=np.float32)
+    B, Lq, M = scores.shape
+    keys = score_keys(scores)
+    out = np.full((B, Lq, topk), -1, np.int64)
+    for b in range(B):
+        n = M if ctx_len is None else min(max(int(ctx_len[b]), 0), M)
+        for t in range(Lq):
+            k = keys[b, t, :n].astype(np.int64)
+            order = np.lexsort((np.arange(n), -k))  # key descending, then position
+            chosen = np.sort(order[:topk])
+            out[b, t, :len(chosen)] = chosen
     return out.astype(np.int32)

@@ -354,6 +354,30 @@ SMLA_API int smla_combine(const float* part_o, const float* part_lse, void* out,
   return SMLA_OK;
 }
 
+SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, int q_len,
+                       int max_ctx, int topk, int32_t* out_pos, void* hip_stream) {
+  if (batch < 0 || q_len < 0 || max_ctx < 0 || topk < 0 || topk > SMLA_MAX_TOPK)
+    return SMLA_ERR_DIM;
+  const int64_t rows = (int64_t)batch * q_len;
+  if (rows == 0 || topk == 0) return SMLA_OK;
+  if (rows > 0x7fffffffLL) return SMLA_ERR_DIM;
+  if (!out_pos || (max_ctx > 0 && !scores)) return SMLA_ERR_NULL;
+  if (!aligned(scores, 4) || !aligned(ctx_len, 4) || !aligned(out_pos, 4)) return SMLA_ERR_ALIGN;
+  smla::TopkParams tp;
+  tp.scores = scores;
+  tp.ctx = ctx_len;
+  tp.out = out_pos;
+  tp.rows = rows;
+  tp.q_len = q_len;
+  tp.max_ctx = max_ctx;
+  tp.topk = topk;
+  if (smla::launch_topk(tp, (hipStream_t)hip_stream) != hipSuccess) {
+    (void)hipGetLastError();
+    return SMLA_ERR_LAUNCH;
+  }
+  return SMLA_OK;
+}
+
 SMLA_API const char* smla_status_str(int status) {
   switch (status) {
     case SMLA_OK: return "ok";

@@ -62,6 +62,15 @@ struct CombineParams {
   int tokens, heads, nsplit;
 };
 
+struct TopkParams {
+  const float* scores;  // [rows, max_ctx] fp32 index scores
+  const int32_t* ctx;   // [batch] valid positions per sequence, or null: max_ctx
+  int32_t* out;         // [rows, topk] selected positions, ascending, -1 padded
+  int64_t rows;         // batch * q_len
+  int q_len, max_ctx, topk;
+};
+
+hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 hipError_t launch_split(const SplitParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, hipStream_t st);
 int split_heads_per_block(int heads);

@@ -37,7 +37,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["smla_plan_nsplit", "smla_plan_nsplit_cus", "smla_workspace_bytes",
                             "smla_workspace_lse_offset", "smla_fused_in_launch", "smla_set_merge_polls",
-                            "smla_decode", "smla_decode_fused", "smla_decode_paged",
+                            "smla_decode", "smla_decode_fused", "smla_topk", "smla_decode_paged",
                             "smla_decode_dense", "smla_plan_nsplit_dense", "smla_split",
                             "smla_combine", "smla_status_str"]), names
 
@@ -292,3 +292,21 @@ def test_planner_path_without_device(smla):
     assert smla.lib.smla_fused_in_launch(1, 1, 8, 4) == -6
     # a valid fused call with NSPLIT > 1 asks the device whether to merge in-launch
     assert _call(smla, "smla_decode_fused", nsplit=4, ws=0x60000, ws_bytes=1 << 24) == -6
+
+
+def test_topk_arguments(smla):
+    """smla_topk validates before launching; empty calls launch nothing."""
+    f = smla.lib.smla_topk
+    vp = ctypes.c_void_p
+    sc, ctx, out = vp(0x10000), vp(0x20000), vp(0x30000)
+    assert f(sc, ctx, -1, 1, 100, 8, out, None) == -2
+    assert f(sc, ctx, 1, -1, 100, 8, out, None) == -2
+    assert f(sc, ctx, 1, 1, -5, 8, out, None) == -2
+    assert f(sc, ctx, 1, 1, 100, -1, out, None) == -2
+    assert f(sc, ctx, 1, 1, 100, (1 << 24) + 1, out, None) == -2
+    assert f(sc, ctx, 1, 1, 100, 8, None, None) == -1
+    assert f(None, ctx, 1, 1, 100, 8, out, None) == -1
+    assert f(vp(0x10002), ctx, 1, 1, 100, 8, out, None) == -5
+    assert f(sc, ctx, 1, 1, 100, 8, vp(0x30001), None) == -5
+    assert f(sc, ctx, 0, 1, 100, 8, out, None) == 0   # no rows
+    assert f(sc, ctx, 1, 1, 100, 0, out, None) == 0   # topk 0

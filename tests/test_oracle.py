@@ -344,3 +344,69 @@ def test_pin_dense_positions():
     assert d[0, 1].tolist() == [0, 1, 2, -1, -1]
     assert d[1, 0].tolist() == [-1] * 5
     assert d[2, 0].tolist() == [0, 1, 2, 3, 4]
+
+
+# ------------------------------------------------------------ top-k producer
+
+def _beats(a: float, b: float) -> bool:
+    """Whether score a ranks above score b, from float comparisons (not from
+    bit patterns): any +NaN above everything else, any -NaN below; among the
+    rest the larger value, and between equal values +0 above -0."""
+    import math
+    an, bn = math.isnan(a), math.isnan(b)
+    sa, sb = math.copysign(1.0, a) > 0, math.copysign(1.0, b) > 0
+    if an or bn:
+        ra = 2 if an and sa else -2 if an else 0
+        rb = 2 if bn and sb else -2 if bn else 0
+        return ra > rb
+    if a != b:
+        return a > b
+    return sa and not sb  # +0 above -0; identical values tie
+
+
+def _brute_topk(row, n, k):
+    """Position i is chosen iff fewer than k positions beat it, where j beats
+    i if its score ranks above i's, or ties with it at a lower position."""
+    vals = [float(v) for v in row[:n]]
+    chosen = []
+    for i in range(n):
+        beaten_by = sum(1 for j in range(n) if j != i and
+                        (_beats(vals[j], vals[i]) or (not _beats(vals[i], vals[j]) and j < i)))
+        if beaten_by < k:
+            chosen.append(i)
+    return chosen + [-1] * (k - len(chosen))
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "special"])
+def test_pin_topk_brute_force(kind):
+    rng = np.random.default_rng({"normal": 11, "ties": 12, "special": 13}[kind])
+    B, Lq, M = 3, 2, 70
+    if kind == "normal":
+        s = rng.standard_normal((B, Lq, M)).astype(np.float32)
+    elif kind == "ties":
+        s = rng.integers(-3, 4, size=(B, Lq, M)).astype(np.float32) * np.float32(0.25)
+    else:
+        pool = np.array([0.0, -0.0, 1.5, -1.5, np.inf, -np.inf, np.nan, -np.nan, 1e-40, -1e-40],
+                        np.float32)
+        s = pool[rng.integers(0, len(pool), size=(B, Lq, M))]
+    ctx = [70, 33, 5]
+    for k in (1, 4, 17, 40, 70, 80):
+        got = oracle.topk_positions(s, ctx, k)
+        for b in range(B):
+            for t in range(Lq):
+                assert got[b, t].tolist() == _brute_topk(s[b, t], min(ctx[b], M), k), (kind, k, b, t)
+
+
+def test_pin_topk_special_cases():
+    s = np.zeros((2, 1, 50), np.float32)  # all equal: the lowest positions win
+    assert oracle.topk_positions(s, None, 7)[0, 0].tolist() == list(range(7))
+    got = oracle.topk_positions(s, [3, -4], 5)  # short and negative contexts: -1 padding
+    assert got[0, 0].tolist() == [0, 1, 2, -1, -1] and got[1, 0].tolist() == [-1] * 5
+    assert oracle.topk_positions(s, [500, 50], 50)[0, 0].tolist() == list(range(50))  # clipped at M
+    r = np.arange(50, dtype=np.float32)[None, None, :].repeat(2, axis=0)  # increasing: the last k
+    assert oracle.topk_positions(r, None, 6)[1, 0].tolist() == list(range(44, 50))
+    # the same set as a partition of distinct values by a different library routine
+    rng = np.random.default_rng(5)
+    d = rng.permutation(4000).astype(np.float32)[None, None, :] - 1999.5
+    want = np.sort(np.argpartition(-d[0, 0], 300)[:300])
+    assert oracle.topk_positions(d, None, 300)[0, 0].tolist() == want.tolist()

@@ -27,7 +27,7 @@ DV = 512         # value width: the first 512 columns of a row
 PAGE = 64        # tokens per page in the paged pools
 SCALE = float(np.float32(1.0 / math.sqrt(192.0)))
 
-SUB_Q, SUB_KV, SUB_IDX, SUB_PAGES, SUB_CTX = 0, 1, 2, 3, 4
+SUB_Q, SUB_KV, SUB_IDX, SUB_PAGES, SUB_CTX, SUB_SCORES = 0, 1, 2, 3, 4, 5
 
 
 # ----------------------------------------------------------------- bf16 bits
@@ -189,6 +189,30 @@ def dense_inputs(name: str, seed: int, batch: int, q_len: int, heads: int, ctx,
     kv = normal_bf16(np.random.default_rng(seed + SUB_KV), (kv_rows, D)) if with_kv else None
     return Inputs(name, q, kv, idx, kv_rows, pool_seed=None if with_kv else seed + SUB_KV,
                   ctx=ctx, page_table=table, pos=pos, dense=True)
+
+
+def index_scores(seed: int, batch: int, q_len: int, max_ctx: int, kind: str = "normal") -> np.ndarray:
+    """Synthetic index scores [batch, q_len, max_ctx] fp32 for the top-k
+    producer (real ones come from a trained indexer, which the pages do not
+    describe).  kind: "normal" N(0,1); "ties" multiples of 1/4 in [-1, 1]
+    (every value repeats many times); "equal" all zero; "special" a mix of
+    +-0, +-inf, +-NaN, subnormals and ordinary values."""
+    rng = np.random.default_rng(seed + SUB_SCORES)
+    shape = (batch, q_len, max_ctx)
+    if kind == "normal":
+        return rng.standard_normal(shape, dtype=np.float32)
+    if kind == "ties":
+        return rng.integers(-4, 5, size=shape).astype(np.float32) * np.float32(0.25)
+    if kind == "equal":
+        return np.zeros(shape, np.float32)
+    if kind == "special":
+        pool = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, -np.nan, 1e-40, -1e-40, 3.0, -3.0],
+                        np.float32)
+        s = rng.standard_normal(shape, dtype=np.float32)
+        pick = rng.random(shape) < 0.3
+        s[pick] = pool[rng.integers(0, len(pool), size=int(pick.sum()))]
+        return s
+    raise ValueError(kind)
 
 
 # The five workload shapes: (1) tiny, (2) single request at long context,

@@ -23,6 +23,10 @@ Timing protocol
   * single_launch: the same step through smla_decode_fused, the merge inside
     the split launch (list workloads, when the shape allows it; skipped with
     --no-sweep, so that a profiled run holds only the two-launch kernels);
+  * topk: the top-k producer (smla_topk) on synthetic N(0,1) index scores of
+    the workload's shape (every context position of every query token),
+    graph-timed, with the score bytes it must read per call against the
+    HBM roofline (skipped with --no-sweep);
   * cpu_baseline: the fp64 oracle, as is, on the host cores, over a bounded
     sample of the same workload, scaled to steps/s;
   * nsplit_sweep: steps/s and the split kernel's gathered-KV rate of the same
@@ -266,9 +270,12 @@ class Workload:
 
     def settle(self, g, seconds):
         """Untimed replays of graph g for `seconds` (clocks ramp up under load)."""
+        self.settle_graph(g, seconds, max(1, 64 // self.n_rot))
+
+    def settle_graph(self, g, seconds, per_sync=1):
         t0 = time.time()
         while time.time() - t0 < seconds:
-            for _ in range(max(1, 64 // self.n_rot)):
+            for _ in range(per_sync):
                 g.replay()
             self.torch.cuda.synchronize()
 
@@ -284,6 +291,49 @@ class Workload:
                 "split_kv_gbps": round(self.mean_kv_bytes / (split_us * 1e-6) / 1e9, 2),
                 "split_roofline_frac": round(self.mean_kv_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                 "steps_timed": n}
+
+
+def topk_figure(w, steps):
+    """smla_topk over index scores shaped like the workload: one row per
+    query token over its whole context; rotation over score sets whose bytes
+    exceed 512 MB when a set is smaller (cold reads)."""
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    inp = w.inp
+    max_ctx = int(inp.ctx.max()) if inp.ctx is not None else inp.kv_rows
+    k = inp.topk
+    set_bytes = w.B * w.Lq * max_ctx * 4
+    n_sets = max(1, min(64, -(-(512 << 20) // set_bytes)))
+    sets = [torch.from_numpy(wl.index_scores(9000 + i, w.B, w.Lq, max_ctx)).to(w.dev) for i in range(n_sets)]
+    ctx = torch.tensor(inp.ctx, dtype=torch.int32, device=w.dev) if inp.ctx is not None else None
+    out = torch.empty((w.B, w.Lq, k), dtype=torch.int32, device=w.dev)
+    g = torch.cuda.CUDAGraph()
+    torch.cuda.synchronize()
+    w.stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(w.stream):
+        with torch.cuda.graph(g, stream=w.stream):
+            for i in range(n_sets):
+                w.smla.smla_topk(sets[i], k, out, ctx)
+    torch.cuda.synchronize()
+    w.settle_graph(g, 0.1)
+    reps = max(1, -(-steps // n_sets))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = 1e3 * a.elapsed_time(b) / (reps * n_sets)
+    valid = int(np.sum(np.minimum(inp.ctx, max_ctx))) * w.Lq if inp.ctx is not None else w.B * w.Lq * max_ctx
+    read = valid * 4 + w.B * w.Lq * k * 4
+    return {"us_per_call": round(us, 3), "rows": w.B * w.Lq, "positions_per_row": max_ctx, "topk": k,
+            "bytes_per_call": read, "gbps": round(read / (us * 1e-6) / 1e9, 2),
+            "roofline_frac": round(read / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "cache_state": f"rotation over {n_sets} score sets",
+            "bytes": "valid scores x 4 B read + topk x 4 B written per row",
+            "entry_point": "smla_topk"}
 
 
 def main():
@@ -332,6 +382,11 @@ def main():
     split_us = w.split_time(nsplit, args.kernel_steps, us_per_step)
     split_only = w.split_fn(nsplit) if rows_mode else step
     single_launch = None
+    topk = None
+    if not args.no_sweep and w.kind != "dense":
+        topk = topk_figure(w, min(args.steps, 512))
+        log(f"[bench] topk producer: {topk['us_per_call']:.2f} us per call ({topk['rows']} rows x "
+            f"{topk['positions_per_row']} positions, k={topk['topk']}, {topk['gbps']:.0f} GB/s of scores)")
     if not args.no_sweep and w.fused_in_launch(nsplit):
         fused_us = w.time_graph(w.graph_of(w.fused_fn(nsplit)), args.steps)[0]
         single_launch = {"us_per_step": round(fused_us, 3), "steps_per_s": round(1e6 / fused_us, 2),
@@ -441,6 +496,8 @@ def main():
     }
     if single_launch:
         result["single_launch"] = single_launch
+    if topk:
+        result["topk_producer"] = topk
     if sweep:
         result["nsplit_sweep"] = sweep
     if secondary:

@@ -13,15 +13,18 @@
 // unique, and it is written in ascending position order.
 //
 // Algorithm: one workgroup per row.  A radix select over the key finds the
-// topk-th largest key T in three histogram passes (11, 11 and 10 bits, each
-// over the elements whose higher bits match the bins found so far; LDS
-// histograms).  A last pass walks the row in position order, one element per
-// thread per tile: an element is taken if its key exceeds T, or equals T and
-// fewer than (topk - count above T) equal keys precede it; one block-wide scan
-// per tile gives each taken element its output slot.  Rows with no more valid
-// positions than topk take them all and pad with -1.  Loads are coalesced
-// (thread t reads position base + t); after the first pass the row is served
-// by the L2.
+// topk-th largest key T digit by digit (11, 11 and 10 bits), each digit from
+// an LDS histogram of the keys whose higher bits match the digits found so
+// far.  The first digit's histogram covers the whole row; the keys in its
+// bin are then copied, with their positions, into LDS (when they fit), so
+// the last two digits never touch memory again; otherwise (heavy ties) those
+// digits re-read the row.  A last pass walks the row in position order, each
+// thread over 16 consecutive positions per tile: an element is taken if its
+// key exceeds T, or equals T and fewer than (topk - count above T) equal keys
+// precede it; one block-wide scan per tile gives every taken element its
+// output slot.  Rows with no more valid positions than topk take them all
+// and pad with -1.  Every thread keeps 16 loads in flight; after the first
+// pass the row is served by the L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -32,7 +35,10 @@ namespace {
 
 constexpr int kTopkThreads = 1024;
 constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kBins = 2048;  // 11-bit digits (the last digit has 10 bits)
+constexpr int kBins = 2048;   // 11-bit digits (the last digit has 10 bits)
+constexpr int kPer = 16;      // elements per thread per tile (loads in flight)
+constexpr int kTile = kTopkThreads * kPer;
+constexpr int kCandCap = 8192;  // keys of the first digit's bin kept in LDS
 
 __device__ __forceinline__ uint32_t score_key(float x) {
   const uint32_t u = __float_as_uint(x);
@@ -69,10 +75,49 @@ __device__ __forceinline__ uint32_t scan_excl(uint32_t v, uint32_t* sw, uint32_t
   return r;
 }
 
+// Keys of one coalesced tile: element j of thread t is position
+// base + j * kTopkThreads + t; positions at or past n read as key 0 with
+// valid = false.  All kPer loads are issued before any is used.
+__device__ __forceinline__ void load_tile(const float* sc, int base, int n, uint32_t (&k)[kPer],
+                                          uint32_t& valid) {
+  float v[kPer];
+  valid = 0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int pos = base + j * kTopkThreads + (int)threadIdx.x;
+    v[j] = pos < n ? sc[pos] : 0.f;
+    valid |= (uint32_t)(pos < n) << j;
+  }
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) k[j] = score_key(v[j]);
+}
+
+// The digit (bits [sh, sh + width)) at which the count of counted keys,
+// from the top, reaches `need`: returns it in sel[0] and the count of keys
+// in higher bins in sel[1] (one thread finds the crossing).
+__device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, uint32_t* sw,
+                                           uint32_t* sel) {
+  const int tid = threadIdx.x;
+  const int hi = kBins - 1 - 2 * tid, lo = hi - 1;  // bins past the digit's width are empty
+  const uint32_t ch = hist[hi], cl = hist[lo];
+  uint32_t tot;
+  const uint32_t ex = scan_excl(ch + cl, sw, &tot);
+  if (ex < need && ex + ch >= need) {
+    sel[0] = (uint32_t)hi;
+    sel[1] = ex;
+  } else if (ex + ch < need && ex + ch + cl >= need) {
+    sel[0] = (uint32_t)lo;
+    sel[1] = ex + ch;
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t sw[kTopkWaves + 1];
-  __shared__ uint32_t sel[2];  // the bin found, the count of keys above it
+  __shared__ uint32_t sel[2];  // the digit found, the count of keys above it
+  __shared__ uint32_t ncand;
+  __shared__ uint32_t cand[kCandCap];  // keys of the first digit's bin
 
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -88,66 +133,103 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
     return;
   }
 
-  // ---- radix select of the topk-th largest key: digit d of the key is
-  // bits [sh, sh + width) with (sh, width) = (21, 11), (10, 11), (0, 10);
-  // prefix = the key bits above the digit found so far
-  uint32_t prefix = 0, need = (uint32_t)p.topk;
+  // ---- first digit (bits 21..31) over the whole row
+  for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  for (int base = 0; base < n; base += kTile) {
+    uint32_t k[kPer], valid;
+    load_tile(sc, base, n, k, valid);
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (valid >> j & 1) atomicAdd(&hist[k[j] >> 21], 1u);
+  }
+  __syncthreads();
+  uint32_t need = (uint32_t)p.topk;
+  find_digit(hist, need, sw, sel);
+  uint32_t prefix = sel[0];
+  need -= sel[1];
+  const uint32_t in_bin = hist[prefix];
+  const bool cached = in_bin <= (uint32_t)kCandCap;
+  __syncthreads();
+
+  // ---- keys of that bin into LDS (order irrelevant: only counted below)
+  if (cached) {
+    for (int base = 0; base < n; base += kTile) {
+      uint32_t k[kPer], valid;
+      load_tile(sc, base, n, k, valid);
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        if ((valid >> j & 1) && (k[j] >> 21) == prefix) cand[atomicAdd(&ncand, 1u)] = k[j];
+    }
+    __syncthreads();
+  }
+
+  // ---- second and third digits (bits 10..20, then 0..9) among the keys
+  // whose higher digits match
 #pragma unroll 1
-  for (int level = 0; level < 3; ++level) {
-    const int sh = level == 0 ? 21 : level == 1 ? 10 : 0;
-    const int width = level == 2 ? 10 : 11;
-    const int hsh = sh + width;  // bits of the prefix start here (32: none)
+  for (int level = 1; level < 3; ++level) {
+    const int sh = level == 1 ? 10 : 0;
+    const int width = level == 1 ? 11 : 10;
+    const int hsh = sh + width;
+    const uint32_t mask = (1u << width) - 1;
     for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
     __syncthreads();
-    for (int base = 0; base < n; base += kTopkThreads) {
-      const int pos = base + tid;
-      if (pos < n) {
-        const uint32_t k = score_key(sc[pos]);
-        if (hsh >= 32 || (k >> hsh) == prefix)
-          atomicAdd(&hist[(k >> sh) & ((1u << width) - 1)], 1u);
+    if (cached) {
+      for (uint32_t i = tid; i < in_bin; i += kTopkThreads) {
+        const uint32_t k = cand[i];
+        if ((k >> hsh) == prefix) atomicAdd(&hist[(k >> sh) & mask], 1u);
+      }
+    } else {
+      for (int base = 0; base < n; base += kTile) {
+        uint32_t k[kPer], valid;
+        load_tile(sc, base, n, k, valid);
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if ((valid >> j & 1) && (k[j] >> hsh) == prefix) atomicAdd(&hist[(k[j] >> sh) & mask], 1u);
       }
     }
     __syncthreads();
-    // scan the bins from the top: thread t holds bins hi = kBins-1-2t and
-    // lo = hi - 1 (bins past the digit's width are empty)
-    const int hi = kBins - 1 - 2 * tid, lo = hi - 1;
-    const uint32_t ch = hist[hi], cl = hist[lo];
-    uint32_t tot;
-    const uint32_t ex = scan_excl(ch + cl, sw, &tot);
-    if (ex < need && ex + ch >= need) {
-      sel[0] = (uint32_t)hi;
-      sel[1] = ex;
-    } else if (ex + ch < need && ex + ch + cl >= need) {
-      sel[0] = (uint32_t)lo;
-      sel[1] = ex + ch;
-    }
-    __syncthreads();
+    find_digit(hist, need, sw, sel);
     prefix = (prefix << width) | sel[0];
     need -= sel[1];
     __syncthreads();
   }
-  const uint32_t T = prefix;  // the topk-th largest key; `need` equal keys are taken
+  const uint32_t T = prefix;  // the topk-th largest key; `need` keys equal to it are taken
 
-  // ---- ordered selection: keys above T, and the first `need` keys equal to T
+  // ---- ordered selection: keys above T, and the first `need` keys equal to
+  // T; thread t walks positions base + kPer*t .. + kPer-1 of each tile
   uint32_t written = 0, ties_seen = 0;
-  for (int base = 0; base < n && written < (uint32_t)p.topk; base += kTopkThreads) {
-    const int pos = base + tid;
-    uint32_t gt = 0, eq = 0;
-    if (pos < n) {
-      const uint32_t k = score_key(sc[pos]);
-      gt = k > T;
-      eq = k == T;
+  for (int base = 0; base < n && written < (uint32_t)p.topk; base += kTile) {
+    const int p0 = base + kPer * tid;
+    float v[kPer];
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) v[j] = p0 + j < n ? sc[p0 + j] : 0.f;
+    uint32_t gtm = 0, eqm = 0;  // bit j: element j above / equal to T
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const uint32_t k = score_key(v[j]);
+      const bool ok = p0 + j < n;
+      gtm |= (uint32_t)(ok && k > T) << j;
+      eqm |= (uint32_t)(ok && k == T) << j;
     }
     uint32_t tot;
-    const uint32_t ex = scan_excl(gt | (eq << 16), sw, &tot);
-    const uint32_t gt_ex = ex & 0xffffu, eq_ex = ex >> 16;
-    const uint32_t gt_tot = tot & 0xffffu, eq_tot = tot >> 16;
+    const uint32_t ex = scan_excl((uint32_t)__builtin_popcount(gtm) | ((uint32_t)__builtin_popcount(eqm) << 16),
+                                  sw, &tot);
     const uint32_t rem = need > ties_seen ? need - ties_seen : 0u;  // ties still to take
-    const bool take = gt || (eq && eq_ex < rem);
-    const uint32_t slot = written + gt_ex + min(eq_ex, rem);
-    if (take && slot < (uint32_t)p.topk) out[slot] = pos;
-    written += gt_tot + min(eq_tot, rem);
-    ties_seen += eq_tot;
+    uint32_t gt_before = ex & 0xffffu, eq_before = ex >> 16;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const bool gt = gtm >> j & 1, eq = eqm >> j & 1;
+      if (gt || (eq && eq_before < rem)) {
+        const uint32_t slot = written + gt_before + min(eq_before, rem);
+        if (slot < (uint32_t)p.topk) out[slot] = p0 + j;
+      }
+      gt_before += gt;
+      eq_before += eq;
+    }
+    written += (tot & 0xffffu) + min(tot >> 16, rem);
+    ties_seen += tot >> 16;
   }
 }
 

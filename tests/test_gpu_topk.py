@@ -5,7 +5,8 @@ oracle.topk_positions element for element (selected set, ascending order and
 -1 padding).  Scores: N(0,1), heavy ties, all equal, and a mix of special
 values (+-0, +-inf, +-NaN, subnormals), over rows that are shorter than topk,
 exactly topk, one longer, not a multiple of the workgroup width, with and
-without per-sequence context lengths; then the full sizes of the batch-1
+without per-sequence context lengths, with more equal keys than the LDS
+candidate copy holds; then the full sizes of the batch-1
 (65536) and batch-64 (32768) shapes and ragged contexts up to 131072,
 compared on every row.  Last, the path end to end: scores -> smla_topk ->
 smla_decode_paged against oracle.topk_positions -> rows_of_positions ->
@@ -56,6 +57,7 @@ CASES = [  # kind, batch, q_len, max_ctx, topk, ctx
     ("equal", 2, 1, 7000, 2048, [7000, 3000]),
     ("special", 2, 2, 6000, 700, [6000, 5999]),
     ("normal", 1, 1, 20000, 5000, None),
+    ("equal", 1, 2, 20000, 2048, None),      # > 8192 keys in the first digit's bin: no LDS copy
 ]
 
 
@@ -73,6 +75,16 @@ def test_topk_full_size(smla, shape):
     scores = index_scores(7100 + b, b, lq, m, "normal")
     got = _run(smla, scores, 2048)
     _same(got, oracle.topk_positions(scores, None, 2048), f"full size {shape}")
+
+
+def test_topk_two_values(smla):
+    """Half the scores 1.0, half 0.0, over 30000 positions: the threshold bin
+    holds about 15000 keys (more than the LDS copy takes) and the ties at 1.0
+    must go to the lowest positions."""
+    rng = np.random.default_rng(7150)
+    scores = (rng.random((2, 1, 30000)) < 0.5).astype(np.float32)
+    for k in (2048, 15000, 29999):
+        _same(_run(smla, scores, k), oracle.topk_positions(scores, None, k), f"two values k={k}")
 
 
 def test_topk_ragged_contexts(smla):

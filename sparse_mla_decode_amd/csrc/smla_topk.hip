@@ -18,13 +18,15 @@
 // far.  The first digit's histogram covers the whole row; the keys in its
 // bin are then copied, with their positions, into LDS (when they fit), so
 // the last two digits never touch memory again; otherwise (heavy ties) those
-// digits re-read the row.  A last pass walks the row in position order, each
-// thread over 16 consecutive positions per tile: an element is taken if its
-// key exceeds T, or equals T and fewer than (topk - count above T) equal keys
-// precede it; one block-wide scan per tile gives every taken element its
-// output slot.  Rows with no more valid positions than topk take them all
-// and pad with -1.  Every thread keeps 16 loads in flight; after the first
-// pass the row is served by the L2.
+// digits re-read the row.  A last pass walks the row in position order: an
+// element is taken if its key exceeds T, or equals T and fewer than
+// (topk - count above T) equal keys precede it.  Its output slot is the count
+// of taken elements before it: inside a wave from ballots (a masked
+// popcount), across the (element, wave) blocks of a tile from one 256-entry
+// scan.  Rows with no more valid positions than topk take them all and pad
+// with -1.  Every pass reads coalesced tiles (element j of thread t is
+// position base + j * 1024 + t) with 16 loads in flight per thread; after the
+// first pass the row is served by the L2.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -118,6 +120,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   __shared__ uint32_t sel[2];  // the digit found, the count of keys above it
   __shared__ uint32_t ncand;
   __shared__ uint32_t cand[kCandCap];  // keys of the first digit's bin
+  __shared__ uint32_t blk[kPer * kTopkWaves + 1];  // per (element, wave) counts, then prefixes
 
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -198,38 +201,70 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   const uint32_t T = prefix;  // the topk-th largest key; `need` keys equal to it are taken
 
   // ---- ordered selection: keys above T, and the first `need` keys equal to
-  // T; thread t walks positions base + kPer*t .. + kPer-1 of each tile
+  // T.  Position order inside a tile is (element j, wave, lane); counts are
+  // packed as (above | equal << 16), at most 16384 each per tile.
+  const int lane = tid & 63, wave = tid >> 6;
   uint32_t written = 0, ties_seen = 0;
   for (int base = 0; base < n && written < (uint32_t)p.topk; base += kTile) {
-    const int p0 = base + kPer * tid;
-    float v[kPer];
-#pragma unroll
-    for (int j = 0; j < kPer; ++j) v[j] = p0 + j < n ? sc[p0 + j] : 0.f;
-    uint32_t gtm = 0, eqm = 0;  // bit j: element j above / equal to T
+    uint32_t k[kPer], valid;
+    load_tile(sc, base, n, k, valid);
+    uint64_t gtb[kPer], eqb[kPer];
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const uint32_t k = score_key(v[j]);
-      const bool ok = p0 + j < n;
-      gtm |= (uint32_t)(ok && k > T) << j;
-      eqm |= (uint32_t)(ok && k == T) << j;
+      const bool ok = valid >> j & 1;
+      gtb[j] = __ballot(ok && k[j] > T);
+      eqb[j] = __ballot(ok && k[j] == T);
     }
-    uint32_t tot;
-    const uint32_t ex = scan_excl((uint32_t)__builtin_popcount(gtm) | ((uint32_t)__builtin_popcount(eqm) << 16),
-                                  sw, &tot);
+    if (lane == 0) {
+#pragma unroll
+      for (int j = 0; j < kPer; ++j)
+        blk[j * kTopkWaves + wave] =
+            (uint32_t)__builtin_popcountll(gtb[j]) | ((uint32_t)__builtin_popcountll(eqb[j]) << 16);
+    }
+    __syncthreads();
+    if (wave == 0) {  // exclusive scan of the 256 block counts, 4 per lane
+      constexpr int kB = kPer * kTopkWaves / 64;
+      uint32_t c[kB], sum = 0;
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        c[i] = blk[lane * kB + i];
+        sum += c[i];
+      }
+      uint32_t inc = sum;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(inc, d, 64);
+        if (lane >= d) inc += y;
+      }
+      uint32_t run = inc - sum;
+#pragma unroll
+      for (int i = 0; i < kB; ++i) {
+        blk[lane * kB + i] = run;
+        run += c[i];
+      }
+      if (lane == 63) blk[kPer * kTopkWaves] = inc;
+    }
+    __syncthreads();
     const uint32_t rem = need > ties_seen ? need - ties_seen : 0u;  // ties still to take
-    uint32_t gt_before = ex & 0xffffu, eq_before = ex >> 16;
 #pragma unroll
     for (int j = 0; j < kPer; ++j) {
-      const bool gt = gtm >> j & 1, eq = eqm >> j & 1;
+      const uint32_t pre = blk[j * kTopkWaves + wave];
+      const bool gt = gtb[j] >> lane & 1, eq = eqb[j] >> lane & 1;
+      const uint32_t gt_before =
+          (pre & 0xffffu) + __builtin_amdgcn_mbcnt_hi((uint32_t)(gtb[j] >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)gtb[j], 0u));
+      const uint32_t eq_before =
+          (pre >> 16) + __builtin_amdgcn_mbcnt_hi((uint32_t)(eqb[j] >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)eqb[j], 0u));
       if (gt || (eq && eq_before < rem)) {
         const uint32_t slot = written + gt_before + min(eq_before, rem);
-        if (slot < (uint32_t)p.topk) out[slot] = p0 + j;
+        if (slot < (uint32_t)p.topk) out[slot] = base + j * kTopkThreads + tid;
       }
-      gt_before += gt;
-      eq_before += eq;
     }
+    const uint32_t tot = blk[kPer * kTopkWaves];
     written += (tot & 0xffffu) + min(tot >> 16, rem);
     ties_seen += tot >> 16;
+    __syncthreads();  // blk is rewritten by the next tile
   }
 }
 

@@ -6,7 +6,7 @@ oracle.topk_positions element for element (selected set, ascending order and
 values (+-0, +-inf, +-NaN, subnormals), over rows that are shorter than topk,
 exactly topk, one longer, not a multiple of the workgroup width, with and
 without per-sequence context lengths, with more equal keys than the LDS
-candidate copy holds; then the full sizes of the batch-1
+candidate copy holds, with rows 16-byte aligned (16-byte loads) or not; then the full sizes of the batch-1
 (65536) and batch-64 (32768) shapes and ragged contexts up to 131072,
 compared on every row.  Last, the path end to end: scores -> smla_topk ->
 smla_decode_paged against oracle.topk_positions -> rows_of_positions ->
@@ -58,6 +58,8 @@ CASES = [  # kind, batch, q_len, max_ctx, topk, ctx
     ("special", 2, 2, 6000, 700, [6000, 5999]),
     ("normal", 1, 1, 20000, 5000, None),
     ("equal", 1, 2, 20000, 2048, None),      # > 8192 keys in the first digit's bin: no LDS copy
+    ("normal", 2, 1, 5001, 2048, [5001, 4999]),  # rows not 16-byte aligned: 4-byte loads
+    ("ties", 1, 1, 9001, 2048, None),
 ]
 
 

@@ -92,6 +92,8 @@ def parse():
                     help="seconds of untimed graph replays before the timed steps")
     ap.add_argument("--no-sweep", action="store_true",
                     help="skip the NSPLIT sweep, the single-launch figure and the secondary batch-64 figure")
+    ap.add_argument("--topk-only", action="store_true",
+                    help="only time the top-k producer on the workload's shape (one JSON line) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration) and exit")
     return ap.parse_args()
@@ -358,6 +360,10 @@ def main():
     B, Lq, H, K, T = w.B, w.Lq, w.H, w.K, w.T
     log(f"[bench] workload={args.workload} B={B} Lq={Lq} H={H} K={K} kv_rows={w.inp.kv_rows} "
         f"caches={w.n_caches} index_sets={len(w.sets)}")
+    if args.topk_only:
+        tk = topk_figure(w, args.steps)
+        print(json.dumps({"workload": args.workload, "topk_producer": tk}), flush=True)
+        return
     nsplit = args.nsplit if args.nsplit > 0 else w.plan()
     rows_mode = w.kind == "rows"
     step = w.step_fn(nsplit)

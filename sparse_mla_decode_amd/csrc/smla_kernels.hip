@@ -407,7 +407,6 @@ void split_kernel(SplitParams p) {
   constexpr int KP = TR / 32;                 // 32-row K-steps of PV per tile
   constexpr int L = TR * kRowGran / NTD;      // DMA instructions per loading thread per tile
   constexpr int kTileBytes = TR * kRow * 2;
-  constexpr int kRowBytes = kRow * 2;
   constexpr int CB = (kDV / 16) / NCS;        // 16-column blocks of O per wave
   // QK^T K-steps per wave: all 18, or with K-split pairs the 9 of one parity
   constexpr int KSW = KSPLIT ? kKSteps / 2 : kKSteps;

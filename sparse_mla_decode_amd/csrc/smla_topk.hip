@@ -206,7 +206,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   __syncthreads();
 
   // ---- keys of that bin into LDS (order irrelevant: only counted below)
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
   if (cached) {
     for_tiles<kPerScan, V4>(sc, n, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
       uint32_t mm = 0;  // bit j: element j is in the bin

@@ -14,21 +14,27 @@
 //            flash-decode style partial + reduce.
 //
 // Design for CDNA4 (gfx950, wave64):
-//   * workgroup = (token, split, head block); a head block is up to 64 heads
-//     = 4 groups of 16 (the M/N width of one MFMA), one or two waves each.
-//   * the split's rows are gathered in tiles of 32 or 64 rows (x 1152 B)
-//     with 16-byte loads by all threads, staged through registers into a
-//     padded LDS tile (double buffered): the loads of tile n+1 are in flight
-//     while tile n is computed.  Every wave of the workgroup reads the
-//     same LDS tile, so a row is fetched from HBM once per workgroup.
+//   * workgroup = (token, head block, split); a head block is 16, 32 or 64
+//     heads (by head count) in groups of 16, the N width of one MFMA.
+//   * the split's rows are gathered in 32-row tiles (x 1152 B) by LDS-DMA
+//     (global_load_lds, 16 bytes per lane), straight into one of two LDS
+//     tile buffers laid out for the measured bank rules: tile n+1 loads while
+//     tile n is computed.  Every wave of the workgroup reads the same tile,
+//     so a row is fetched from HBM once per workgroup.
 //   * S^T = KV_tile * Q^T on v_mfma_f32_16x16x32_bf16 (rows on M, heads on N)
-//     so that each lane owns one head: the online-softmax max needs only two
+//     so that each lane owns one head: the online-softmax max needs two
 //     cross-lane exchanges per tile and the running sum none until the end.
+//     The waves of a 16-head group pair up along K (even / odd K-steps) and
+//     add their halves through LDS (16- and 64-head blocks).
 //   * O^T += V^T * P^T on the same MFMA; the softmax output is already laid
-//     out as the B operand (no shuffles), V^T is read from the LDS tile.
+//     out as the B operand (no shuffles), V^T comes from LDS transpose reads;
+//     the waves of a head group split the 512 value columns.
 //   * masked entries (-1, out of range, past the slice end) load a static
 //     all-zero row, so their V contribution is exactly zero, and get a score
 //     of -inf.
+//   * the partials are merged by a second launch (combine kernels), or, for
+//     smla_decode_fused, inside the split launch (fused_combine).
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -338,8 +344,10 @@ __device__ __forceinline__ void fused_combine(const SplitParams& p, int unit, in
 // ---------------------------------------------------------------------------
 // Split kernel.  HG head groups of 16 per workgroup; each wave owns GPW
 // head groups and one of NCS column slices of the 512 value columns.  Every
-// wave computes S for its head groups; the PV work and the O accumulators
-// are divided among the NCS waves that share head groups.  With GPW = 2 a
+// wave holds S for its head groups: it computes all of QK^T, or with KSPLIT
+// the K-steps of one parity, the two parities adding their halves through
+// LDS; the PV work and the O accumulators are divided among the NCS waves
+// that share head groups.  With GPW = 2 a
 // wave feeds every LDS operand read (a K-tile of QK^T, a V^T block of PV) to
 // two MFMAs, one per head group, halving LDS traffic per head; it then needs
 // about 460 registers and runs one wave per SIMD.  TR rows per tile, two
@@ -1029,8 +1037,9 @@ static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t 
 //    SIMD, i.e. 8 waves per CU).  Two head groups per wave would halve the
 //    LDS reads per head but need about 480 registers, one wave per SIMD:
 //    measured 20% slower, the LDS latency is no longer hidden.  A third tile
-//    buffer (two tiles in flight) measured 13% slower: it gained nothing in
-//    overlap and its always-issued refills round the tile count up.
+//    buffer (two tiles in flight) measured about 3% slower on a 64 x 64-head
+//    batch: it gained nothing in overlap, and its refills, issued every step
+//    so that the compiler keeps the pipeline full, round the tile count up.
 constexpr int kGpwLarge = 1;
 static_assert(kCuLdsBytes / split_lds_bytes(4, 4, 1, true) == 2, "two 16-head workgroups per CU");
 static_assert(kCuLdsBytes / split_lds_bytes(4, 2, 1, false) == 2, "two 32-head workgroups per CU");

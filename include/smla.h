@@ -45,7 +45,7 @@
  * Ownership and execution.  The caller owns every buffer, including the
  * workspace; the library allocates no device memory and keeps no per-call
  * state (its globals are a per-device cache of the CU count and the
- * smla_set_merge_polls setting).  Work is
+ * smla_set_merge_polls and smla_set_topk_min_chunks settings).  Work is
  * enqueued on `hip_stream` (a hipStream_t; NULL = the legacy default stream)
  * and the call returns without waiting for it: buffers must stay alive and
  * unmodified until the stream has passed the call.  The calls never
@@ -266,10 +266,32 @@ int smla_combine(const float *part_o, const float *part_lse, void *out, float *l
  * is unique.  The output is the topk_pos of smla_decode_paged (or, for a flat
  * cache where positions are rows, the topk_idx of smla_decode).  scores,
  * ctx_len and out_pos 4-byte aligned; scores may be NULL when max_ctx == 0.
- * batch, q_len or topk 0 launch nothing.  Errors as smla_decode.
+ * batch, q_len or topk 0 launch nothing.
+ *
+ * Work split.  Without a workspace (NULL, or smaller than
+ * smla_topk_workspace_bytes) one workgroup selects each row.  With one, and
+ * when there are fewer rows than twice the CUs and a row spans at least
+ * smla_set_topk_min_chunks chunks of 4096 positions (default 12), each row
+ * is also cut into chunks over several workgroups (four launches: chunk
+ * histograms, a row scan, candidate lists in position order, the
+ * selection); same output.  The workspace (256-byte aligned) is
+ * scratch: any content on entry, nothing kept after the call.
+ * Errors as smla_decode (SMLA_ERR_DEVICE only when a workspace is given and
+ * the CU count cannot be read).
  */
 int smla_topk(const float *scores, const int32_t *ctx_len, int batch, int q_len, int max_ctx,
-              int topk, int32_t *out_pos, void *hip_stream);
+              int topk, int32_t *out_pos, void *workspace, size_t workspace_bytes,
+              void *hip_stream);
+
+/* Bytes of workspace for smla_topk's multi-workgroup form. */
+size_t smla_topk_workspace_bytes(int batch, int q_len, int max_ctx);
+
+/*
+ * The chunk count from which smla_topk cuts rows over several workgroups
+ * (0 = never).  Process-wide; applies to calls made after it.  Returns the
+ * previous value, or SMLA_ERR_DIM if min_chunks < 0.
+ */
+int smla_set_topk_min_chunks(int min_chunks);
 
 /* Static description of a status code (never NULL). */
 const char *smla_status_str(int status);

@@ -10,7 +10,8 @@ without the built library raises ImportError.
 Functions carry the C names: smla_plan_nsplit, smla_plan_nsplit_cus,
 smla_workspace_bytes, smla_workspace_lse_offset, smla_decode, smla_decode_fused,
 smla_fused_in_launch, smla_set_merge_polls, smla_decode_paged, smla_decode_dense,
-smla_plan_nsplit_dense, smla_split, smla_combine, smla_topk, smla_status_str.
+smla_plan_nsplit_dense, smla_split, smla_combine, smla_topk, smla_topk_workspace_bytes,
+smla_set_topk_min_chunks, smla_status_str.
 """
 from __future__ import annotations
 
@@ -72,8 +73,12 @@ def _load() -> ctypes.CDLL:
     lib.smla_plan_nsplit_dense.restype = i32
     lib.smla_combine.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp]
     lib.smla_combine.restype = i32
-    lib.smla_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp]
+    lib.smla_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, sz, vp]
     lib.smla_topk.restype = i32
+    lib.smla_topk_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.smla_topk_workspace_bytes.restype = sz
+    lib.smla_set_topk_min_chunks.argtypes = [i32]
+    lib.smla_set_topk_min_chunks.restype = i32
     lib.smla_status_str.argtypes = [i32]
     lib.smla_status_str.restype = ctypes.c_char_p
     return lib
@@ -328,11 +333,26 @@ def smla_combine(part_o: torch.Tensor, part_lse: torch.Tensor, out: torch.Tensor
         raise SmlaError(rc, "smla_combine")
 
 
-def smla_topk(scores: torch.Tensor, topk: int, out_pos: torch.Tensor, ctx_len=None, stream=None) -> None:
+def smla_topk_workspace_bytes(batch: int, q_len: int, max_ctx: int) -> int:
+    return int(_lib_handle().smla_topk_workspace_bytes(batch, q_len, max_ctx))
+
+
+def smla_set_topk_min_chunks(min_chunks: int) -> int:
+    """Chunk count from which smla_topk spreads a row over several workgroups
+    (0 = never); returns the previous value."""
+    r = _lib_handle().smla_set_topk_min_chunks(min_chunks)
+    if r < 0:
+        raise SmlaError(r, "smla_set_topk_min_chunks")
+    return r
+
+
+def smla_topk(scores: torch.Tensor, topk: int, out_pos: torch.Tensor, ctx_len=None, stream=None,
+              workspace_t="auto") -> None:
     """Top-k producer: out_pos [B, Lq, topk] int32 = the positions of the topk
     largest of scores [B, Lq, max_ctx] fp32 among positions < ctx_len[b]
     (all when ctx_len is None), ascending, -1 padded (ranking as in
-    include/smla.h)."""
+    include/smla.h).  workspace_t: "auto" allocates the multi-workgroup
+    form's workspace, None runs one workgroup per row, or a uint8 tensor."""
     if scores.dtype != torch.float32 or not scores.is_contiguous() or scores.dim() != 3:
         raise ValueError("scores must be a contiguous float32 [batch, q_len, max_ctx] tensor")
     b, lq, max_ctx = scores.shape
@@ -341,7 +361,12 @@ def smla_topk(scores: torch.Tensor, topk: int, out_pos: torch.Tensor, ctx_len=No
     if ctx_len is not None and (ctx_len.dtype != torch.int32 or tuple(ctx_len.shape) != (b,)
                                 or not ctx_len.is_contiguous()):
         raise ValueError("ctx_len must be a contiguous int32 [batch] tensor")
+    ws = workspace_t
+    if isinstance(ws, str):
+        n = smla_topk_workspace_bytes(b, lq, max_ctx)
+        ws = torch.empty(n, dtype=torch.uint8, device=scores.device) if n else None
+    ws_bytes = 0 if ws is None else ws.numel() * ws.element_size()
     rc = _lib_handle().smla_topk(_ptr(scores), _ptr(ctx_len), b, lq, max_ctx, int(topk), _ptr(out_pos),
-                                 _stream(stream))
+                                 _ptr(ws), ws_bytes, _stream(stream))
     if rc != 0:
         raise SmlaError(rc, "smla_topk")

@@ -354,15 +354,37 @@ SMLA_API int smla_combine(const float* part_o, const float* part_lse, void* out,
   return SMLA_OK;
 }
 
+// the multi-workgroup top-k form pays for its four launches when the rows
+// alone leave CUs idle and rows are long (measured: 1 x 65536 and 128 rows
+// up to 131072 gain, 64 x 32768 loses)
+constexpr int kTopkMultiMinChunks = 12;  // 45057 positions and more
+std::atomic<int> g_topk_min_chunks{kTopkMultiMinChunks};
+bool topk_multi(int64_t rows, int max_ctx, int cus) {
+  const int m = g_topk_min_chunks.load(std::memory_order_relaxed);
+  return m > 0 && rows < 2 * (int64_t)cus && smla::topk_chunks(max_ctx) >= m;
+}
+
+SMLA_API int smla_set_topk_min_chunks(int min_chunks) {
+  if (min_chunks < 0) return SMLA_ERR_DIM;
+  return g_topk_min_chunks.exchange(min_chunks, std::memory_order_relaxed);
+}
+
+SMLA_API size_t smla_topk_workspace_bytes(int batch, int q_len, int max_ctx) {
+  if (batch < 0 || q_len < 0 || max_ctx < 0) return 0;
+  return (size_t)batch * q_len * smla::topk_ws_row_bytes(max_ctx);
+}
+
 SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, int q_len,
-                       int max_ctx, int topk, int32_t* out_pos, void* hip_stream) {
+                       int max_ctx, int topk, int32_t* out_pos, void* workspace,
+                       size_t workspace_bytes, void* hip_stream) {
   if (batch < 0 || q_len < 0 || max_ctx < 0 || topk < 0 || topk > SMLA_MAX_TOPK)
     return SMLA_ERR_DIM;
   const int64_t rows = (int64_t)batch * q_len;
   if (rows == 0 || topk == 0) return SMLA_OK;
   if (rows > 0x7fffffffLL) return SMLA_ERR_DIM;
   if (!out_pos || (max_ctx > 0 && !scores)) return SMLA_ERR_NULL;
-  if (!aligned(scores, 4) || !aligned(ctx_len, 4) || !aligned(out_pos, 4)) return SMLA_ERR_ALIGN;
+  if (!aligned(scores, 4) || !aligned(ctx_len, 4) || !aligned(out_pos, 4) || !aligned(workspace, 256))
+    return SMLA_ERR_ALIGN;
   smla::TopkParams tp;
   tp.scores = scores;
   tp.ctx = ctx_len;
@@ -371,6 +393,16 @@ SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, i
   tp.q_len = q_len;
   tp.max_ctx = max_ctx;
   tp.topk = topk;
+  tp.ws = nullptr;
+  tp.ws_row_bytes = smla::topk_ws_row_bytes(max_ctx);
+  tp.chunks = smla::topk_chunks(max_ctx);
+  if (workspace && workspace_bytes >= (size_t)rows * tp.ws_row_bytes &&
+      rows * tp.chunks <= 0x7fffffffLL) {
+    int cus = 0;
+    const int rc = device_cus(&cus);
+    if (rc != SMLA_OK) return rc;
+    if (topk_multi(rows, max_ctx, cus)) tp.ws = workspace;
+  }
   if (smla::launch_topk(tp, (hipStream_t)hip_stream) != hipSuccess) {
     (void)hipGetLastError();
     return SMLA_ERR_LAUNCH;

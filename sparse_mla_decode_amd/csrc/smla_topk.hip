@@ -47,9 +47,11 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Exclusive prefix sum of one value per thread over the workgroup; *total
-// receives the sum.  sw: kTopkWaves + 1 words of LDS.
+// Exclusive prefix sum of one value per thread over a workgroup of NT
+// threads; *total receives the sum.  sw: NT / 64 + 1 words of LDS.
+template <int NT = kTopkThreads>
 __device__ __forceinline__ uint32_t scan_excl(uint32_t v, uint32_t* sw, uint32_t* total) {
+  constexpr int kW = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t inc = v;
 #pragma unroll
@@ -60,19 +62,19 @@ __device__ __forceinline__ uint32_t scan_excl(uint32_t v, uint32_t* sw, uint32_t
   if (lane == 63) sw[w] = inc;
   __syncthreads();
   if (w == 0) {
-    const uint32_t t = lane < kTopkWaves ? sw[lane] : 0u;
+    const uint32_t t = lane < kW ? sw[lane] : 0u;
     uint32_t ti = t;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
       const uint32_t y = __shfl_up(ti, d, 64);
       if (lane >= d) ti += y;
     }
-    if (lane < kTopkWaves) sw[lane] = ti - t;
-    if (lane == kTopkWaves - 1) sw[kTopkWaves] = ti;
+    if (lane < kW) sw[lane] = ti - t;
+    if (lane == kW - 1) sw[kW] = ti;
   }
   __syncthreads();
   const uint32_t r = sw[w] + inc - v;
-  *total = sw[kTopkWaves];
+  *total = sw[kW];
   __syncthreads();  // sw is reused by the next call
   return r;
 }
@@ -163,28 +165,40 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
   __syncthreads();
 }
 
-// V4: every row starts 16-byte aligned (16-byte loads).
-template <bool V4>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-  __shared__ uint32_t hist[kBins];
-  __shared__ uint32_t sw[kTopkWaves + 1];
-  __shared__ uint32_t sel[2];  // the digit found, the count of keys above it
-  __shared__ uint32_t ncand;
-  __shared__ uint32_t cand[kCandCap];  // keys of the first digit's bin
+// LDS of a row's selection (one workgroup of kTopkThreads).
+struct TopkSmem {
+  uint32_t hist[kBins];
+  uint32_t sw[kTopkWaves + 1];
+  uint32_t sel[2];  // the digit found, the count of keys above it
+  uint32_t ncand;
+  uint32_t cand[kCandCap];  // keys (of the first digit's bin, or the row's candidates)
+  int32_t cpos[kCandCap];   // positions of the row's candidates (select kernel)
+};
 
+__device__ __forceinline__ int row_len(const TopkParams& p, int64_t row) {
+  int n = p.max_ctx;
+  if (p.ctx) n = min(max(p.ctx[(int)(row / p.q_len)], 0), p.max_ctx);
+  return n;
+}
+
+// every valid position of a row with n <= topk, then -1
+__device__ __forceinline__ void take_all(const TopkParams& p, int64_t row, int n) {
+  int32_t* out = p.out + row * p.topk;
+  for (int i = threadIdx.x; i < p.topk; i += blockDim.x) out[i] = i < n ? i : -1;
+}
+
+// The whole selection of one row (n > topk) by one workgroup.  V4: the row
+// starts 16-byte aligned (16-byte loads).
+template <bool V4>
+__device__ void topk_row(const TopkParams& p, int64_t row, int n, TopkSmem& sm) {
+  uint32_t* hist = sm.hist;
+  uint32_t* sw = sm.sw;
+  uint32_t* sel = sm.sel;
+  uint32_t& ncand = sm.ncand;
+  uint32_t* cand = sm.cand;
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
-  const int b = (int)(row / p.q_len);
   const float* sc = p.scores + row * p.max_ctx;
   int32_t* out = p.out + row * p.topk;
-  int n = p.max_ctx;
-  if (p.ctx) n = min(max(p.ctx[b], 0), p.max_ctx);
-  if (p.topk <= 0) return;
-
-  if (n <= p.topk) {  // every valid position, then -1
-    for (int i = tid; i < p.topk; i += kTopkThreads) out[i] = i < n ? i : -1;
-    return;
-  }
 
   // ---- first digit (bits 21..31) over the whole row
   for (int i = tid; i < kBins; i += kTopkThreads) hist[i] = 0;
@@ -317,15 +331,306 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   }
 }
 
+template <bool V4>
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+  __shared__ TopkSmem sm;
+  if (p.topk <= 0) return;
+  const int64_t row = blockIdx.x;
+  const int n = row_len(p, row);
+  if (n <= p.topk)
+    take_all(p, row, n);
+  else
+    topk_row<V4>(p, row, n, sm);
+}
+
+// ---------------------------------------------------------------------------
+// Multi-workgroup form for few long rows (one workgroup per row would leave
+// most CUs idle).  Four launches, each row cut into chunks of kChunk
+// positions; no atomics in device memory, no waits between workgroups:
+//   1. topk_hist_kernel (row x chunk): the chunk's first-digit histogram,
+//      all 2048 bins written to the workspace;
+//   2. topk_scan_kernel (row): the row's histogram (sum over its chunks), the
+//      first digit b1 and the count above it; for every chunk, its count of
+//      keys with digit >= b1 and the exclusive prefix of those counts (its
+//      offset in the row's candidate list); the total;
+//   3. topk_cand_kernel (row x chunk): the chunk's keys with digit >= b1,
+//      with their positions, written in position order from its offset, so
+//      the row's candidate list is in ascending position order;
+//   4. topk_select_kernel (row): the candidates into LDS, the last two digits
+//      among those with digit b1, then the ordered selection over the
+//      candidates (no sort needed).  A row with more candidates than LDS
+//      holds takes the one-workgroup path (topk_row) instead.
+// ---------------------------------------------------------------------------
+constexpr int kChunkThreads = 256;
+constexpr int kChunk = kChunkThreads * kPer;  // 4096 positions per chunk workgroup
+
+enum : uint32_t { kMetaTrivial = 1u, kMetaFallback = 2u };
+
+struct TopkWs {  // a row's slice of the workspace
+  uint32_t* hist;  // [chunks][kBins]
+  uint32_t* off;   // [chunks + 1] candidate offsets, then the total
+  uint32_t* meta;  // [4]: flags, b1, need after the first digit, total
+  uint2* cand;     // [kCandCap] (key, position)
+};
+__device__ __forceinline__ TopkWs row_ws(const TopkParams& p, int64_t row) {
+  uint8_t* base = (uint8_t*)p.ws + row * p.ws_row_bytes;
+  TopkWs w;
+  w.cand = (uint2*)base;
+  w.hist = (uint32_t*)(base + kCandCap * sizeof(uint2));
+  w.off = w.hist + (size_t)p.chunks * kBins;
+  w.meta = w.off + p.chunks + 1;
+  return w;
+}
+
+// the keys of a chunk, thread t holding positions c0 + 16 t .. + 15
+template <bool V4>
+__device__ __forceinline__ void load_chunk(const float* sc, int p0, int n, uint32_t (&k)[kPer],
+                                           uint32_t& valid) {
+  float v[kPer];
+  if (V4 && p0 + kPer <= n) {
+#pragma unroll
+    for (int g = 0; g < kPer / 4; ++g) {
+      const float4 x = *(const float4*)(sc + p0 + 4 * g);
+      v[4 * g] = x.x;
+      v[4 * g + 1] = x.y;
+      v[4 * g + 2] = x.z;
+      v[4 * g + 3] = x.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) v[e] = p0 + e < n ? sc[p0 + e] : 0.f;
+  }
+  valid = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    k[e] = score_key(v[e]);
+    valid |= (uint32_t)(p0 + e < n) << e;
+  }
+}
+
+template <bool V4>
+__global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(TopkParams p) {
+  __shared__ uint32_t hist[kBins];
+  const int64_t row = blockIdx.x / p.chunks;
+  const int c = blockIdx.x % p.chunks;
+  const int n = row_len(p, row);
+  if (n <= p.topk || c * kChunk >= n) return;  // trivial row, or past its end
+  const TopkWs w = row_ws(p, row);
+  for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
+  __syncthreads();
+  uint32_t k[kPer], valid;
+  load_chunk<V4>(p.scores + row * p.max_ctx, c * kChunk + kPer * threadIdx.x, n, k, valid);
+#pragma unroll
+  for (int e = 0; e < kPer; ++e)
+    if (valid >> e & 1) atomicAdd(&hist[k[e] >> 21], 1u);
+  __syncthreads();
+  uint32_t* dst = w.hist + (size_t)c * kBins;
+  for (int i = threadIdx.x; i < kBins; i += kChunkThreads) dst[i] = hist[i];
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_scan_kernel(TopkParams p) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sw[kTopkWaves + 1];
+  __shared__ uint32_t sel[2];
+  __shared__ uint32_t cnt[kTopkThreads];  // per chunk (a loop covers more chunks)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t row = blockIdx.x;
+  const int n = row_len(p, row);
+  const TopkWs w = row_ws(p, row);
+  if (n <= p.topk) {
+    if (tid == 0) w.meta[0] = kMetaTrivial;
+    return;
+  }
+  const int nch = (n + kChunk - 1) / kChunk;
+  // (loads are issued 16 at a time: a loop of dependent sums would cost one
+  // memory round trip per chunk)
+  for (int i = tid; i < kBins; i += kTopkThreads) {
+    uint32_t t = 0;
+    for (int c0 = 0; c0 < nch; c0 += 16) {
+      uint32_t v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = c0 + u < nch ? w.hist[(size_t)(c0 + u) * kBins + i] : 0u;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) t += v[u];
+    }
+    hist[i] = t;
+  }
+  __syncthreads();
+  find_digit(hist, (uint32_t)p.topk, sw, sel);
+  const uint32_t b1 = sel[0], need = (uint32_t)p.topk - sel[1];
+  // chunk c's keys with digit >= b1: wave (c % 16) sums bins b1 .. 2047
+  uint32_t run = 0;  // offsets so far (thread 0 only)
+  for (int c0 = 0; c0 < nch; c0 += kTopkThreads) {
+    for (int c = c0 + wave; c < min(nch, c0 + kTopkThreads); c += kTopkWaves) {
+      uint32_t t = 0;
+      const uint32_t* hc = w.hist + (size_t)c * kBins;
+      for (int i0 = (int)b1 + lane; i0 < kBins; i0 += 64 * 8) {
+        uint32_t v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = i0 + 64 * u < kBins ? hc[i0 + 64 * u] : 0u;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t += v[u];
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d, 64);
+      if (lane == 0) cnt[c - c0] = t;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      for (int c = c0; c < min(nch, c0 + kTopkThreads); ++c) {
+        w.off[c] = run;
+        run += cnt[c - c0];
+      }
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    w.off[nch] = run;
+    w.meta[0] = run > (uint32_t)kCandCap ? kMetaFallback : 0u;
+    w.meta[1] = b1;
+    w.meta[2] = need;
+    w.meta[3] = run;
+  }
+}
+
+template <bool V4>
+__global__ __launch_bounds__(kChunkThreads) void topk_cand_kernel(TopkParams p) {
+  __shared__ uint32_t sw[kChunkThreads / 64 + 1];
+  const int64_t row = blockIdx.x / p.chunks;
+  const int c = blockIdx.x % p.chunks;
+  const int n = row_len(p, row);
+  if (n <= p.topk || c * kChunk >= n) return;
+  const TopkWs w = row_ws(p, row);
+  const int p0 = c * kChunk + kPer * threadIdx.x;
+  uint32_t k[kPer], valid;
+  load_chunk<V4>(p.scores + row * p.max_ctx, p0, n, k, valid);  // in flight with the reads below
+  const uint32_t flags = w.meta[0], b1 = w.meta[1], off = w.off[c];
+  if (flags != 0u) return;  // trivial or fallback row
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) m |= (uint32_t)((valid >> e & 1) && (k[e] >> 21) >= b1) << e;
+  uint32_t tot;
+  uint32_t o = off + scan_excl<kChunkThreads>((uint32_t)__builtin_popcount(m), sw, &tot);
+  if (m) {
+#pragma unroll
+    for (int e = 0; e < kPer; ++e)
+      if (m >> e & 1) w.cand[o++] = make_uint2(k[e], (uint32_t)(p0 + e));
+  }
+}
+
+template <bool V4>
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p) {
+  __shared__ TopkSmem sm;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int n = row_len(p, row);
+  if (n <= p.topk) {
+    take_all(p, row, n);
+    return;
+  }
+  const TopkWs w = row_ws(p, row);
+  if (w.meta[0] == kMetaFallback) {
+    topk_row<V4>(p, row, n, sm);
+    return;
+  }
+  const uint32_t b1 = w.meta[1], total = w.meta[3];
+  uint32_t need = w.meta[2];
+  {
+    constexpr int kL = kCandCap / kTopkThreads;  // all loads in flight at once
+    uint2 e[kL];
+#pragma unroll
+    for (int u = 0; u < kL; ++u) {
+      const uint32_t i = tid + u * kTopkThreads;
+      e[u] = i < total ? w.cand[i] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < kL; ++u) {
+      const uint32_t i = tid + u * kTopkThreads;
+      if (i < total) {
+        sm.cand[i] = e[u].x;
+        sm.cpos[i] = (int32_t)e[u].y;
+      }
+    }
+  }
+  // the last two digits among the candidates with first digit b1
+  uint32_t prefix = b1;
+#pragma unroll 1
+  for (int level = 1; level < 3; ++level) {
+    const int sh = level == 1 ? 10 : 0;
+    const int width = level == 1 ? 11 : 10;
+    const int hsh = sh + width;
+    const uint32_t mask = (1u << width) - 1;
+    for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+    __syncthreads();
+    for (uint32_t i = tid; i < total; i += kTopkThreads) {
+      const uint32_t k = sm.cand[i];
+      if ((k >> hsh) == prefix) atomicAdd(&sm.hist[(k >> sh) & mask], 1u);
+    }
+    __syncthreads();
+    find_digit(sm.hist, need, sm.sw, sm.sel);
+    prefix = (prefix << width) | sm.sel[0];
+    need -= sm.sel[1];
+    __syncthreads();
+  }
+  const uint32_t T = prefix;
+  // ordered selection over the candidates (ascending positions): thread t
+  // holds candidates 16 t .. 16 t + 15 (total <= kCandCap <= 16 * threads)
+  static_assert(kCandCap <= kPer * kTopkThreads, "one tile of candidates");
+  const int i0 = kPer * tid;
+  uint32_t gtm = 0, eqm = 0;
+#pragma unroll
+  for (int e = 0; e < kPer; ++e) {
+    const bool ok = (uint32_t)(i0 + e) < total;
+    const uint32_t k = ok ? sm.cand[i0 + e] : 0u;
+    gtm |= (uint32_t)(ok && k > T) << e;
+    eqm |= (uint32_t)(ok && k == T) << e;
+  }
+  uint32_t tot;
+  const uint32_t ex = scan_excl((uint32_t)__builtin_popcount(gtm) | ((uint32_t)__builtin_popcount(eqm) << 16),
+                                sm.sw, &tot);
+  int32_t* out = p.out + row * p.topk;
+  if (gtm | eqm) {
+    const uint32_t gt_ex = ex & 0xffffu, eq_ex = ex >> 16;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) {
+      const uint32_t below = (1u << e) - 1;
+      const uint32_t gt_before = gt_ex + (uint32_t)__builtin_popcount(gtm & below);
+      const uint32_t eq_before = eq_ex + (uint32_t)__builtin_popcount(eqm & below);
+      if ((gtm >> e & 1) || ((eqm >> e & 1) && eq_before < need)) {
+        const uint32_t slot = gt_before + min(eq_before, need);
+        if (slot < (uint32_t)p.topk) out[slot] = sm.cpos[i0 + e];
+      }
+    }
+  }
+}
+
 }  // namespace
+
+size_t topk_ws_row_bytes(int max_ctx) {
+  const size_t chunks = ((size_t)max_ctx + kChunk - 1) / kChunk;
+  const size_t b = kCandCap * sizeof(uint2) + (chunks * kBins + chunks + 1 + 4) * sizeof(uint32_t);
+  return (b + 255) / 256 * 256;
+}
+
+int topk_chunks(int max_ctx) { return (max_ctx + kChunk - 1) / kChunk; }
+
+template <bool V4>
+static hipError_t launch_topk_t(const TopkParams& p, hipStream_t st) {
+  if (!p.ws) {
+    hipLaunchKernelGGL(topk_kernel<V4>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st, p);
+    return hipGetLastError();
+  }
+  const unsigned rc = (unsigned)(p.rows * p.chunks);
+  hipLaunchKernelGGL(topk_hist_kernel<V4>, dim3(rc), dim3(kChunkThreads), 0, st, p);
+  hipLaunchKernelGGL(topk_scan_kernel, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st, p);
+  hipLaunchKernelGGL(topk_cand_kernel<V4>, dim3(rc), dim3(kChunkThreads), 0, st, p);
+  hipLaunchKernelGGL(topk_select_kernel<V4>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st) {
   const bool v4 = ((uintptr_t)p.scores & 15) == 0 && p.max_ctx % 4 == 0;
-  if (v4)
-    hipLaunchKernelGGL(topk_kernel<true>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st, p);
-  else
-    hipLaunchKernelGGL(topk_kernel<false>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st, p);
-  return hipGetLastError();
+  return v4 ? launch_topk_t<true>(p, st) : launch_topk_t<false>(p, st);
 }
 
 }  // namespace smla

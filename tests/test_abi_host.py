@@ -37,7 +37,9 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["smla_plan_nsplit", "smla_plan_nsplit_cus", "smla_workspace_bytes",
                             "smla_workspace_lse_offset", "smla_fused_in_launch", "smla_set_merge_polls",
-                            "smla_decode", "smla_decode_fused", "smla_topk", "smla_decode_paged",
+                            "smla_decode", "smla_decode_fused", "smla_topk", "smla_topk_workspace_bytes",
+                            "smla_set_topk_min_chunks",
+                            "smla_decode_paged",
                             "smla_decode_dense", "smla_plan_nsplit_dense", "smla_split",
                             "smla_combine", "smla_status_str"]), names
 
@@ -299,14 +301,33 @@ def test_topk_arguments(smla):
     f = smla.lib.smla_topk
     vp = ctypes.c_void_p
     sc, ctx, out = vp(0x10000), vp(0x20000), vp(0x30000)
-    assert f(sc, ctx, -1, 1, 100, 8, out, None) == -2
-    assert f(sc, ctx, 1, -1, 100, 8, out, None) == -2
-    assert f(sc, ctx, 1, 1, -5, 8, out, None) == -2
-    assert f(sc, ctx, 1, 1, 100, -1, out, None) == -2
-    assert f(sc, ctx, 1, 1, 100, (1 << 24) + 1, out, None) == -2
-    assert f(sc, ctx, 1, 1, 100, 8, None, None) == -1
-    assert f(None, ctx, 1, 1, 100, 8, out, None) == -1
-    assert f(vp(0x10002), ctx, 1, 1, 100, 8, out, None) == -5
-    assert f(sc, ctx, 1, 1, 100, 8, vp(0x30001), None) == -5
-    assert f(sc, ctx, 0, 1, 100, 8, out, None) == 0   # no rows
-    assert f(sc, ctx, 1, 1, 100, 0, out, None) == 0   # topk 0
+    assert f(sc, ctx, -1, 1, 100, 8, out, None, 0, None) == -2
+    assert f(sc, ctx, 1, -1, 100, 8, out, None, 0, None) == -2
+    assert f(sc, ctx, 1, 1, -5, 8, out, None, 0, None) == -2
+    assert f(sc, ctx, 1, 1, 100, -1, out, None, 0, None) == -2
+    assert f(sc, ctx, 1, 1, 100, (1 << 24) + 1, out, None, 0, None) == -2
+    assert f(sc, ctx, 1, 1, 100, 8, None, None, 0, None) == -1
+    assert f(None, ctx, 1, 1, 100, 8, out, None, 0, None) == -1
+    assert f(vp(0x10002), ctx, 1, 1, 100, 8, out, None, 0, None) == -5
+    assert f(sc, ctx, 1, 1, 100, 8, vp(0x30001), None, 0, None) == -5
+    assert f(sc, ctx, 1, 1, 100, 8, out, vp(0x40010), 1 << 20, None) == -5  # workspace 256-aligned
+    assert f(sc, ctx, 0, 1, 100, 8, out, None, 0, None) == 0   # no rows
+    assert f(sc, ctx, 1, 1, 100, 0, out, None, 0, None) == 0   # topk 0
+
+
+def test_topk_workspace_size(smla):
+    """Per row: the candidate list (8192 x 8 B), 2048 bins per 4096-position
+    chunk, chunk offsets and 4 words, rounded up to 256 B."""
+    f = smla.lib.smla_topk_workspace_bytes
+    for m in (0, 1, 4096, 4097, 65536, 131072):
+        ch = -(-m // 4096)
+        row = 8192 * 8 + (ch * 2048 + ch + 1 + 4) * 4
+        assert f(3, 2, m) == 6 * (-(-row // 256) * 256), m
+    assert f(-1, 1, 10) == 0
+
+
+def test_topk_min_chunks_setting(smla):
+    prev = smla.lib.smla_set_topk_min_chunks(3)
+    assert prev >= 0
+    assert smla.lib.smla_set_topk_min_chunks(prev) == 3
+    assert smla.lib.smla_set_topk_min_chunks(-1) == -2

@@ -99,9 +99,9 @@ int smla_plan_nsplit(int batch, int q_len, int heads, int topk);
 /*
  * The same planner as a pure function of the CU count: no device access, so
  * it runs (and is tested) on hosts without a GPU.  The rule: the largest
- * NSPLIT whose workgroups (batch * q_len * head blocks * NSPLIT) all fit on
- * the device at once, two per CU, with at least one 32-row tile per split;
- * then the fewest splits that keep the same number of tiles per split.  It
+ * NSPLIT whose workgroups (batch * q_len * head blocks * NSPLIT) get one CU
+ * each, with at least one 32-row tile per split; then the fewest splits
+ * that keep the same number of tiles per split.  It
  * fills every CU at batch 1 and drops to NSPLIT 1 once the batch alone
  * fills the device ("The Occupancy Hypothesis", "The Occupancy Insight":
  * blocks in flight, not per-block work, hide memory latency; "The Split-K

@@ -213,11 +213,13 @@ SMLA_API int smla_plan_nsplit_cus(int cus, int batch, int q_len, int heads, int 
   const int64_t units = tokens * ((heads + hpb - 1) / hpb);  // workgroups per split
   // A split workgroup costs a fixed start-up (list, q, first gather) plus one
   // step per 32-row tile, and at small batch the whole call is one such
-  // latency chain.  So: the most splits whose workgroups are all resident at
-  // once (one wave of workgroups over the device), each split at least one
-  // whole tile ...
+  // latency chain.  So: the most splits whose workgroups get a CU each (one
+  // workgroup per CU: where LDS would fit two, the second on a CU ran no
+  // faster than one more tile per workgroup, and more splits cost the combine
+  // more; measured on 9 tokens x 8 heads: 22 splits of 3 tiles 13.3 us per
+  // step, 32 of 2 tiles 14.5 us), each split at least one whole tile ...
   constexpr int kTile = smla::kTileRows;
-  const int64_t slots = (int64_t)cus * smla::split_blocks_per_cu(heads);
+  const int64_t slots = cus;
   int64_t ns = slots / units;
   const int64_t max_ns = topk / kTile;
   if (ns > max_ns) ns = max_ns;

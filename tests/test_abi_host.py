@@ -79,12 +79,6 @@ def _hpb(h):
     return 16 if h <= 16 else 32 if h <= 32 else 64
 
 
-def _blocks_per_cu(h):
-    # up to 32 heads: two tile buffers, two workgroups per CU; 64-head
-    # blocks: four tile buffers, one workgroup per CU
-    return 2 if h <= 32 else 1
-
-
 def _tiles(k, ns):
     return -(-(-(-k // ns)) // TILE)
 
@@ -100,7 +94,7 @@ def test_planner_bounds(smla, cus, shape):
     assert ns == 1 or per >= TILE                # a split holds at least one tile
     assert -(-k // per) == ns                    # no trailing empty split
     units = b * lq * -(-h // _hpb(h))            # workgroups per split
-    slots = _blocks_per_cu(h) * cus
+    slots = cus                                  # one workgroup per CU
     assert ns == 1 or units * ns <= slots        # one wave of workgroups
     # no NSPLIT that still fits in one wave needs fewer tiles per split ...
     best = max(1, min(slots // units, k // TILE))
@@ -112,8 +106,8 @@ def test_planner_bounds(smla, cus, shape):
 def test_planner_fills_small_batches(smla):
     # batch 1, one head group: one 32-row tile per split
     assert smla.smla_plan_nsplit_cus(256, 1, 1, 8, 2048) == 64
-    # 9 query tokens: 56 splits would fit, but 2 tiles each already needs only 32
-    assert smla.smla_plan_nsplit_cus(256, 1, 9, 8, 2048) == 32
+    # 9 query tokens: 28 splits would fit, but 3 tiles each already needs only 22
+    assert smla.smla_plan_nsplit_cus(256, 1, 9, 8, 2048) == 22
     # batch 64 x 64 heads: 64 workgroups per split, 4 splits fill 256 slots
     assert smla.smla_plan_nsplit_cus(256, 64, 1, 64, 2048) == 4
     # batch 128 x 128 heads: 256 workgroups per split already fill the device

@@ -28,7 +28,9 @@ Timing protocol
     graph-timed, with the score bytes it must read per call against the
     HBM roofline (skipped with --no-sweep);
   * cpu_baseline: the fp64 oracle, as is, on the host cores, over a bounded
-    sample of the same workload, scaled to steps/s;
+    sample of the same workload, scaled to steps/s (and on one core);
+  * dispatch_floor_us: a graph of back-to-back empty kernel launches, the
+    per-launch floor under every step (two launches per step);
   * nsplit_sweep: steps/s and the split kernel's gathered-KV rate of the same
     workload at each NSPLIT of its sweep (the planner's marked), and, beside
     a batch-1 workload, the same figures for the batch-64 workload at the
@@ -500,6 +502,7 @@ def main():
                  "frac": round(flops / (split_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
         "kernel_sha": kernel_sha(),
     }
+    result["dispatch_floor_us"] = round(dispatch_floor_us(), 3)
     if single_launch:
         result["single_launch"] = single_launch
     if topk:
@@ -511,6 +514,30 @@ def main():
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w.inp, w.caches[0], torch.from_numpy(w.sets[0]), args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+def dispatch_floor_us(n=256):
+    """Microseconds per launch of an empty kernel, back to back in a graph."""
+    import torch
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(n):
+                torch.cuda._sleep(0)
+    torch.cuda.synchronize()
+    for _ in range(20):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(10):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return 1e3 * a.elapsed_time(b) / (10 * n)
 
 
 def cpu_baseline(inp, kv_dev, idx0, seconds):
@@ -539,10 +566,20 @@ def cpu_baseline(inp, kv_dev, idx0, seconds):
         done_seqs += 1
         b += 1
     steps_per_s = (done_seqs / T_seq) / elapsed
+    # the same on one core, over a quarter of the time budget
+    q_s, kv_s, idx_s = wl.oracle_view(inp0, kv_dev, [0])
+    one, t1 = 0, 0.0
+    while t1 < seconds / 4:
+        t0 = time.perf_counter()
+        oracle.decode(q_s, kv_s, idx_s, inp.scale, nthreads=1)
+        t1 += time.perf_counter() - t0
+        one += 1
     return {"value": round(steps_per_s, 4), "unit": "steps/s", "cores": used, "kind": "oracle",
             "sample": f"{done_seqs} sequence(s) x {inp.q_len} token(s) x {inp.heads} heads of the first "
                       f"index set in {elapsed:.1f} s of fp64 oracle work, scaled to the {T_seq}-sequence step",
-            "host_threads_available": threads}
+            "host_threads_available": threads,
+            "single_core": {"value": round((one / T_seq) / t1, 4), "unit": "steps/s", "cores": 1,
+                            "sample": f"sequence 0 {one} times in {t1:.1f} s, scaled to the step"}}
 
 
 if __name__ == "__main__":

@@ -126,10 +126,10 @@ int smla_fused_in_launch(int batch, int q_len, int heads, int nsplit);
 /*
  * Bound on the polls (each a short sleep and one device-scope load) of a
  * workgroup that waits for the other partials of its unit in the
- * single-launch merge of smla_decode_fused; default 2048.  0 = never wait: the last workgroup to
- * arrive merges the whole unit (same results, bit for bit).  Process-wide;
- * applies to calls made after it.  Returns the previous value, or
- * SMLA_ERR_DIM if polls < 0.
+ * single-launch merge of smla_decode_fused; default 2048.  0 = never wait:
+ * the last workgroup to arrive merges the whole unit (same results, bit for
+ * bit).  Process-wide; applies to calls made after it.  Returns the previous
+ * value, or SMLA_ERR_DIM if polls < 0.
  */
 int smla_set_merge_polls(int polls);
 

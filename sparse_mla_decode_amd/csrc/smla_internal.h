@@ -22,7 +22,7 @@ constexpr int kTileRows = 32;
 constexpr int kListCap = 2048;
 // ... per configuration: the K-split workgroup whose 4 waves share one head
 // group (column quarters) stages half as many, so that two fit a CU's LDS
-constexpr int split_list_cap(int ncs, bool ksplit) { return ksplit && ncs == 4 ? 1024 : kListCap; }
+constexpr int split_list_cap(int ncs, int ks) { return ks == 2 && ncs == 4 ? 1024 : kListCap; }
 
 // Where the rows of a token's list come from.
 enum RowSource : int {

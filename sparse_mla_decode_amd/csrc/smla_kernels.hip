@@ -24,11 +24,15 @@
 //   * S^T = KV_tile * Q^T on v_mfma_f32_16x16x32_bf16 (rows on M, heads on N)
 //     so that each lane owns one head: the online-softmax max needs two
 //     cross-lane exchanges per tile and the running sum none until the end.
-//     The waves of a 16-head group pair up along K (even / odd K-steps) and
-//     add their halves through LDS (16- and 64-head blocks).
+//     In 16-head blocks the waves of the group pair up along K (even / odd
+//     K-steps) and add their halves through LDS.  In 64-head blocks four
+//     waves share a pair of head groups along K (one K-step residue mod 4
+//     each), reduce-scatter the partial scores through LDS, and each then
+//     owns the softmax of 8 heads; the bf16 weights go back through LDS.
 //   * O^T += V^T * P^T on the same MFMA; the softmax output is already laid
-//     out as the B operand (no shuffles), V^T comes from LDS transpose reads;
-//     the waves of a head group split the 512 value columns.
+//     out as the B operand (no shuffles; in 64-head blocks it is written to
+//     LDS in that layout), V^T comes from LDS transpose reads; the waves of
+//     a head group split the 512 value columns.
 //   * masked entries (-1, out of range, past the slice end) load a static
 //     all-zero row, so their V contribution is exactly zero, and get a score
 //     of -inf.
@@ -79,6 +83,11 @@ __device__ __forceinline__ float sum4_lanes(float x) {
   const unsigned w = __float_as_uint(y);
   const auto b = __builtin_amdgcn_permlane32_swap(w, w, false, false);
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// The value of lane l ^ 8 (DPP row rotate by 8 within each row of 16 lanes).
+__device__ __forceinline__ float ror8_lanes(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));
 }
 
 // Row indices are int32, so a row is valid iff 0 <= r < min(kv_rows, 2^31-1);
@@ -343,15 +352,23 @@ __device__ __forceinline__ void fused_combine(const SplitParams& p, int unit, in
 
 // ---------------------------------------------------------------------------
 // Split kernel.  HG head groups of 16 per workgroup; each wave owns GPW
-// head groups and one of NCS column slices of the 512 value columns.  Every
-// wave holds S for its head groups: it computes all of QK^T, or with KSPLIT
-// the K-steps of one parity, the two parities adding their halves through
-// LDS; the PV work and the O accumulators are divided among the NCS waves
-// that share head groups.  With GPW = 2 a
-// wave feeds every LDS operand read (a K-tile of QK^T, a V^T block of PV) to
-// two MFMAs, one per head group, halving LDS traffic per head; it then needs
-// about 460 registers and runs one wave per SIMD.  TR rows per tile, two
-// tile buffers: one tile is in flight while the other is computed.
+// head groups and one of NCS column slices of the 512 value columns; the PV
+// work and the O accumulators are divided among the NCS waves that share
+// head groups.  KS is the number of waves that share a head group's QK^T
+// along K:
+//   KS = 1: every wave computes all of QK^T for its head groups;
+//   KS = 2: the K-steps of one parity, the two parities adding their halves
+//           through LDS, after which both waves hold all of S;
+//   KS = 4 (GPW = 2, NCS = 4): the four waves of a head pair take the
+//           K-steps of one residue mod 4 each, for both head groups; a
+//           reduce-scatter through LDS leaves each wave the full scores of
+//           8 heads x all tile rows, whose softmax it owns (running max,
+//           sum, rescale factor), and the bf16 weights go back through LDS
+//           as the PV operands of all four.  Each LDS operand read feeds two
+//           MFMAs (one per head group) with no duplicated softmax, at about
+//           200 registers: two waves per SIMD.
+// TR rows per tile, two tile buffers: one tile is in flight while the other
+// is computed.
 // ---------------------------------------------------------------------------
 // The dispatcher hands workgroup i to XCD i % kXcds (round robin over the
 // eight XCDs, each with its own L2).  This renumbering gives every XCD a
@@ -400,12 +417,16 @@ __device__ __forceinline__ void dma_tile(const u32x4* src, uint8_t* lds,
 // Keeps a value in its registers up to this point.
 __device__ __forceinline__ void keep_live(uint64_t v) { asm volatile("" ::"v"(v)); }
 
-template <int HG, int NCS, int GPW, int TR, bool KSPLIT, int SRC>
+template <int HG, int NCS, int GPW, int TR, int KS, int SRC>
 __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
-__attribute__((amdgpu_waves_per_eu(GPW == 1 ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(GPW == 1 || KS == 4 ? 2 : 1)))
 void split_kernel(SplitParams p) {
   static_assert(HG % GPW == 0, "whole head groups per wave");
+  static_assert(KS == 1 || KS == 2 || KS == 4, "K-split factor");
+  constexpr bool KSPLIT = KS == 2;  // K-split pairs
+  constexpr bool KQ = KS == 4;      // K-split quads with the softmax owned per 8 heads
   static_assert(!KSPLIT || NCS % 2 == 0, "K-split pairs waves of opposite parity");
+  static_assert(!KQ || (NCS == 4 && GPW == 2 && TR == 32), "K-split quad shape");
   constexpr int NT = 64 * (HG / GPW) * NCS;
   // waves that issue the tile loads: all of them, or half of them when the
   // tile's wave loads do not split evenly (36 per 32-row tile: not over 8)
@@ -416,13 +437,14 @@ void split_kernel(SplitParams p) {
   constexpr int L = TR * kRowGran / NTD;      // DMA instructions per loading thread per tile
   constexpr int kTileBytes = TR * kRow * 2;
   constexpr int CB = (kDV / 16) / NCS;        // 16-column blocks of O per wave
-  // QK^T K-steps per wave: all 18, or with K-split pairs the 9 of one parity
-  constexpr int KSW = KSPLIT ? kKSteps / 2 : kKSteps;
+  // QK^T K-steps per wave: all 18, with K-split pairs the 9 of one parity,
+  // with quads those of one residue mod 4 (5 or 4)
+  constexpr int KSW = KSPLIT ? kKSteps / 2 : KQ ? (kKSteps + 3) / 4 : kKSteps;
   static_assert(TR * kRowGran % NTD == 0, "tile must split evenly over the loading threads");
   static_assert(TR % 32 == 0, "tile shape");
   // list entries staged at a time (the K-split 16-head workgroup stages
   // 1024 so that two of them fit a CU's LDS)
-  constexpr int LCAP = split_list_cap(NCS, KSPLIT);
+  constexpr int LCAP = split_list_cap(NCS, KS);
   // K-split: one slot of partial scores per (head group, K parity); the
   // waves of a head group with cs < 2 write them, every wave reads the other
   // parity's slot
@@ -435,8 +457,15 @@ void split_kernel(SplitParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
   __shared__ __attribute__((aligned(16))) int list_s[LCAP];
-  // partial S^T per (head group, parity) slot: [slot][gi][rb][lane]
-  __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? kXsSlots * GPW * RB * 64 : 1];
+  // K-split pairs: partial S^T per (head group, parity) slot: [slot][gi][rb][lane];
+  // quads: every wave's partial S^T, [wave][gi][rb][lane ^ 8*rb]
+  __shared__ __attribute__((aligned(16)))
+  floatx4 xs[KSPLIT ? kXsSlots * GPW * RB * 64 : KQ ? (NT / 64) * GPW * RB * 64 : 1];
+  // quads: the bf16 weights P^T as PV B operands, [head pair][gi][g][head][8],
+  // the owners' rescale factors per head, and their final sums and maxima
+  __shared__ __attribute__((aligned(16))) u32x4 ps[KQ ? (HG / GPW) * GPW * 64 : 1];
+  __shared__ float alpha_s[KQ ? HG * 16 : 1];
+  __shared__ float fin_l[KQ ? HG * 16 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -445,6 +474,20 @@ void split_kernel(SplitParams p) {
   const int l16 = lane & 15;  // MFMA row / column within a 16-wide block
   const int hg0 = (wave / NCS) * GPW;  // first head group of this wave
   const int cs = wave % NCS;
+  // K-split quads: head pair hp = wave / NCS; the wave's QK^T K-steps are
+  // those of residue kr = (cs + 2 hp) mod 4 (five for kr < 2, else four, so
+  // the two waves of a SIMD under round-robin placement, cs and cs + 4, get
+  // one of each); it owns the softmax of heads 8a .. 8a + 7 of the pair's
+  // head group go (go = cs / 2, a = cs % 2)
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int hp = wave_u / NCS, cs_u = wave_u % NCS;
+  const int kr = (cs_u + 2 * hp) & 3;
+  const int go = cs_u >> 1, own_a = cs_u & 1;
+  // a quad owner's lane holds head 8a + (l16 & 7) of group go, tile rows
+  // 16 rbl + 4g .. +3: the lanes of the wave's own half (l16 / 8 = a) take
+  // row block 0, the others row block 1
+  const int rbl = (l16 >> 3) != own_a;
+  const int own_j = 8 * own_a + (l16 & 7);
 
   // workgroup -> (token, head block, split), splits fastest, in the XCD-
   // contiguous numbering: a token's head blocks and splits share one XCD, so
@@ -511,9 +554,14 @@ void split_kernel(SplitParams p) {
                             ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + h[gi]) * kRow) + g
                             : g_zero_row + g;
     if (KSPLIT) qrow += 4 * (cs & 1);
+    if (KQ) qrow += 4 * kr;
 #pragma unroll
-    for (int k = 0; k < KSW; ++k)
-      qb[gi][k] = __builtin_bit_cast(bf16x8, qrow[k * 4 * (KSPLIT ? 2 : 1)]);
+    for (int k = 0; k < KSW; ++k) {
+      if (KQ && k == KSW - 1 && kr >= 2)
+        qb[gi][k] = bf16x8{};  // K-step kr + 16 is past the row: never used
+      else
+        qb[gi][k] = __builtin_bit_cast(bf16x8, qrow[k * 4 * (KSPLIT ? 2 : KQ ? 4 : 1)]);
+    }
   }
 
   // QK^T operand: row 16*rb + l16, granule 4*ks + g, i.e. block ks/2 and
@@ -523,6 +571,8 @@ void split_kernel(SplitParams p) {
   const int qk_odd = l16 * 128 + ((g ^ hq) ^ 4) * 16;
   // K-split: K-step 2k + par is block k, in-block half par (par = cs & 1)
   const int qk_half = (cs & 1) ? qk_odd : qk_even;
+  // quads: K-step kr + 4k is block kr / 2 + 2k, in-block half kr & 1
+  const int qk_quad = ((kr & 1) ? qk_odd : qk_even) + (kr >> 1) * TR * 128;
   // V^T transpose read: source lane (e, s') of group g reads row 4g + e
   // (+16 for slots 4-7, +32 per PV K-step), columns 16*cb + 4s' .. +3 =
   // granule 2cb + b0 (b0 = s' >> 1) at byte 8*b1 (b1 = s' & 1); in-block
@@ -565,9 +615,9 @@ void split_kernel(SplitParams p) {
   }
 
   // LDS-DMA loads of tile t (list entries t*TR.. of the staged chunk); a
-  // masked entry or one past the chunk loads the zero row.  The L loads of a lane share one 64-bit address (see
-  // dma_tile), returned so that the caller keeps it live until the loads are
-  // known to be complete.
+  // masked entry or one past the chunk loads the zero row.  The L loads of a
+  // lane share one 64-bit address (see dma_tile), returned so that the caller
+  // keeps it live until the loads are known to be complete.
   static_assert(DP == 1, "one row per lane per tile");
   auto issue = [&](uint8_t* buf, int t) __attribute__((always_inline)) -> uint64_t {
     const int32_t r = list_s[t * TR + dma_row[0]];  // t * TR + TR <= LCAP
@@ -576,6 +626,137 @@ void split_kernel(SplitParams p) {
     if (wave < DW)
       dma_tile<NTD, WPB / RG>(src, buf + wave * 64 * 16, std::make_integer_sequence<int, L>{});
     return (uint64_t)(uintptr_t)src;
+  };
+
+  // Consume tile t held in T, K-split quads.
+  auto compute_quad = [&](const uint8_t* T, int t) __attribute__((always_inline)) {
+    if constexpr (KQ) {
+      // ---- partial S^T = KV_tile * Q^T over the wave's K-steps kr + 4k, for
+      // both head groups of the pair (each operand read feeds two MFMAs)
+      const bool five = kr < 2;  // wave-uniform: a fifth K-step
+      bf16x8 av[KSW][RB];
+#pragma unroll
+      for (int k = 0; k < KSW - 1; ++k)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          av[k][rb] = *(const bf16x8*)(T + qk_quad + 2 * k * TR * 128 + rb * 16 * 128);
+      if (five) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          av[KSW - 1][rb] =
+              *(const bf16x8*)(T + qk_quad + 2 * (KSW - 1) * TR * 128 + rb * 16 * 128);
+      }
+      floatx4 acc[GPW][RB];
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) acc[gi][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KSW - 1; ++k)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int gi = 0; gi < GPW; ++gi)
+            acc[gi][rb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k][rb], qb[gi][k], acc[gi][rb], 0, 0, 0);
+      if (five) {
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+          for (int gi = 0; gi < GPW; ++gi)
+            acc[gi][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[KSW - 1][rb], qb[gi][KSW - 1],
+                                                                  acc[gi][rb], 0, 0, 0);
+      }
+
+      // ---- reduce-scatter through LDS: every wave stores its four blocks
+      // (row block 1 at lane ^ 8, so that each owner lane reads its own
+      // position); the owner adds the pair's other three waves to its own part
+      // (block (go, 0) of this lane, or block (go, 1) of lane ^ 8)
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb)
+          xs[((wave_u * GPW + gi) * RB + rb) * 64 + (lane ^ (8 * rb))] = acc[gi][rb];
+      barrier_lds();
+      const floatx4 own0 = go ? acc[1][0] : acc[0][0];
+      const floatx4 own1 = go ? acc[1][1] : acc[0][1];
+      floatx4 sv;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = ror8_lanes(own1[i]);
+        sv[i] = rbl ? x : own0[i];
+      }
+#pragma unroll
+      for (int c = 1; c < NCS; ++c) {
+        const int src = hp * NCS + ((cs_u + c) & (NCS - 1));
+        sv += xs[((src * GPW + go) * RB + rbl) * 64 + lane];
+      }
+
+      // ---- online softmax of the owned head: 4 rows here, 32 over the 8
+      // lanes l16, l16 ^ 8 of the four lane groups
+      const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rbl + 4 * g);
+      float s4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s4[i] = r4[i] >= 0 ? sv[i] * p.scale_log2 : -__builtin_inff();
+      float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
+      mx = max4_lanes(mx);
+      mx = fmaxf(mx, ror8_lanes(mx));
+      // lazy rescaling as below; the factor goes to every wave holding O of
+      // this head (exactly 1 when the max stays)
+      float alpha = 1.f;
+      if (mx > m_run[0] + kRescaleLog2) {
+        const float m_new = fmaxf(m_run[0], mx);
+        alpha = __builtin_amdgcn_exp2f(m_run[0] - m_new);  // 0 while m_run = -inf
+        l_run[0] *= alpha;
+        m_run[0] = m_new;
+      }
+      const float m_use = m_run[0] == -__builtin_inff() ? 0.f : m_run[0];
+      float pw[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pw[i] = __builtin_amdgcn_exp2f(s4[i] - m_use);
+        l_run[0] += pw[i];
+      }
+      // P^T for PV K slots 4 rbl .. +3 of lane group g, head own_j (the slot
+      // order of the V^T transpose reads below)
+      *(u32x2*)((uint8_t*)ps + (((hp * GPW + go) * 4 + g) * 16 + own_j) * 16 + 8 * rbl) =
+          u32x2{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3])};
+      if (g == 0 && !rbl) alpha_s[hp * GPW * 16 + go * 16 + own_j] = alpha;
+      barrier_lds();
+
+      // ---- O^T += V^T * P^T over this wave's column quarter, both head groups
+      float al[GPW];
+      bool scale = false;
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi) {
+        al[gi] = alpha_s[hp * GPW * 16 + gi * 16 + l16];
+        scale |= al[gi] != 1.f;
+      }
+      if (__any(scale)) {
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi)
+#pragma unroll
+          for (int cb = 0; cb < CB; ++cb) oacc[gi][cb] *= al[gi];
+      }
+      bf16x8 pq[GPW];
+#pragma unroll
+      for (int gi = 0; gi < GPW; ++gi)
+        pq[gi] = __builtin_bit_cast(bf16x8, ps[(hp * GPW + gi) * 64 + g * 16 + l16]);
+      shortx4 vt[CB][2];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int off = pv_base[cb & 3] + (cb >> 2) * TR * 128;
+        vt[cb][0] = lds_tr16(T + off);
+        vt[cb][1] = lds_tr16(T + off + 16 * 128);
+      }
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const bf16x8 a8 = __builtin_bit_cast(bf16x8, vt[cb]);
+#pragma unroll
+        for (int gi = 0; gi < GPW; ++gi)
+          oacc[gi][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, pq[gi], oacc[gi][cb], 0, 0, 0);
+      }
+    }
   };
 
   // Consume tile t held in T.
@@ -783,7 +964,10 @@ void split_kernel(SplitParams p) {
       // refill the other buffer, which every wave finished with in the
       // previous step
       if (n + 1 < ntiles) addr[b ^ 1] = issue(buf(std::integral_constant<int, b ^ 1>{}), n + 1);
-      compute(buf(bconst), n);
+      if constexpr (KQ)
+        compute_quad(buf(bconst), n);
+      else
+        compute(buf(bconst), n);
     };
     for (int n0 = 0; n0 < ntiles; n0 += 2) {
       step(std::integral_constant<int, 0>{}, n0);
@@ -799,13 +983,51 @@ void split_kernel(SplitParams p) {
     }
   }
 
-  // ---- epilogue: O / l and LSE = (m * ln 2) + ln l
+  // ---- epilogue: O / l and LSE = (m * ln 2) + ln l.  Per head group: 1 / l
+  // for this lane's head, and the LSE of head lse_h if this lane writes it
+  float inv[GPW], lse_v[GPW];
+  int lse_h[GPW];
+  bool lse_w[GPW];
+  if constexpr (KQ) {
+    // the owner sums its head over the 8 lanes (x + partner is the same sum
+    // in both lanes) and hands l to the waves holding the head's O
+    float l_tot = sum4_lanes(l_run[0]);
+    l_tot += ror8_lanes(l_tot);
+    const float lse_own =
+        l_tot > 0.f ? m_run[0] * kLn2 + __logf(l_tot) : -__builtin_inff();
+    if (g == 0 && !rbl) fin_l[hp * GPW * 16 + go * 16 + own_j] = l_tot;
+    barrier_lds();
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const float l = fin_l[hp * GPW * 16 + gi * 16 + l16];
+      inv[gi] = l > 0.f ? 1.f / l : 0.f;
+      lse_v[gi] = lse_own;
+      lse_h[gi] = hblk * kHeadsPerBlock + hp * GPW * 16 + go * 16 + own_j;
+      lse_w[gi] = gi == 0 && g == 0 && !rbl;
+    }
+  } else {
+#pragma unroll
+    for (int gi = 0; gi < GPW; ++gi) {
+      const float l_tot = sum4_lanes(l_run[gi]);
+      const bool any = l_tot > 0.f;
+      inv[gi] = any ? 1.f / l_tot : 0.f;
+      lse_v[gi] = any ? m_run[gi] * kLn2 + __logf(l_tot) : -__builtin_inff();
+      lse_h[gi] = h[gi];
+      lse_w[gi] = g == 0 && cs == 0;
+    }
+  }
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
-    const float l_tot = sum4_lanes(l_run[gi]);
-    const bool any = l_tot > 0.f;
-    const float inv = any ? 1.f / l_tot : 0.f;
-    const float lse_v = any ? m_run[gi] * kLn2 + __logf(l_tot) : -__builtin_inff();
+    if (lse_w[gi] && lse_h[gi] < p.heads) {
+      const int64_t th = (int64_t)tok * p.heads + lse_h[gi];
+      const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + lse_h[gi];
+      if (p.nsplit == 1)
+        p.lse[th] = lse_v[gi];
+      else if (p.sync)  // read by other workgroups in this launch: coherent store
+        __hip_atomic_store(p.part_lse + slot, lse_v[gi], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      else
+        p.part_lse[slot] = lse_v[gi];
+    }
     if (!h_ok[gi]) continue;
     const int64_t th = (int64_t)tok * p.heads + h[gi];
     if (p.nsplit == 1) {
@@ -813,25 +1035,22 @@ void split_kernel(SplitParams p) {
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int c0 = (cs * CB + cb) * 16 + 4 * g;
-        const floatx4 o = oacc[gi][cb] * inv;
+        const floatx4 o = oacc[gi][cb] * inv[gi];
         *(u32x2*)(orow + c0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       }
-      if (g == 0 && cs == 0) p.lse[th] = lse_v;
     } else {
       const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + h[gi];
       float* orow = p.part_o + slot * kDV;
       if (p.sync) {  // read by other workgroups in this launch: coherent stores
 #pragma unroll
-        for (int cb = 0; cb < CB; ++cb) st_agent(orow + (cs * CB + cb) * 16 + 4 * g, oacc[gi][cb] * inv);
-        if (g == 0 && cs == 0)
-          __hip_atomic_store(p.part_lse + slot, lse_v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int cb = 0; cb < CB; ++cb)
+          st_agent(orow + (cs * CB + cb) * 16 + 4 * g, oacc[gi][cb] * inv[gi]);
       } else {
 #pragma unroll
         for (int cb = 0; cb < CB; ++cb) {
           const int c0 = (cs * CB + cb) * 16 + 4 * g;
-          *(floatx4*)(orow + c0) = oacc[gi][cb] * inv;
+          *(floatx4*)(orow + c0) = oacc[gi][cb] * inv[gi];
         }
-        if (g == 0 && cs == 0) p.part_lse[slot] = lse_v;
       }
     }
   }
@@ -999,28 +1218,31 @@ __global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineP
 // LDS of one split workgroup: two tile buffers, the staged index list, and
 // with K-split pairs the exchange slots of partial scores (one 16-row block
 // of 16 heads = 1 KiB per slot, head group and row block)
-constexpr int split_lds_bytes(int waves, int ncs, int gpw, bool ksplit) {
-  return 2 * kTileRows * kRow * 2 + split_list_cap(ncs, ksplit) * 4 +
-         (ksplit ? (waves / ncs) * 2 * gpw * (kTileRows / 16) * 64 * 16 : 0);
+constexpr int split_lds_bytes(int waves, int ncs, int gpw, int ks) {
+  return 2 * kTileRows * kRow * 2 + split_list_cap(ncs, ks) * 4 +
+         (ks == 2 ? (waves / ncs) * 2 * gpw * (kTileRows / 16) * 64 * 16 : 0) +
+         (ks == 4 ? waves * gpw * (kTileRows / 16) * 64 * 16 + (waves / ncs) * gpw * 64 * 16 +
+                        2 * (waves / ncs) * gpw * 16 * 4
+                  : 0);
 }
 constexpr int kCuLdsBytes = 160 * 1024;
 
-template <int HG, int NCS, int GPW, int TR, bool KSPLIT>
+template <int HG, int NCS, int GPW, int TR, int KS>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
   static_assert(TR == kTileRows, "the planner's tile");
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
   const dim3 grid((unsigned)nwg), block(64 * (HG / GPW) * NCS);
   switch (p.src) {
     case kSrcPositions:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KSPLIT, kSrcPositions>), grid, block, 0,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcPositions>), grid, block, 0,
                          st, p);
       break;
     case kSrcDense:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KSPLIT, kSrcDense>), grid, block, 0, st,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcDense>), grid, block, 0, st,
                          p);
       break;
     default:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KSPLIT, kSrcRows>), grid, block, 0, st,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcRows>), grid, block, 0, st,
                          p);
   }
   return hipGetLastError();
@@ -1032,22 +1254,21 @@ static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t 
 //    two workgroups per CU;
 //  * up to 32 heads: 4 waves = 2 head groups x 2 column halves, each wave
 //    all of QK^T; two workgroups per CU;
-//  * more (64-head blocks): 8 waves = 4 head groups x 2 column halves in
-//    K-split pairs; one workgroup per CU (its registers allow two waves per
-//    SIMD, i.e. 8 waves per CU).  Two head groups per wave would halve the
-//    LDS reads per head but need about 480 registers, one wave per SIMD:
-//    measured 20% slower, the LDS latency is no longer hidden.  A third tile
-//    buffer (two tiles in flight) measured about 3% slower on a 64 x 64-head
-//    batch: it gained nothing in overlap, and its refills, issued every step
-//    so that the compiler keeps the pipeline full, round the tile count up.
-constexpr int kGpwLarge = 1;
-static_assert(kCuLdsBytes / split_lds_bytes(4, 4, 1, true) == 2, "two 16-head workgroups per CU");
-static_assert(kCuLdsBytes / split_lds_bytes(4, 2, 1, false) == 2, "two 32-head workgroups per CU");
+//  * more (64-head blocks): 8 waves = 2 head pairs x 4 column quarters in
+//    K-split quads (QK^T for both groups of a pair, softmax owned per 8
+//    heads); one workgroup per CU (about 200 registers: two waves per SIMD,
+//    i.e. 8 waves per CU).  A third tile buffer (two tiles in flight)
+//    measured about 3% slower on a 64 x 64-head batch: it gained nothing in
+//    overlap, and its refills, issued every step so that the compiler keeps
+//    the pipeline full, round the tile count up.
+static_assert(kCuLdsBytes / split_lds_bytes(4, 4, 1, 2) == 2, "two 16-head workgroups per CU");
+static_assert(kCuLdsBytes / split_lds_bytes(4, 2, 1, 1) == 2, "two 32-head workgroups per CU");
+static_assert(split_lds_bytes(8, 4, 2, 4) <= kCuLdsBytes, "one 64-head workgroup per CU");
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
-  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, true>(p, 1, st);
-  if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, false>(p, 1, st);
-  return launch_split_t<4, 2, kGpwLarge, 32, true>(p, (p.heads + 63) / 64, st);
+  if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, 2>(p, 1, st);
+  if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, 1>(p, 1, st);
+  return launch_split_t<4, 4, 2, 32, 4>(p, (p.heads + 63) / 64, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }
@@ -1055,8 +1276,8 @@ int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 3
 // workgroups of the head class resident per CU: LDS bounds the 4-wave
 // classes at two; the 8-wave class at 2 waves per SIMD is one per CU
 int split_blocks_per_cu(int heads) {
-  if (heads <= 16) return kCuLdsBytes / split_lds_bytes(4, 4, 1, true);
-  if (heads <= 32) return kCuLdsBytes / split_lds_bytes(4, 2, 1, false);
+  if (heads <= 16) return kCuLdsBytes / split_lds_bytes(4, 4, 1, 2);
+  if (heads <= 32) return kCuLdsBytes / split_lds_bytes(4, 2, 1, 1);
   return 1;
 }
 

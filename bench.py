@@ -426,12 +426,14 @@ def main():
     flops = T * H * K * 2 * (576 + 512) * (int((w.sets[0] >= 0).sum()) / max(1, T * K))
     achieved = kv_split / (split_us * 1e-6) / 1e9
     traffic = None
+    mfma_counters = None  # the profile's MFMA counters, while it matches this kernel
     if os.path.exists(TRAFFIC_FILE):
         key = args.workload + (str(args.spec_ctx) if args.workload in ("spec", "verify") else "") + \
             ("_paged" if w.kind == "paged" else "")
         rec = json.load(open(TRAFFIC_FILE)).get(key)
         if rec and rec.get("kernel_sha") == kernel_sha() and rec.get("nsplit") == nsplit and not args.warm:
             traffic = rec.get("bytes_per_launch")
+            mfma_counters = rec
 
     # ---- NSPLIT sweep of the same workload, and the batch-64 workload at the
     # planner's NSPLIT beside a batch-1 headline (graph timing only)
@@ -499,7 +501,19 @@ def main():
         },
         "mfma": {"achieved_tflops": round(flops / (split_us * 1e-6) / 1e12, 3),
                  "peak_tflops": MFMA_BF16_PEAK_TFLOPS,
-                 "frac": round(flops / (split_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5)},
+                 "frac": round(flops / (split_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 5),
+                 "flops": "algorithmic: tokens x heads x valid entries x 2 x (576 + 512)",
+                 "counters": None if not mfma_counters or "mfma_flops_per_launch" not in mfma_counters else {
+                     "executed_flops_per_launch": mfma_counters["mfma_flops_per_launch"],
+                     "executed_tflops": round(mfma_counters["mfma_flops_per_launch"]
+                                              / (split_us * 1e-6) / 1e12, 3),
+                     "busy_frac": round(mfma_counters["mfma_busy_simd_cycles"]
+                                        / (1024 * split_us * 1e-6 * 2.4e9), 5),
+                     "source": mfma_counters.get("source"),
+                     "note": "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (heads padded to 16-head groups, "
+                             "entries to 32-row tiles, and the QK^T both K-split pairs of a 16-head "
+                             "block compute, included) and SQ_VALU_MFMA_BUSY_CYCLES over 1024 SIMDs "
+                             "x the live split time x 2.4 GHz"}},
         "kernel_sha": kernel_sha(),
     }
     result["dispatch_floor_us"] = round(dispatch_floor_us(), 3)

@@ -417,7 +417,7 @@ __device__ __forceinline__ void dma_tile(const u32x4* src, uint8_t* lds,
 // Keeps a value in its registers up to this point.
 __device__ __forceinline__ void keep_live(uint64_t v) { asm volatile("" ::"v"(v)); }
 
-template <int HG, int NCS, int GPW, int TR, int KS, int SRC>
+template <int HG, int NCS, int GPW, int TR, int KS, int NBUF, int SRC>
 __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
 __attribute__((amdgpu_waves_per_eu(GPW == 1 || KS == 4 ? 2 : 1)))
 void split_kernel(SplitParams p) {
@@ -427,6 +427,9 @@ void split_kernel(SplitParams p) {
   constexpr bool KQ = KS == 4;      // K-split quads with the softmax owned per 8 heads
   static_assert(!KSPLIT || NCS % 2 == 0, "K-split pairs waves of opposite parity");
   static_assert(!KQ || (NCS == 4 && GPW == 2 && TR == 32), "K-split quad shape");
+  // tile buffers: two, or for quads over long slices three (two tiles in
+  // flight while one is computed)
+  static_assert(NBUF == 2 || (NBUF == 3 && KQ), "tile buffers");
   constexpr int NT = 64 * (HG / GPW) * NCS;
   // waves that issue the tile loads: all of them, or half of them when the
   // tile's wave loads do not split evenly (36 per 32-row tile: not over 8)
@@ -456,6 +459,7 @@ void split_kernel(SplitParams p) {
   // for every outstanding load before each LDS read).
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tb2[NBUF > 2 ? kTileBytes : 16];
   __shared__ __attribute__((aligned(16))) int list_s[LCAP];
   // K-split pairs: partial S^T per (head group, parity) slot: [slot][gi][rb][lane];
   // quads: every wave's partial S^T, [wave][gi][rb][lane ^ 8*rb]
@@ -619,8 +623,9 @@ void split_kernel(SplitParams p) {
   // lane share one 64-bit address (see dma_tile), returned so that the caller
   // keeps it live until the loads are known to be complete.
   static_assert(DP == 1, "one row per lane per tile");
-  auto issue = [&](uint8_t* buf, int t) __attribute__((always_inline)) -> uint64_t {
-    const int32_t r = list_s[t * TR + dma_row[0]];  // t * TR + TR <= LCAP
+  auto issue = [&](uint8_t* buf, int t, int ntiles) __attribute__((always_inline)) -> uint64_t {
+    // a tile past the last (three buffers refill every step) loads the zero row
+    const int32_t r = t < ntiles ? list_s[min(t * TR + dma_row[0], LCAP - 1)] : -1;
     const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
     const u32x4* src = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran[0];
     if (wave < DW)
@@ -628,8 +633,10 @@ void split_kernel(SplitParams p) {
     return (uint64_t)(uintptr_t)src;
   };
 
-  // Consume tile t held in T, K-split quads.
-  auto compute_quad = [&](const uint8_t* T, int t) __attribute__((always_inline)) {
+  // Consume tile t held in T, K-split quads; refill() issues the step's tile
+  // loads once this wave's QK^T operand reads are done (LDS-DMA writes
+  // landing in LDS hold off the waves' LDS reads).
+  auto compute_quad = [&](const uint8_t* T, int t, auto&& refill) __attribute__((always_inline)) {
     if constexpr (KQ) {
       // ---- partial S^T = KV_tile * Q^T over the wave's K-steps kr + 4k, for
       // both head groups of the pair (each operand read feeds two MFMAs)
@@ -677,6 +684,7 @@ void split_kernel(SplitParams p) {
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
           xs[((wave_u * GPW + gi) * RB + rb) * 64 + (lane ^ (8 * rb))] = acc[gi][rb];
+      refill();
       barrier_lds();
       const floatx4 own0 = go ? acc[1][0] : acc[0][0];
       const floatx4 own1 = go ? acc[1][1] : acc[0][1];
@@ -947,34 +955,69 @@ void split_kernel(SplitParams p) {
   if (lo < hi) store_list(min(hi - lo, LCAP));
   auto buf = [&](auto bconst) __attribute__((always_inline)) -> uint8_t* {
     constexpr int b = decltype(bconst)::value;
-    return b == 0 ? tb0 : tb1;
+    return b == 0 ? tb0 : b == 1 ? tb1 : tb2;
   };
+  // With three buffers q has landed before the first tile loads go out: the
+  // compiler otherwise waits, at the entry of the tile loop (whose MFMAs read
+  // q), for every load outstanding, the two tiles in flight included.
+  if constexpr (NBUF > 2) wait_vmcnt<0>();
   for (int clo = lo; clo < hi; clo += LCAP) {
     const int n_ent = min(hi - clo, LCAP);
     const int ntiles = (n_ent + TR - 1) / TR;
-    // double buffering: tile n+1 loads while tile n is computed
-    uint64_t addr[2] = {};  // per buffer: the address its last loads read
-    addr[0] = issue(tb0, 0);
+    // NBUF buffers: tiles n+1 .. n+NBUF-1 load while tile n is computed.
+    // With two, the refill past the last tile is skipped.  With three, every
+    // step issues one refill (a tile past the last loads the zero row) and
+    // the steps come in unconditional rounds of three, whose steps past the
+    // last tile only wait, pass the barrier and refill: the number of loads
+    // in flight is then the same at every wait, and no branch joins paths
+    // with different loads outstanding (at such joins the compiler waits for
+    // all of them, draining the pipeline).
+    uint64_t addr[NBUF] = {};  // per buffer: the address its last loads read
+    addr[0] = issue(tb0, 0, ntiles);
+    if constexpr (NBUF > 2) addr[1] = issue(tb1, 1, ntiles);
     // one pipeline step on buffer b (a compile-time constant)
     auto step = [&](auto bconst, int n) __attribute__((always_inline)) {
       constexpr int b = decltype(bconst)::value;
-      wait_vmcnt<0>();     // tile n landed
+      // tile n landed (with three buffers tile n+1's L loads may still be out)
+      wait_vmcnt<(NBUF - 2) * L>();
       keep_live(addr[b]);  // its loads are done: their address may go
       barrier_raw();
-      // refill the other buffer, which every wave finished with in the
-      // previous step
-      if (n + 1 < ntiles) addr[b ^ 1] = issue(buf(std::integral_constant<int, b ^ 1>{}), n + 1);
-      if constexpr (KQ)
-        compute_quad(buf(bconst), n);
-      else
+      // refill the buffer every wave finished with in the previous step
+      constexpr int bn = (b + NBUF - 1) % NBUF;
+      auto refill = [&]() __attribute__((always_inline)) {
+        if (NBUF > 2 || n + 1 < ntiles)
+          addr[bn] = issue(buf(std::integral_constant<int, bn>{}), n + NBUF - 1, ntiles);
+      };
+      if constexpr (KQ && NBUF > 2) {
+        // the refill goes out after the tile's QK^T (it still has two steps
+        // to land); a step past the last tile only refills
+        if (n < ntiles)
+          compute_quad(buf(bconst), n, refill);
+        else
+          refill();
+      } else if constexpr (KQ) {
+        refill();
+        compute_quad(buf(bconst), n, [] {});
+      } else {
+        refill();
         compute(buf(bconst), n);
+      }
     };
-    for (int n0 = 0; n0 < ntiles; n0 += 2) {
-      step(std::integral_constant<int, 0>{}, n0);
-      if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
+    if constexpr (NBUF > 2) {
+      for (int n0 = 0; n0 < ntiles; n0 += 3) {
+        step(std::integral_constant<int, 0>{}, n0);
+        step(std::integral_constant<int, 1>{}, n0 + 1);
+        step(std::integral_constant<int, 2>{}, n0 + 2);
+      }
+      wait_vmcnt<0>();  // the refills past the last tile
+    } else {
+      for (int n0 = 0; n0 < ntiles; n0 += 2) {
+        step(std::integral_constant<int, 0>{}, n0);
+        if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
+      }
     }
-    keep_live(addr[0]);
-    keep_live(addr[1]);
+#pragma unroll
+    for (int b = 0; b < NBUF; ++b) keep_live(addr[b]);
     barrier_raw();  // list_s and the buffers are reused by the next chunk
     const int nxt = clo + LCAP;
     if (nxt < hi) {
@@ -1215,11 +1258,13 @@ __global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineP
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// LDS of one split workgroup: two tile buffers, the staged index list, and
-// with K-split pairs the exchange slots of partial scores (one 16-row block
-// of 16 heads = 1 KiB per slot, head group and row block)
-constexpr int split_lds_bytes(int waves, int ncs, int gpw, int ks) {
-  return 2 * kTileRows * kRow * 2 + split_list_cap(ncs, ks) * 4 +
+// LDS of one split workgroup: the tile buffers (two, or three for K-split
+// quads over long slices), the staged index list, with K-split pairs the exchange slots of
+// partial scores (one 16-row block of 16 heads = 1 KiB per slot, head group
+// and row block), with quads every wave's partial scores, the bf16 weights
+// and two floats per head
+constexpr int split_lds_bytes(int waves, int ncs, int gpw, int ks, int nbuf = 2) {
+  return nbuf * kTileRows * kRow * 2 + split_list_cap(ncs, ks) * 4 +
          (ks == 2 ? (waves / ncs) * 2 * gpw * (kTileRows / 16) * 64 * 16 : 0) +
          (ks == 4 ? waves * gpw * (kTileRows / 16) * 64 * 16 + (waves / ncs) * gpw * 64 * 16 +
                         2 * (waves / ncs) * gpw * 16 * 4
@@ -1227,28 +1272,28 @@ constexpr int split_lds_bytes(int waves, int ncs, int gpw, int ks) {
 }
 constexpr int kCuLdsBytes = 160 * 1024;
 
-template <int HG, int NCS, int GPW, int TR, int KS>
+template <int HG, int NCS, int GPW, int TR, int KS, int NB = 2>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
   static_assert(TR == kTileRows, "the planner's tile");
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
   const dim3 grid((unsigned)nwg), block(64 * (HG / GPW) * NCS);
   switch (p.src) {
     case kSrcPositions:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcPositions>), grid, block, 0,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcPositions>), grid, block, 0,
                          st, p);
       break;
     case kSrcDense:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcDense>), grid, block, 0, st,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcDense>), grid, block, 0, st,
                          p);
       break;
     default:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcRows>), grid, block, 0, st,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcRows>), grid, block, 0, st,
                          p);
   }
   return hipGetLastError();
 }
 
-// Per head class (all with two tile buffers):
+// Per head class:
 //  * up to 16 heads: 4 waves sharing one 16-head group, each with a quarter
 //    of the 512 V columns, in K-split pairs (even / odd K-steps of QK^T);
 //    two workgroups per CU;
@@ -1256,19 +1301,25 @@ static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t 
 //    all of QK^T; two workgroups per CU;
 //  * more (64-head blocks): 8 waves = 2 head pairs x 4 column quarters in
 //    K-split quads (QK^T for both groups of a pair, softmax owned per 8
-//    heads); one workgroup per CU (about 200 registers: two waves per SIMD,
-//    i.e. 8 waves per CU).  A third tile buffer (two tiles in flight)
-//    measured about 3% slower on a 64 x 64-head batch: it gained nothing in
-//    overlap, and its refills, issued every step so that the compiler keeps
-//    the pipeline full, round the tile count up.
+//    heads); one workgroup per CU (about 230 registers: two waves per SIMD,
+//    i.e. 8 waves per CU), with a third tile buffer over long slices.
 static_assert(kCuLdsBytes / split_lds_bytes(4, 4, 1, 2) == 2, "two 16-head workgroups per CU");
 static_assert(kCuLdsBytes / split_lds_bytes(4, 2, 1, 1) == 2, "two 32-head workgroups per CU");
-static_assert(split_lds_bytes(8, 4, 2, 4) <= kCuLdsBytes, "one 64-head workgroup per CU");
+static_assert(split_lds_bytes(8, 4, 2, 4, 3) <= kCuLdsBytes, "one 64-head workgroup per CU");
+
+// 64-head blocks over slices of at least this many tiles take three tile
+// buffers.  Measured: 128 x 128 heads with 64-tile slices 111 against 115 us;
+// 64 x 64 heads with 16-tile slices unchanged; dense verify with 4- to
+// 16-tile slices 4-7% slower (the rounds of three steps pad the tail).
+constexpr int kDeepTiles = 32;
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
   if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, 2>(p, 1, st);
   if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, 1>(p, 1, st);
-  return launch_split_t<4, 4, 2, 32, 4>(p, (p.heads + 63) / 64, st);
+  const int hblocks = (p.heads + 63) / 64;
+  if ((p.per_split + kTileRows - 1) / kTileRows >= kDeepTiles)
+    return launch_split_t<4, 4, 2, 32, 4, 3>(p, hblocks, st);
+  return launch_split_t<4, 4, 2, 32, 4, 2>(p, hblocks, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }

@@ -366,8 +366,8 @@ __device__ __forceinline__ void fused_combine(const SplitParams& p, int unit, in
 //           sum, rescale factor), and the bf16 weights go back through LDS
 //           as the PV operands of all four.  Each LDS operand read feeds two
 //           MFMAs (one per head group) with no duplicated softmax, at about
-//           200 registers: two waves per SIMD.
-// TR rows per tile, two tile buffers: one tile is in flight while the other
+//           220 registers: two waves per SIMD.
+// TR rows per tile, NBUF tile buffers: NBUF - 1 tiles are in flight while one
 // is computed.
 // ---------------------------------------------------------------------------
 // The dispatcher hands workgroup i to XCD i % kXcds (round robin over the
@@ -466,7 +466,7 @@ void split_kernel(SplitParams p) {
   __shared__ __attribute__((aligned(16)))
   floatx4 xs[KSPLIT ? kXsSlots * GPW * RB * 64 : KQ ? (NT / 64) * GPW * RB * 64 : 1];
   // quads: the bf16 weights P^T as PV B operands, [head pair][gi][g][head][8],
-  // the owners' rescale factors per head, and their final sums and maxima
+  // the owners' rescale factors per head, and their final sums
   __shared__ __attribute__((aligned(16))) u32x4 ps[KQ ? (HG / GPW) * GPW * 64 : 1];
   __shared__ float alpha_s[KQ ? HG * 16 : 1];
   __shared__ float fin_l[KQ ? HG * 16 : 1];
@@ -513,9 +513,6 @@ void split_kernel(SplitParams p) {
     h_ok[gi] = h[gi] < p.heads;
   }
 
-  // Q^T as the B operand of S^T = KV * Q^T: lane (g, l16) holds
-  // q[h][32*ks + 8*g .. +7] for every K-step ks (zeros for padding heads,
-  // read from the zero row: 72 granules cover 18 K-steps x 4 groups).
   // this split's slice of the list; the first chunk's entries are loaded
   // before q, so that the tile loads can start as soon as the list is in
   const int lo = min(split * p.per_split, p.topk);
@@ -550,7 +547,10 @@ void split_kernel(SplitParams p) {
   };
   if (lo < hi) load_list(lo, min(hi - lo, LCAP));
 
-  // with K-split pairs wave half cs holds K-steps 2k + cs
+  // Q^T as the B operand of S^T = KV * Q^T: lane (g, l16) holds
+  // q[h][32*ks + 8*g .. +7] for each of the wave's K-steps ks (zeros for
+  // padding heads, read from the zero row: 72 granules cover 18 K-steps x 4
+  // groups): all 18, with K-split pairs 2k + (cs & 1), with quads kr + 4k
   bf16x8 qb[GPW][KSW];
 #pragma unroll
   for (int gi = 0; gi < GPW; ++gi) {
@@ -590,7 +590,7 @@ void split_kernel(SplitParams p) {
                  cs * (CB / 4) * TR * 128;
 
   // DMA: wave instruction it fills slots 64*m .. 64*m + 63, m = it*WPB + wave
-  // (WPB = waves per workgroup): block kb = m / RG, rows 8*(m % RG) + lane/8
+  // (WPB = DW, the loading waves): block kb = m / RG, rows 8*(m % RG) + lane/8
   // (RG = TR/8 row groups per block), in-block slot lane % 8, which holds
   // granule (lane % 8) ^ h(row).  If RG >= WPB a lane cycles through
   // DP = RG / WPB rows (d = it % DP, kb = it / DP); otherwise it keeps one

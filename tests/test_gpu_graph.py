@@ -6,6 +6,7 @@ times with the program's own eager work and device synchronisations between
 replays (other calls on the same buffers, fills of the outputs with NaN),
 and checks every replay bit for bit against the eager result of the same
 call.  Covered: smla_decode at NSPLIT 1 and 4 (split and combine kernels),
+and over 64-head slices long enough for three tile buffers,
 smla_decode_paged, smla_decode_dense (folded), smla_decode_fused (single
 launch, with its synchronisation words) and smla_topk.
 """
@@ -84,6 +85,26 @@ def test_graph_decode(smla, nsplit):
 
     def disturb():  # the same workspace used by an eager call on other inputs
         smla.smla_decode(odev["q"], odev["kv"], odev["idx"], oout, olse, other.scale, nsplit,
+                         workspace_t=ws)
+    _replays(fn, [out, lse], disturb)
+
+
+def test_graph_decode_three_buffers(smla):
+    """64 heads over slices of 79 tiles: the three-buffer pipeline (refills
+    of tiles past the last load the zero row) replayed."""
+    inp = flat_inputs("graph3", 9510, 1, 1, 64, 65536, 5000)
+    dev = to_device(inp, "cuda")
+    out, lse = _bufs(inp)
+    ws = smla.workspace(inp.batch, inp.q_len, inp.heads, 2, "cuda")
+    other = flat_inputs("graph3_other", 9511, 1, 1, 64, 65536, 5000)
+    odev = to_device(other, "cuda")
+    oout, olse = _bufs(other)
+
+    def fn():
+        smla.smla_decode(dev["q"], dev["kv"], dev["idx"], out, lse, inp.scale, 2, workspace_t=ws)
+
+    def disturb():
+        smla.smla_decode(odev["q"], odev["kv"], odev["idx"], oout, olse, other.scale, 2,
                          workspace_t=ws)
     _replays(fn, [out, lse], disturb)
 

@@ -5,7 +5,8 @@ head counts that leave partial head blocks (1, 17, 24, 33, 130, 1000), list
 lengths that leave ragged tiles (1, 33, 100, 257) or span several staged list
 chunks (5000); masked, out-of-range and duplicated indices; fully empty
 selections and empty splits; topk == 0; the split kernel's partials against
-the oracle's per-split results; the combine kernel alone on synthetic
+the oracle's per-split results; seeded random shapes across the head
+classes, list lengths and split counts; the combine kernel alone on synthetic
 partials (both its few-pair and many-pair forms, with NaN in the slots of
 empty splits); bit-exact repeatability; output and workspace buffers
 poisoned with NaN beforehand; a non-default stream.
@@ -88,6 +89,33 @@ def test_shapes(smla, shape):
     for ns in nsplits:
         out, lse, used = _decode(smla, inp, dev, ns)
         _parity(*_host(out, lse), o_r, l_r, f"b{b} q{lq} h{h} k{k} nsplit={ns} (used {used})")
+
+
+# Seeded random shapes over every head class, list length and split count
+# (including NSPLIT above the list length and the planner), each against the
+# oracle: the fixed shapes above pin the known corners, these sample between.
+def _random_shapes(n=10, seed=4242):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        h = int(rng.choice([1, 3, 8, 15, 16, 19, 32, 40, 63, 64, 65, 96, 129]))
+        k = int(rng.integers(1, 3000))
+        rows = int(rng.integers(k, 3 * k + 2))
+        b, lq = int(rng.integers(1, 4)), int(rng.integers(1, 3))
+        ns = [0, int(rng.integers(1, 9)), int(rng.integers(9, 130))]
+        out.append((b, lq, h, k, rows, ns))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(), ids=lambda s: "b{}q{}h{}k{}r{}".format(*s[:5]))
+def test_random_shapes(smla, shape):
+    b, lq, h, k, rows, nsplits = shape
+    inp = flat_inputs("rand_shape", 6000 + h * 13 + k, b, lq, h, rows, k)
+    dev = to_device(inp, "cuda")
+    o_r, l_r = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
+    for ns in nsplits:
+        out, lse, used = _decode(smla, inp, dev, ns)
+        _parity(*_host(out, lse), o_r, l_r, f"b{b} q{lq} h{h} k{k} rows{rows} nsplit={ns} (used {used})")
 
 
 # ------------------------------------------------------------ masking

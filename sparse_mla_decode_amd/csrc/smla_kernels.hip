@@ -1195,7 +1195,9 @@ __global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) 
 // one pair, 128 threads per pair, two pairs per workgroup.  Every thread
 // walks all splits itself (the pair's LSE values are the same addresses for
 // its 128 threads), so there is no LDS, no barrier and no cross-wave
-// reduction; the grid alone supplies the parallelism.
+// reduction; the grid alone supplies the parallelism.  Workgroups take
+// pairs in the XCD-contiguous numbering of the split kernel, so that a
+// token's pairs are merged on the XCD whose L2 took its partials.
 constexpr int kWidePairs = 2;
 // from this many (token, head) pairs on, the wide combine has >= 512
 // workgroups, enough to cover the device
@@ -1203,7 +1205,8 @@ constexpr int64_t kWideMinPairs = 1024;
 
 template <int CH>
 __global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineParams p) {
-  const int64_t th = (int64_t)blockIdx.x * kWidePairs + (threadIdx.x >> 7);
+  const int64_t th =
+      (int64_t)xcd_contiguous(blockIdx.x, gridDim.x) * kWidePairs + (threadIdx.x >> 7);
   if (th >= (int64_t)p.tokens * p.heads) return;
   const int c4 = threadIdx.x & 127;
   const int64_t tok = th / p.heads;

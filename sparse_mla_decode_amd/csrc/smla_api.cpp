@@ -20,12 +20,12 @@ static_assert(SMLA_ROW == smla::kRow && SMLA_DV == smla::kDV, "widths out of syn
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
 
-// CU count of the current device, queried once per device.
 // bound on the polls of a workgroup waiting for its unit's partials in the
 // single-launch merge (each poll: a short sleep and one device-scope load)
 constexpr int kDefaultMergePolls = 2048;
 std::atomic<int> g_merge_polls{kDefaultMergePolls};
 
+// CU count of the current device, queried once per device.
 int device_cus(int* cus) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) {

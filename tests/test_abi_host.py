@@ -151,7 +151,7 @@ def test_single_launch_query(smla):
     q = smla.lib.smla_fused_in_launch
     assert q(1, 1, 8, 1) == 0
     assert q(1, 1, 8, 65) == 0 and q(4, 1, 128, 1024) == 0
-    assert q(1, 1, 0, 4) == -2 and q(-1, 1, 8, 4) == -2 and q(1, 1, 5000, 4) == -2
+    assert q(1, 1, 0, 4) == -2 and q(-1, 1, 8, 4) == -2 and q(1, 1, 4097, 4) == -2
     assert q(1, 1, 8, 0) == -3 and q(1, 1, 8, 1025) == -3
 
 
@@ -185,7 +185,7 @@ def test_invalid_arguments_rejected_before_launch(smla, fn):
     assert _call(smla, fn, idx=0) == -1
     assert _call(smla, fn, batch=-1) == -2
     assert _call(smla, fn, heads=0) == -2
-    assert _call(smla, fn, heads=5000) == -2
+    assert _call(smla, fn, heads=4097) == -2  # one above SMLA_MAX_HEADS
     assert _call(smla, fn, topk=-3) == -2
     assert _call(smla, fn, kv_rows=-1) == -2
     assert _call(smla, fn, nsplit=-1) == -3

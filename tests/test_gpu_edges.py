@@ -9,7 +9,8 @@ the oracle's per-split results; seeded random shapes across the head
 classes, list lengths and split counts; the combine kernel alone on synthetic
 partials (both its few-pair and many-pair forms, with NaN in the slots of
 empty splits); bit-exact repeatability; output and workspace buffers
-poisoned with NaN beforehand; a non-default stream.
+poisoned with NaN beforehand; a non-default stream; the limits (4096 heads,
+NSPLIT 1024, a list over all 65536 rows of a cache).
 """
 from __future__ import annotations
 
@@ -84,6 +85,32 @@ SHAPES = [  # batch, q_len, heads, topk, kv_rows, nsplits
 def test_shapes(smla, shape):
     b, lq, h, k, rows, nsplits = shape
     inp = flat_inputs("shape", 5000 + h * 7 + k, b, lq, h, rows, k)
+    dev = to_device(inp, "cuda")
+    o_r, l_r = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
+    for ns in nsplits:
+        out, lse, used = _decode(smla, inp, dev, ns)
+        _parity(*_host(out, lse), o_r, l_r, f"b{b} q{lq} h{h} k{k} nsplit={ns} (used {used})")
+
+
+# The library's limits and the largest list: the most heads a call accepts
+# (4096: 64 head blocks), the most splits (1024, with 2 and with 0.1 entries
+# per split), and a list that is a permutation of a whole 65536-row cache
+# (attention over every row: one split walks 2048 tiles and 64 staged list
+# chunks, the planner's split count 256 of 8 tiles).
+LIMITS = [  # batch, q_len, heads, topk, kv_rows, nsplits
+    (1, 1, 4096, 300, 4096, [1, 0, 3]),
+    (1, 1, 8, 2048, 4096, [1024]),
+    (2, 1, 16, 100, 4096, [1024]),
+    (1, 1, 8, 65536, 65536, [0, 1]),
+]
+
+
+@pytest.mark.parametrize("shape", LIMITS, ids=lambda s: "b{}q{}h{}k{}n{}".format(*s[:5]))
+def test_limits(smla, shape):
+    b, lq, h, k, rows, nsplits = shape
+    inp = flat_inputs("limits", 7000 + h * 3 + k, b, lq, h, rows, k)
+    if k == rows:  # a permutation of the whole cache
+        assert (np.sort(inp.idx, axis=-1) == np.arange(rows)).all()
     dev = to_device(inp, "cuda")
     o_r, l_r = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
     for ns in nsplits:

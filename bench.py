@@ -54,6 +54,7 @@ METRIC = "decode steps/s + gathered-KV HBM GB/s (% of roofline), sparse MLA topk
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 1152
+MIN_GRAPH_STEPS = 32  # steps per captured graph, at least
 KERNEL_SRC = os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", "smla_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -164,6 +165,9 @@ class Workload:
         self.out = torch.empty((self.B, self.Lq, self.H, 512), dtype=torch.bfloat16, device=dev)
         self.lse = torch.empty((self.B, self.Lq, self.H), dtype=torch.float32, device=dev)
         self.n_rot = self.n_caches * len(self.sets)
+        # steps per captured graph: whole rotation cycles, at least MIN_GRAPH_STEPS
+        # (a graph of one step, as without rotation, would time the graph launch)
+        self.graph_len = self.n_rot * max(1, -(-MIN_GRAPH_STEPS // self.n_rot))
         self.valid_rows = [int((x >= 0).sum()) for x in self.sets]  # every set points inside its cache
         if self.kind == "dense":
             # every query token of a sequence attends to the same context rows:
@@ -236,14 +240,14 @@ class Workload:
         return f
 
     def graph_of(self, fn):
-        """One rotation cycle of fn(i) captured in a HIP graph."""
+        """graph_len calls fn(i) (whole rotation cycles) captured in a HIP graph."""
         torch = self.torch
         torch.cuda.synchronize()
         self.stream.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(self.stream):
             with torch.cuda.graph(g, stream=self.stream):
-                for i in range(self.n_rot):
+                for i in range(self.graph_len):
                     fn(i)
         torch.cuda.synchronize()
         g.replay()
@@ -253,7 +257,7 @@ class Workload:
     def time_graph(self, g, min_launches):
         """Mean microseconds per captured call over whole-cycle replays."""
         torch = self.torch
-        reps = max(1, -(-min_launches // self.n_rot))
+        reps = max(1, -(-min_launches // self.graph_len))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         a.record()
@@ -261,7 +265,7 @@ class Workload:
             g.replay()
         b.record()
         torch.cuda.synchronize()
-        return 1e3 * a.elapsed_time(b) / (reps * self.n_rot), reps * self.n_rot
+        return 1e3 * a.elapsed_time(b) / (reps * self.graph_len), reps * self.graph_len
 
     def split_time(self, nsplit, kernel_steps, step_us):
         """The split kernel's time per launch: a graph of split-only launches
@@ -274,7 +278,7 @@ class Workload:
 
     def settle(self, g, seconds):
         """Untimed replays of graph g for `seconds` (clocks ramp up under load)."""
-        self.settle_graph(g, seconds, max(1, 64 // self.n_rot))
+        self.settle_graph(g, seconds, max(1, 64 // self.graph_len))
 
     def settle_graph(self, g, seconds, per_sync=1):
         t0 = time.time()

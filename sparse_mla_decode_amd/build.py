@@ -16,8 +16,12 @@ SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "smla_topk
            os.path.join(CSRC, "smla_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-# Packed-fp32 VALU ops stay disabled in every device compile.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-fp32 VALU ops stay disabled in every device compile.  Kernel-argument
+# preloading: up to 14 leading scalar or pointer arguments of a kernel arrive
+# in SGPRs when its waves start (the decode kernels put their first-needed
+# fields there); struct arguments are never preloaded.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-kernarg-preload-count=14"]
 
 
 def build(verbose: bool = False) -> str:

@@ -417,10 +417,55 @@ __device__ __forceinline__ void dma_tile(const u32x4* src, uint8_t* lds,
 // Keeps a value in its registers up to this point.
 __device__ __forceinline__ void keep_live(uint64_t v) { asm volatile("" ::"v"(v)); }
 
+// Kernel arguments.  What a workgroup needs before its first memory access
+// (the list, q and cache addresses and the sizes that locate its slice)
+// comes first, as separate scalar arguments: the library is built with
+// kernel-argument preloading, so the dispatcher places those 14 dwords in
+// SGPRs before the waves start and the first list load waits on no read of
+// the argument segment (0.3 us, a cold scalar load, at the head of every
+// workgroup's chain of dependent accesses).  The rest of SplitParams travels
+// in a struct, which is never preloaded.
+struct SplitTail {
+  const int32_t* table;
+  const int32_t* ctx;
+  uint16_t* out;
+  float* lse;
+  float* part_o;
+  float* part_lse;
+  uint32_t* sync;
+  int src, max_pages, page_size, merge_polls;
+  float scale_log2;
+};
+
 template <int HG, int NCS, int GPW, int TR, int KS, int NBUF, int SRC>
 __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
 __attribute__((amdgpu_waves_per_eu(GPW == 1 || KS == 4 ? 2 : 1)))
-void split_kernel(SplitParams p) {
+void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_kv, int64_t a_kv_rows,
+                  int a_topk, int a_per_split, int a_nsplit, int a_heads, int a_tokens, int a_q_len,
+                  SplitTail tl) {
+  SplitParams p;
+  p.idx = a_idx;
+  p.q = a_q;
+  p.kv = a_kv;
+  p.kv_rows = a_kv_rows;
+  p.topk = a_topk;
+  p.per_split = a_per_split;
+  p.nsplit = a_nsplit;
+  p.heads = a_heads;
+  p.tokens = a_tokens;
+  p.q_len = a_q_len;
+  p.table = tl.table;
+  p.ctx = tl.ctx;
+  p.out = tl.out;
+  p.lse = tl.lse;
+  p.part_o = tl.part_o;
+  p.part_lse = tl.part_lse;
+  p.sync = tl.sync;
+  p.src = tl.src;
+  p.max_pages = tl.max_pages;
+  p.page_size = tl.page_size;
+  p.merge_polls = tl.merge_polls;
+  p.scale_log2 = tl.scale_log2;
   static_assert(HG % GPW == 0, "whole head groups per wave");
   static_assert(KS == 1 || KS == 2 || KS == 4, "K-split factor");
   constexpr bool KSPLIT = KS == 2;  // K-split pairs
@@ -1124,7 +1169,10 @@ constexpr int kCombCols = 128;               // columns per workgroup
 constexpr int kCombC4 = kCombCols / 4;       // 4-float lanes per split group
 
 template <int SG, int PER>
-__global__ __launch_bounds__(kCombC4 * SG) void combine_kernel(CombineParams p) {
+__global__ __launch_bounds__(kCombC4 * SG)
+void combine_kernel(const float* a_part_o, const float* a_part_lse, uint16_t* a_out, float* a_lse,
+                    int a_tokens, int a_heads, int a_nsplit) {
+  const CombineParams p{a_part_o, a_part_lse, a_out, a_lse, a_tokens, a_heads, a_nsplit};
   __shared__ floatx4 acc_s[SG][kCombC4];
   __shared__ float m_s[SG], w_s[SG];
 
@@ -1213,7 +1261,10 @@ constexpr int kWidePairs = 2;
 constexpr int64_t kWideMinPairs = 1024;
 
 template <int CH>
-__global__ __launch_bounds__(128 * kWidePairs) void combine_wide_kernel(CombineParams p) {
+__global__ __launch_bounds__(128 * kWidePairs)
+void combine_wide_kernel(const float* a_part_o, const float* a_part_lse, uint16_t* a_out,
+                         float* a_lse, int a_tokens, int a_heads, int a_nsplit) {
+  const CombineParams p{a_part_o, a_part_lse, a_out, a_lse, a_tokens, a_heads, a_nsplit};
   const int64_t th = (int64_t)combine_order(p) * kWidePairs + (threadIdx.x >> 7);
   if (th >= (int64_t)p.tokens * p.heads) return;
   const int c4 = threadIdx.x & 127;
@@ -1283,23 +1334,44 @@ constexpr int split_lds_bytes(int waves, int ncs, int gpw, int ks, int nbuf = 2)
 }
 constexpr int kCuLdsBytes = 160 * 1024;
 
+static SplitTail split_tail(const SplitParams& p) {
+  SplitTail t;
+  t.table = p.table;
+  t.ctx = p.ctx;
+  t.out = p.out;
+  t.lse = p.lse;
+  t.part_o = p.part_o;
+  t.part_lse = p.part_lse;
+  t.sync = p.sync;
+  t.src = p.src;
+  t.max_pages = p.max_pages;
+  t.page_size = p.page_size;
+  t.merge_polls = p.merge_polls;
+  t.scale_log2 = p.scale_log2;
+  return t;
+}
+
 template <int HG, int NCS, int GPW, int TR, int KS, int NB = 2>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
   static_assert(TR == kTileRows, "the planner's tile");
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
   const dim3 grid((unsigned)nwg), block(64 * (HG / GPW) * NCS);
+  const SplitTail t = split_tail(p);
   switch (p.src) {
     case kSrcPositions:
       hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcPositions>), grid, block, 0,
-                         st, p);
+                         st, p.idx, p.q, p.kv, p.kv_rows, p.topk, p.per_split, p.nsplit, p.heads,
+                         p.tokens, p.q_len, t);
       break;
     case kSrcDense:
       hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcDense>), grid, block, 0, st,
-                         p);
+                         p.idx, p.q, p.kv, p.kv_rows, p.topk, p.per_split, p.nsplit, p.heads,
+                         p.tokens, p.q_len, t);
       break;
     default:
       hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcRows>), grid, block, 0, st,
-                         p);
+                         p.idx, p.q, p.kv, p.kv_rows, p.topk, p.per_split, p.nsplit, p.heads,
+                         p.tokens, p.q_len, t);
   }
   return hipGetLastError();
 }
@@ -1347,7 +1419,7 @@ template <int SG, int PER>
 static hipError_t launch_combine_t(const CombineParams& p, hipStream_t st) {
   const int64_t nwg = (int64_t)p.tokens * p.heads * (kDV / kCombCols);
   hipLaunchKernelGGL((combine_kernel<SG, PER>), dim3((unsigned)nwg), dim3(kCombC4 * SG), 0, st,
-                     p);
+                     p.part_o, p.part_lse, p.out, p.lse, p.tokens, p.heads, p.nsplit);
   return hipGetLastError();
 }
 
@@ -1359,10 +1431,10 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t st) {
     // workgroup of a large grid is resident at once), else of 8
     if (p.nsplit <= 4)
       hipLaunchKernelGGL((combine_wide_kernel<4>), dim3((unsigned)nwg), dim3(128 * kWidePairs), 0,
-                         st, p);
+                         st, p.part_o, p.part_lse, p.out, p.lse, p.tokens, p.heads, p.nsplit);
     else
       hipLaunchKernelGGL((combine_wide_kernel<8>), dim3((unsigned)nwg), dim3(128 * kWidePairs), 0,
-                         st, p);
+                         st, p.part_o, p.part_lse, p.out, p.lse, p.tokens, p.heads, p.nsplit);
     return hipGetLastError();
   }
   // few pairs: the splits of one pair are spread over the waves of a

@@ -501,8 +501,20 @@ __device__ void topk_row(const TopkParams& p, int64_t row, int n, TopkSmem& sm) 
   }
 }
 
+// Kernel arguments: the fields of TopkParams as separate scalars, in its
+// order.  The library is built with kernel-argument preloading, so the first
+// 13 dwords (the score, length and output addresses, rows, q_len, max_ctx,
+// topk and the workspace) reach SGPRs before the waves start, and a
+// workgroup's first score loads wait on no read of the argument segment.
+#define SMLA_TOPK_ARGS                                                                       \
+  const float *a_scores, const int32_t *a_ctx, int32_t *a_out, int64_t a_rows, int a_q_len, \
+      int a_max_ctx, int a_topk, void *a_ws, size_t a_ws_row_bytes, int a_chunks
+#define SMLA_TOPK_PARAMS \
+  { a_scores, a_ctx, a_out, a_rows, a_q_len, a_max_ctx, a_topk, a_ws, a_ws_row_bytes, a_chunks }
+
 template <bool V4>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(SMLA_TOPK_ARGS) {
+  const TopkParams p = SMLA_TOPK_PARAMS;
   __shared__ TopkSmem sm;
   if (p.topk <= 0) return;
   const int64_t row = blockIdx.x;
@@ -553,7 +565,8 @@ __device__ __forceinline__ TopkWs row_ws(const TopkParams& p, int64_t row) {
 }
 
 template <bool V4>
-__global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(TopkParams p) {
+__global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(SMLA_TOPK_ARGS) {
+  const TopkParams p = SMLA_TOPK_PARAMS;
   __shared__ uint32_t hist[kBins];
   const int64_t row = blockIdx.x / p.chunks;
   const int c = blockIdx.x % p.chunks;
@@ -572,7 +585,8 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(TopkParams p) 
   for (int i = threadIdx.x; i < kBins; i += kChunkThreads) dst[i] = hist[i];
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_scan_kernel(TopkParams p) {
+__global__ __launch_bounds__(kTopkThreads) void topk_scan_kernel(SMLA_TOPK_ARGS) {
+  const TopkParams p = SMLA_TOPK_PARAMS;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t sw[kTopkWaves + 1];
   __shared__ uint32_t sel[2];
@@ -638,7 +652,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_scan_kernel(TopkParams p) {
 }
 
 template <bool V4>
-__global__ __launch_bounds__(kChunkThreads) void topk_cand_kernel(TopkParams p) {
+__global__ __launch_bounds__(kChunkThreads) void topk_cand_kernel(SMLA_TOPK_ARGS) {
+  const TopkParams p = SMLA_TOPK_PARAMS;
   __shared__ uint32_t sw[kChunkThreads / 64 + 1];
   const int64_t row = blockIdx.x / p.chunks;
   const int c = blockIdx.x % p.chunks;
@@ -663,7 +678,8 @@ __global__ __launch_bounds__(kChunkThreads) void topk_cand_kernel(TopkParams p) 
 }
 
 template <bool V4>
-__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(TopkParams p) {
+__global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(SMLA_TOPK_ARGS) {
+  const TopkParams p = SMLA_TOPK_PARAMS;
   __shared__ TopkSmem sm;
   const int tid = threadIdx.x;
   const int64_t row = blockIdx.x;
@@ -709,17 +725,23 @@ size_t topk_ws_row_bytes(int max_ctx) {
 
 int topk_chunks(int max_ctx) { return (max_ctx + kChunk - 1) / kChunk; }
 
+#define SMLA_TOPK_PASS(p) \
+  (p).scores, (p).ctx, (p).out, (p).rows, (p).q_len, (p).max_ctx, (p).topk, (p).ws, (p).ws_row_bytes, (p).chunks
+
 template <bool V4>
 static hipError_t launch_topk_t(const TopkParams& p, hipStream_t st) {
   if (!p.ws) {
-    hipLaunchKernelGGL(topk_kernel<V4>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st, p);
+    hipLaunchKernelGGL(topk_kernel<V4>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st,
+                       SMLA_TOPK_PASS(p));
     return hipGetLastError();
   }
   const unsigned rc = (unsigned)(p.rows * p.chunks);
-  hipLaunchKernelGGL(topk_hist_kernel<V4>, dim3(rc), dim3(kChunkThreads), 0, st, p);
-  hipLaunchKernelGGL(topk_scan_kernel, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st, p);
-  hipLaunchKernelGGL(topk_cand_kernel<V4>, dim3(rc), dim3(kChunkThreads), 0, st, p);
-  hipLaunchKernelGGL(topk_select_kernel<V4>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st, p);
+  hipLaunchKernelGGL(topk_hist_kernel<V4>, dim3(rc), dim3(kChunkThreads), 0, st, SMLA_TOPK_PASS(p));
+  hipLaunchKernelGGL(topk_scan_kernel, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st,
+                     SMLA_TOPK_PASS(p));
+  hipLaunchKernelGGL(topk_cand_kernel<V4>, dim3(rc), dim3(kChunkThreads), 0, st, SMLA_TOPK_PASS(p));
+  hipLaunchKernelGGL(topk_select_kernel<V4>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st,
+                     SMLA_TOPK_PASS(p));
   return hipGetLastError();
 }
 

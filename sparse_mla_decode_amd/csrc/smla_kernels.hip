@@ -584,11 +584,32 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
     const int64_t row = (int64_t)pg * p.page_size + (pos - pg_i * p.page_size);
     return row < p.kv_rows && row <= 0x7fffffff ? (int32_t)row : -1;
   };
+  // 64-head blocks with positions: the sequence's page-table slice (up to
+  // kTabStage pages) is loaded with the positions, not after them, and staged
+  // in LDS (in the score-exchange buffer, idle whenever the list is staged),
+  // so that mapping a position is an LDS read instead of a second HBM round
+  // trip behind the position's load.  (The 16- and 32-head workgroups fill
+  // exactly half a CU's LDS each, so they keep the direct lookup.)
+  constexpr int kTabStage = 512;
+  constexpr int TI = (kTabStage + NT - 1) / NT;
+  const bool tab_lds = SRC == kSrcPositions && KQ && tab != nullptr && p.max_pages <= kTabStage;
+  int tv[TI];
+  if (tab_lds) {
+#pragma unroll
+    for (int u = 0; u < TI; ++u) {
+      const int i = u * NT + tid;
+      tv[u] = i < p.max_pages ? tab[i] : -1;
+    }
+  }
   constexpr int LI = LCAP / NT;
   int lv[LI];
   auto load_list = [&](int clo, int n_ent) __attribute__((always_inline)) {
 #pragma unroll
-    for (int u = 0; u < LI; ++u) lv[u] = entry(clo + min(u * NT + tid, n_ent - 1));
+    for (int u = 0; u < LI; ++u) {
+      const int e = clo + min(u * NT + tid, n_ent - 1);
+      // a staged table: the raw position now, its row once the table is in LDS
+      lv[u] = tab_lds ? idx_row[e] : entry(e);
+    }
   };
   if (lo < hi) load_list(lo, min(hi - lo, LCAP));
 
@@ -990,6 +1011,25 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   // past the chunk) is stored as -1, so later reads test only r >= 0.
   const uint32_t kv32 = rows32(p.kv_rows);
   auto store_list = [&](int n_ent) __attribute__((always_inline)) {
+    if (tab_lds) {  // uniform: stage the table, then map the positions through it
+      int32_t* ts = (int32_t*)xs;
+#pragma unroll
+      for (int u = 0; u < TI; ++u) {
+        const int i = u * NT + tid;
+        if (i < kTabStage) ts[i] = tv[u];
+      }
+      barrier_lds();
+#pragma unroll
+      for (int u = 0; u < LI; ++u) {
+        const int32_t pos = lv[u];
+        const int pg_i = pos / p.page_size;
+        const bool in_tab = pos >= 0 && pg_i < p.max_pages;
+        const int32_t pg_s = ts[in_tab ? pg_i : 0];  // every read in bounds
+        const int32_t pg = in_tab ? pg_s : -1;
+        const int64_t row = (int64_t)pg * p.page_size + (pos - pg_i * p.page_size);
+        lv[u] = pg >= 0 && row < p.kv_rows && row <= 0x7fffffff ? (int32_t)row : -1;
+      }
+    }
 #pragma unroll
     for (int u = 0; u < LI; ++u) {
       const int e = u * NT + tid;

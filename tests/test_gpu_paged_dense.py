@@ -104,15 +104,31 @@ def test_paged_batched_full_size(smla, batched, nsplit):
     _parity(*_host(out[seqs], lse[seqs]), o_r, l_r, f"paged batched nsplit={nsplit} (used {used})")
 
 
-def test_paged_edges(smla):
+# heads, topk, pages per sequence, page ids drawn, pages inside the cache,
+# NSPLITs.  24 heads: the 32-head block, which reads the table after each
+# position.  64 and 72 heads: 64-head blocks, which stage a table of up to 512
+# pages in LDS (5000 entries at NSPLIT 1: three staged list chunks, the table
+# restaged for each; 72 heads: a second, partial head block).  600 pages: a
+# table wider than the stage, read after each position.
+PAGED_EDGES = [
+    (24, 150, 12, 40, 30, (1, 3, 0)),
+    (64, 5000, 12, 46, 30, (1, 2, 0)),
+    (72, 300, 12, 46, 30, (1, 3, 0)),
+    (64, 300, 600, 1810, 1700, (1, 3, 0)),
+]
+
+
+@pytest.mark.parametrize("case", PAGED_EDGES, ids=lambda c: f"h{c[0]}k{c[1]}p{c[2]}")
+def test_paged_edges(smla, case):
     """Missing pages, positions beyond the table or negative, rows outside
     the cache, a 16-token page, three sequences of two query tokens."""
     import torch
+    heads, topk, pages_per_seq, n_ids, kv_pages, nsplits = case
     rng = np.random.default_rng(31)
-    page, pages_per_seq, batch, q_len, heads, topk = 16, 12, 3, 2, 24, 150
-    kv_rows = 30 * page  # page ids above 29 point outside the cache
-    inp = flat_inputs("paged_edges", 8100, batch, q_len, heads, kv_rows, topk)
-    table = rng.permutation(40)[: batch * pages_per_seq].reshape(batch, pages_per_seq).astype(np.int32)
+    page, batch, q_len = 16, 3, 2
+    kv_rows = kv_pages * page  # page ids from kv_pages on point outside the cache
+    inp = flat_inputs("paged_edges", 8100, batch, q_len, heads, kv_rows, min(topk, kv_rows))
+    table = rng.permutation(n_ids)[: batch * pages_per_seq].reshape(batch, pages_per_seq).astype(np.int32)
     table[0, 3] = -1
     table[2, :] = -1
     table[2, 5] = 7
@@ -124,7 +140,7 @@ def test_paged_edges(smla):
     t_dev = torch.from_numpy(table).cuda()
     p_dev = torch.from_numpy(pos).cuda()
     o_r, l_r = oracle.decode(inp.q, inp.kv, rows, inp.scale)
-    for nsplit in (1, 3, 0):
+    for nsplit in nsplits:
         out, lse = _outputs(inp, dev["q"].device)
         used = smla.smla_decode_paged(dev["q"], dev["kv"], t_dev, page, p_dev, out, lse, inp.scale,
                                       nsplit)

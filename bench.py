@@ -1,20 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of sparse MLA decode (split-K over the top-k list) on one MI355X.
 
-One step = one smla_decode call (split kernel + LSE-combine kernel) over the
-workload's whole batch, i.e. one attention layer's decode.  Default workload:
-a single request at long context -- batch 1, q_len 1, 8 heads, top-2048 of a
-65536-row 576-wide bf16 latent cache -- with the planner's NSPLIT.
+One step = one smla_decode call (split kernel + LSE-combine kernel when
+NSPLIT > 1) over the workload's whole batch, i.e. one attention layer's
+decode.  Default workload: the large ragged batch -- batch 128, q_len 1, 128
+heads, top-2048 per sequence over contexts uniform in [2048, 131072] in a
+paged pool of 64-token pages (the positions translated to rows by the
+harness) -- with the planner's NSPLIT.
 
 Timing protocol
   * inputs are resident in HBM before timing; successive steps rotate over
     (cache, index set) pairs whose distinct gathered rows exceed 512 MB (2x
     the Infinity Cache), so every step gathers rows from HBM (--warm turns the
-    rotation off: a cache-resident figure, never an HBM one);
-  * steps/s: W warm-up steps, then untimed replays of a HIP graph that holds
-    one rotation cycle for at least --settle seconds (the GPU's clocks ramp
-    up under load over tens of milliseconds), then K steps replayed from that
-    graph, bracketed by device synchronisation;
+    rotation off: a cache-resident figure, never an HBM one).  A workload
+    whose rotation would need more than MAX_ROTATION steps (the tiny one: its
+    whole 1.2 MB cache sits in one XCD's L2) is not rotated and is labelled
+    warm;
+  * steps/s: W warm-up steps, then untimed replays of the timed graph for at
+    least --settle seconds (the GPU's clocks ramp up under load over tens of
+    milliseconds), then exactly K steps -- HIP graphs of consecutive steps of
+    the rotation, at most GRAPH_MAX steps each, replayed back to back --
+    bracketed by device synchronisation;
   * per-kernel durations: an eager loop with HIP events recorded around each
     launch on the launch stream, queued behind a spin kernel so that host
     enqueue time cannot leak into the measured intervals;
@@ -32,9 +38,11 @@ Timing protocol
   * dispatch_floor_us: a graph of back-to-back empty kernel launches, the
     per-launch floor under every step (two launches per step);
   * nsplit_sweep: steps/s and the split kernel's gathered-KV rate of the same
-    workload at each NSPLIT of its sweep (the planner's marked), and, beside
-    a batch-1 workload, the same figures for the batch-64 workload at the
-    planner's NSPLIT ("secondary").
+    workload at each NSPLIT of its sweep (the planner's marked);
+  * secondary: the same figures (steps/s, per-step and split-kernel gathered
+    KV rate and roofline fraction) for every other workload at the planner's
+    NSPLIT, and for the paged workloads with the page tables mapped in the
+    kernel (skipped with --no-secondary or --no-sweep).
 Prints one JSON line.
 """
 from __future__ import annotations
@@ -54,7 +62,9 @@ METRIC = "decode steps/s + gathered-KV HBM GB/s (% of roofline), sparse MLA topk
 HBM_PEAK_GBPS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 ROW_BYTES = 1152
-MIN_GRAPH_STEPS = 32  # steps per captured graph, at least
+MIN_GRAPH_STEPS = 32  # steps per captured graph of the kernel timings, at least
+GRAPH_MAX = 1024      # steps per captured graph of the headline timing, at most
+MAX_ROTATION = 256    # rotation steps, at most (more: the workload runs warm)
 KERNEL_SRC = os.path.join(ROOT, "sparse_mla_decode_amd", "csrc", "smla_kernels.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -79,9 +89,9 @@ def kernel_sha() -> str:
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2048)
-    ap.add_argument("--warmup", type=int, default=64)
-    ap.add_argument("--workload", default="long",
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="ragged",
                     choices=["tiny", "long", "batched", "spec", "ragged", "verify"])
     ap.add_argument("--mode", default="rows", choices=["rows", "paged"],
                     help="paged: positions + page tables mapped in the kernel (batched, ragged)")
@@ -94,7 +104,8 @@ def parse():
     ap.add_argument("--settle", type=float, default=0.3,
                     help="seconds of untimed graph replays before the timed steps")
     ap.add_argument("--no-sweep", action="store_true",
-                    help="skip the NSPLIT sweep, the single-launch figure and the secondary batch-64 figure")
+                    help="skip the NSPLIT sweep, the single-launch and top-k figures and the secondary workloads")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--topk-only", action="store_true",
                     help="only time the top-k producer on the workload's shape (one JSON line) and exit")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -141,17 +152,22 @@ class Workload:
         if self.kind == "paged" and inp.pos is None:
             raise SystemExit(f"--mode paged needs a paged workload (batched, ragged), not {name}")
         self.pos_sets = None
-        if warm:
+        self.warm = warm
+        if not warm:
+            if self.kind == "dense":
+                # no list to vary: rotate over caches whose rows together exceed 512 MB
+                self.sets = [inp.idx]
+                self.n_caches = max(1, -(-(512 << 20) // (inp.kv_rows * ROW_BYTES)))
+            elif self.kind == "paged":
+                self.n_caches, self.sets, self.pos_sets = wl.rotation(inp, positions=True)
+            else:
+                self.n_caches, self.sets = wl.rotation(inp)
+            # a rotation longer than MAX_ROTATION steps (a cache this small
+            # cannot be made cold in any useful sense) is not used
+            self.warm = self.n_caches * len(self.sets) > MAX_ROTATION
+        if self.warm:
             self.n_caches, self.sets = 1, [inp.idx]
             self.pos_sets = [inp.pos] if self.kind == "paged" else None
-        elif self.kind == "dense":
-            # no list to vary: rotate over caches whose rows together exceed 512 MB
-            self.sets = [inp.idx]
-            self.n_caches = max(1, -(-(512 << 20) // (inp.kv_rows * ROW_BYTES)))
-        elif self.kind == "paged":
-            self.n_caches, self.sets, self.pos_sets = wl.rotation(inp, positions=True)
-        else:
-            self.n_caches, self.sets = wl.rotation(inp)
         self.q = wl.bits_to_torch(inp.q).to(dev)
         self.caches = [wl.device_pool(inp.kv_rows, (inp.pool_seed or 0) + 1000 * c, dev)
                        for c in range(self.n_caches)]
@@ -173,11 +189,20 @@ class Workload:
             # every query token of a sequence attends to the same context rows:
             # count each context row once (per query token it would exceed HBM)
             self.valid_rows = [int(np.minimum(inp.ctx, inp.idx.shape[-1]).sum())]
-        self.mean_kv_bytes = sum(self.valid_rows[(i // self.n_caches) % len(self.sets)] * ROW_BYTES
-                                 for i in range(self.n_rot)) / self.n_rot
+        self.mean_kv_bytes = self.kv_bytes(0, self.n_rot)
         self.stream = torch.cuda.Stream()
         self.ws = {}
         torch.cuda.synchronize()
+
+    def kv_bytes(self, first, n):
+        """Mean gathered-KV bytes per step over steps first .. first + n - 1."""
+        return sum(self.valid_rows[(i // self.n_caches) % len(self.sets)] * ROW_BYTES
+                   for i in range(first, first + n)) / n
+
+    def flops(self):
+        """Algorithmic flops of one step: tokens x heads x valid entries x 2 x (576 + 512)."""
+        valid = self.valid_rows[0] if self.kind != "dense" else self.valid_rows[0] * self.Lq
+        return self.H * valid * 2 * (576 + 512)
 
     def plan(self):
         if self.kind == "dense":
@@ -218,10 +243,12 @@ class Workload:
 
     def fused_fn(self, nsplit):
         ws = self.workspace(nsplit)
+        sync = self.smla.fused_sync(self.dev)
 
         def f(i):
             c, ix = self._args(i)
-            self.smla.smla_decode_fused(self.q, c, ix, self.out, self.lse, self.inp.scale, nsplit, ws)
+            self.smla.smla_decode_fused(self.q, c, ix, self.out, self.lse, self.inp.scale, nsplit, ws,
+                                        sync=sync)
         return f
 
     def split_fn(self, nsplit):
@@ -239,20 +266,46 @@ class Workload:
             self.smla.smla_combine(part[0], part[1], self.out, self.lse)
         return f
 
-    def graph_of(self, fn):
-        """graph_len calls fn(i) (whole rotation cycles) captured in a HIP graph."""
+    def graph_of(self, fn, n=None, first=0):
+        """n calls fn(first), fn(first + 1), ... captured in a HIP graph (by
+        default graph_len calls: whole rotation cycles)."""
         torch = self.torch
+        n = self.graph_len if n is None else n
         torch.cuda.synchronize()
         self.stream.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(self.stream):
             with torch.cuda.graph(g, stream=self.stream):
-                for i in range(self.graph_len):
+                for i in range(first, first + n):
                     fn(i)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
         return g
+
+    def time_exact(self, fn, steps, settle):
+        """Microseconds per step over exactly `steps` consecutive steps of the
+        rotation: graphs of at most GRAPH_MAX steps replayed back to back
+        between two events (after `settle` seconds of untimed replays)."""
+        torch = self.torch
+        graphs, first = [], 0
+        while first < steps:
+            n = min(GRAPH_MAX, steps - first)
+            graphs.append(self.graph_of(fn, n, first))
+            first += n
+        t0 = time.time()
+        while time.time() - t0 < settle:
+            for g in graphs:
+                g.replay()
+            torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for g in graphs:
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return 1e3 * a.elapsed_time(b) / steps
 
     def time_graph(self, g, min_launches):
         """Mean microseconds per captured call over whole-cycle replays."""
@@ -293,12 +346,21 @@ class Workload:
         self.settle(g, settle)
         step_us, n = self.time_graph(g, steps)
         split_us = self.split_time(nsplit, kernel_steps, step_us)
+        kv = self.mean_kv_bytes
         return {"nsplit": nsplit, "us_per_step": round(step_us, 3), "steps_per_s": round(1e6 / step_us, 2),
-                "gathered_kv_gbps_per_step": round(self.mean_kv_bytes / (step_us * 1e-6) / 1e9, 2),
+                "mfma_frac_split": round(self.flops() / (split_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                "gathered_kv_gbps_per_step": round(kv / (step_us * 1e-6) / 1e9, 2),
+                "roofline_frac_per_step": round(kv / (step_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
                 "split_us": round(split_us, 3),
-                "split_kv_gbps": round(self.mean_kv_bytes / (split_us * 1e-6) / 1e9, 2),
-                "split_roofline_frac": round(self.mean_kv_bytes / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
-                "steps_timed": n}
+                "split_kv_gbps": round(kv / (split_us * 1e-6) / 1e9, 2),
+                "split_roofline_frac": round(kv / (split_us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+                "kv_bytes_per_step": int(kv), "steps_timed": n,
+                "cache_state": self.cache_state()}
+
+    def cache_state(self):
+        if self.warm:
+            return "warm: one input set, no rotation (cache-resident)"
+        return f"cold: rotation over {self.n_caches} caches x {len(self.sets)} disjoint index sets"
 
 
 def topk_figure(w, steps):
@@ -375,17 +437,20 @@ def main():
     step = w.step_fn(nsplit)
     log(f"[bench] setup {time.time() - t_setup:.1f}s nsplit={nsplit} rotation={w.n_rot} steps")
 
-    # ---- warm-up (eager), then the timed region: K steps from replays of a
-    # HIP graph holding one rotation cycle
+    # ---- warm-up (eager), then the timed region: exactly K consecutive steps
+    # of the rotation, replayed from HIP graphs
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    graph = w.graph_of(step)
-    w.settle(graph, args.settle)
-    us_per_step, steps = w.time_graph(graph, args.steps)
+    steps = args.steps
+    us_per_step = w.time_exact(step, steps, args.settle)
     ms_per_step = us_per_step * 1e-3
     steps_per_s = 1e6 / us_per_step
-    log(f"[bench] graph: {steps} steps -> {us_per_step:.2f} us/step")
+    log(f"[bench] timed: {steps} steps -> {us_per_step:.2f} us/step")
+    # the same steps as whole rotation cycles of a graph of at least
+    # MIN_GRAPH_STEPS steps, over many more launches (a steadier figure)
+    long_us, long_n = w.time_graph(w.graph_of(step), max(args.kernel_steps, 256))
+    log(f"[bench] whole-cycle graph replays: {long_n} steps -> {long_us:.2f} us/step")
 
     # ---- per-kernel durations (a): each kernel alone, one rotation cycle of
     # back-to-back launches per HIP graph, timed with events around replays
@@ -400,7 +465,7 @@ def main():
         log(f"[bench] topk producer: {topk['us_per_call']:.2f} us per call ({topk['rows']} rows x "
             f"{topk['positions_per_row']} positions, k={topk['topk']}, {topk['gbps']:.0f} GB/s of scores)")
     if not args.no_sweep and w.fused_in_launch(nsplit):
-        fused_us = w.time_graph(w.graph_of(w.fused_fn(nsplit)), args.steps)[0]
+        fused_us = w.time_graph(w.graph_of(w.fused_fn(nsplit)), max(args.steps, 256))[0]
         single_launch = {"us_per_step": round(fused_us, 3), "steps_per_s": round(1e6 / fused_us, 2),
                          "entry_point": "smla_decode_fused",
                          "method": "graph replay of smla_decode_fused steps (one kernel per step)"}
@@ -427,20 +492,20 @@ def main():
         f"(event-bracketed: split {ev_split_us:.2f} us, combine {ev_comb_us:.2f} us, eager step {eager_us:.2f} us)")
 
     kv_split = w.mean_kv_bytes
-    flops = T * H * K * 2 * (576 + 512) * (int((w.sets[0] >= 0).sum()) / max(1, T * K))
+    kv_timed = w.kv_bytes(0, steps)  # the K timed steps' mean
+    flops = w.flops()
     achieved = kv_split / (split_us * 1e-6) / 1e9
     traffic = None
     mfma_counters = None  # the profile's MFMA counters, while it matches this kernel
+    prof_avg_ns = None    # the profile's trace-average split duration, likewise
     if os.path.exists(TRAFFIC_FILE):
-        key = args.workload + (str(args.spec_ctx) if args.workload in ("spec", "verify") else "") + \
-            ("_paged" if w.kind == "paged" else "")
-        rec = json.load(open(TRAFFIC_FILE)).get(key)
-        if rec and rec.get("kernel_sha") == kernel_sha() and rec.get("nsplit") == nsplit and not args.warm:
+        rec = json.load(open(TRAFFIC_FILE)).get(profile_key(args.workload, args.spec_ctx, w.kind))
+        if rec and rec.get("kernel_sha") == kernel_sha() and rec.get("nsplit") == nsplit and not w.warm:
             traffic = rec.get("bytes_per_launch")
             mfma_counters = rec
+            prof_avg_ns = rec.get("split_trace_avg_ns")
 
-    # ---- NSPLIT sweep of the same workload, and the batch-64 workload at the
-    # planner's NSPLIT beside a batch-1 headline (graph timing only)
+    # ---- NSPLIT sweep of the same workload (graph timing only)
     sweep = []
     if not args.no_sweep:
         for ns in SWEEPS[args.workload] + ([] if nsplit in SWEEPS[args.workload] else [nsplit]):
@@ -448,16 +513,23 @@ def main():
                               planner=(ns == w.plan())))
             log(f"[bench] sweep nsplit={ns}: {sweep[-1]['us_per_step']:.2f} us/step, "
                 f"split {sweep[-1]['split_us']:.2f} us")
+    # ---- every other workload at the planner's NSPLIT (graph timing only)
     secondary = {}
-    if not args.no_sweep and args.workload in ("long", "tiny", "spec") and w.kind == "rows":
-        w2 = Workload("batched", args.spec_ctx, args.warm, dev)
-        ns2 = w2.plan()
-        secondary["batched"] = dict(w2.summary(ns2, 512, 256), planner=True,
-                                    workload="batched: " + DESCRIPTIONS["batched"])
-        log(f"[bench] batched (planner nsplit={ns2}): {secondary['batched']['us_per_step']:.2f} us/step, "
-            f"split {secondary['batched']['split_us']:.2f} us")
-        del w2
-        torch.cuda.empty_cache()
+    if not args.no_sweep and not args.no_secondary:
+        for name, mode in secondary_list(args.workload, w.kind):
+            t0 = time.time()
+            w2 = Workload(name, args.spec_ctx, args.warm, dev, mode)
+            ns2 = w2.plan()
+            key = name + ("_paged" if mode == "paged" else "")
+            desc = DESCRIPTIONS[name].format(ctx=args.spec_ctx) + \
+                ("; positions mapped through page tables in the kernel" if mode == "paged" else "")
+            secondary[key] = dict(w2.summary(ns2, 512, 256), planner=True, workload=f"{name}: {desc}",
+                                  entry_point=ENTRY[w2.kind])
+            log(f"[bench] secondary {key} (planner nsplit={ns2}): {secondary[key]['us_per_step']:.2f} us/step, "
+                f"split {secondary[key]['split_us']:.2f} us ({secondary[key]['split_roofline_frac']:.3f} of HBM), "
+                f"{time.time() - t0:.1f} s")
+            del w2
+            torch.cuda.empty_cache()
 
     result = {
         "metric": METRIC,
@@ -475,15 +547,16 @@ def main():
         "config": {
             "workload": f"{args.workload}: " + DESCRIPTIONS[args.workload].format(ctx=args.spec_ctx)
                         + ("; positions mapped through page tables in the kernel" if w.kind == "paged" else ""),
-            "entry_point": {"rows": "smla_decode", "paged": "smla_decode_paged",
-                            "dense": "smla_decode_dense"}[w.kind],
+            "entry_point": ENTRY[w.kind],
             "batch": B, "q_len": Lq, "heads": H, "topk": K, "kv_rows": w.inp.kv_rows,
             "nsplit": nsplit, "nsplit_from": "planner" if args.nsplit == 0 else "argument",
-            "cache_state": "warm (no rotation)" if args.warm else
-                           f"cold: rotation over {w.n_caches} caches x {len(w.sets)} disjoint index sets",
-            "timing": f"HIP graph replay of whole rotation cycles, after {args.settle:g} s of untimed replays",
+            "cache_state": w.cache_state(),
+            "timing": (f"exactly {steps} consecutive steps replayed from HIP graphs of at most {GRAPH_MAX} "
+                       f"steps, after {args.settle:g} s of untimed replays"),
         },
-        "gathered_kv_gbps_per_step": round(w.mean_kv_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "gathered_kv_gbps_per_step": round(kv_timed / (ms_per_step * 1e-3) / 1e9, 2),
+        "whole_cycle_timing": {"us_per_step": round(long_us, 3), "steps": long_n,
+                               "method": f"graph of {w.graph_len} steps (whole rotation cycles) replayed"},
         "kernels_us": {"split": round(split_us, 3), "combine": round(comb_us, 3),
                        "method": ("graph of back-to-back launches of one kernel, events around replays"
                                   if rows_mode else
@@ -500,6 +573,13 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": traffic,
             "bytes_per_launch": int(kv_split),
+            "launch_us": round(split_us, 3),
+            "launch_timing": "mean per launch over graph replays of back-to-back split launches (HIP events "
+                             "on the launch stream)",
+            "frac_per_step": round(kv_timed / (us_per_step * 1e-6) / 1e9 / HBM_PEAK_GBPS, 4),
+            "frac_from_profile": (None if not prof_avg_ns else
+                                  round(kv_split / (prof_avg_ns * 1e-9) / 1e9 / HBM_PEAK_GBPS, 4)),
+            "profile_avg_us": None if not prof_avg_ns else round(prof_avg_ns * 1e-3, 3),
             "bytes": ("context rows x 1152 B, each row once (all query tokens share them)"
                       if w.kind == "dense" else "valid list entries x 1152 B"),
         },
@@ -532,6 +612,22 @@ def main():
     if args.cpu_seconds > 0:
         result["cpu_baseline"] = cpu_baseline(w.inp, w.caches[0], torch.from_numpy(w.sets[0]), args.cpu_seconds)
     print(json.dumps(result), flush=True)
+
+
+ENTRY = {"rows": "smla_decode", "paged": "smla_decode_paged", "dense": "smla_decode_dense"}
+
+
+def profile_key(name, spec_ctx, kind):
+    """Key of a workload's record in profiles/traffic.json."""
+    return name + (str(spec_ctx) if name in ("spec", "verify") else "") + ("_paged" if kind == "paged" else "")
+
+
+def secondary_list(head, head_kind):
+    """(workload, mode) of every figure besides the headline one."""
+    figs = [(n, "rows") for n in ("tiny", "long", "batched", "spec", "ragged", "verify")]
+    figs += [("batched", "paged"), ("ragged", "paged")]
+    head_mode = "paged" if head_kind == "paged" else "rows"
+    return [f for f in figs if f != (head, head_mode)]
 
 
 def dispatch_floor_us(n=256):

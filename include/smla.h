@@ -30,28 +30,22 @@
  *   topk_idx   [batch, q_len, topk]         int32 physical row indices
  *   out        [batch, q_len, heads, 512]   bf16
  *   lse        [batch, q_len, heads]        fp32
- *   workspace  SMLA_WS_SYNC_BYTES of synchronisation words (below), then
- *              part_o [T, NSPLIT, heads, 512] fp32 at byte offset
- *              SMLA_WS_SYNC_BYTES, then part_lse [T, NSPLIT, heads] fp32 at
- *              byte offset smla_workspace_lse_offset; T = batch * q_len.
- *              The first SMLA_WS_SYNC_BYTES must be zero before the
- *              workspace's first decode call; every decode call leaves them
- *              zero again, whatever its shape, so a workspace zeroed once
- *              serves any sequence of calls.  smla_split and smla_combine do
- *              not touch them.
+ *   workspace  part_o [T, NSPLIT, heads, 512] fp32 at byte offset 0, then
+ *              part_lse [T, NSPLIT, heads] fp32 at byte offset
+ *              smla_workspace_lse_offset (256-byte aligned); T = batch * q_len.
+ *              Scratch: any content on entry; after a call with NSPLIT > 1
+ *              it holds that call's partials.
  * q, kv_cache, out and workspace must be 16-byte aligned; topk_idx and lse
  * 4-byte aligned.
  *
  * Ownership and execution.  The caller owns every buffer, including the
  * workspace; the library allocates no device memory and keeps no per-call
- * state (its globals are a per-device cache of the CU count and the
- * smla_set_merge_polls and smla_set_topk_min_chunks settings).  Work is
+ * state (its only global is a per-device cache of the CU count).  Work is
  * enqueued on `hip_stream` (a hipStream_t; NULL = the legacy default stream)
  * and the call returns without waiting for it: buffers must stay alive and
  * unmodified until the stream has passed the call.  The calls never
  * synchronise the host, so they can be captured into a HIP graph.  Calls on
- * different streams that share a workspace race (the synchronisation words
- * included: such calls may also wait out their bounded polls, below).
+ * different streams that share a workspace race.
  *
  * Errors.  Every entry point returns SMLA_OK (0) or a negative smla_status.
  * Arguments are validated before anything is enqueued; on an error nothing is
@@ -86,8 +80,8 @@ enum smla_status {
 #define SMLA_MAX_NSPLIT 1024  /* largest NSPLIT accepted */
 #define SMLA_MAX_HEADS 4096   /* largest head count accepted */
 #define SMLA_MAX_TOPK (1 << 24)
-#define SMLA_WS_SYNC_BYTES 16384  /* head of every workspace: single-launch combine words */
-#define SMLA_FUSED_MAX_NSPLIT 64  /* largest NSPLIT merged inside the split launch */
+#define SMLA_FUSED_SYNC_BYTES 16384  /* synchronisation words of smla_decode_fused */
+#define SMLA_FUSED_MAX_NSPLIT 64     /* largest NSPLIT merged inside the split launch */
 
 /*
  * NSPLIT the planner picks for a call of this shape on the current device
@@ -124,16 +118,6 @@ size_t smla_workspace_lse_offset(int batch, int q_len, int heads, int nsplit);
 int smla_fused_in_launch(int batch, int q_len, int heads, int nsplit);
 
 /*
- * Bound on the polls (each a short sleep and one device-scope load) of a
- * workgroup that waits for the other partials of its unit in the
- * single-launch merge of smla_decode_fused; default 2048.  0 = never wait:
- * the last workgroup to arrive merges the whole unit (same results, bit for
- * bit).  Process-wide; applies to calls made after it.  Returns the previous
- * value, or SMLA_ERR_DIM if polls < 0.
- */
-int smla_set_merge_polls(int polls);
-
-/*
  * Full decode: the split kernel over every (token, split) and, when
  * NSPLIT > 1, the combine kernel (smla_combine).  nsplit == 0 asks the planner
  * (smla_plan_nsplit); size the workspace with smla_workspace_bytes for the
@@ -149,25 +133,36 @@ int smla_decode(const void *q, const void *kv_cache, const int32_t *topk_idx, vo
  * smla_decode with the log-sum-exp merge inside the split launch (one kernel
  * instead of two; "The Split-K Imperative": the partials of the slices are
  * merged by log-sum-exp), when 2 <= NSPLIT <= SMLA_FUSED_MAX_NSPLIT,
- * tokens * head blocks <= SMLA_WS_SYNC_BYTES / 16 (head blocks of 16, 32 or
- * 64 heads, by head count) and the grid fits the device's resident
- * workgroups (smla_fused_in_launch); otherwise exactly smla_decode.  The
- * NSPLIT workgroups of a (token, head block) write their partials with
- * device-coherent stores and take tickets on counters in the workspace's
- * synchronisation words; those that see every partial written merge one
- * slice of the output each, and the last to arrive merges the slices of any
- * that stopped waiting (each waits a bounded number of polls,
- * smla_set_merge_polls), so no wait is unbounded even on a shared device.
+ * tokens * head blocks <= SMLA_FUSED_SYNC_BYTES / 16 (head blocks of 16, 32
+ * or 64 heads, by head count) and the grid fits the device's resident
+ * workgroups (smla_fused_in_launch); otherwise exactly smla_decode (the
+ * sync words are then not touched).
+ *   sync [SMLA_FUSED_SYNC_BYTES] (4-byte aligned): synchronisation words of
+ *     the in-launch merge, owned by the caller.  They must be zero before
+ *     their first use and every call leaves them zero, whatever its shape,
+ *     so one zeroed buffer serves any sequence of calls on one stream.  May
+ *     be NULL when the call does not merge in the launch.
+ *   merge_polls (>= 0): bound on the polls (each a short sleep and one
+ *     device-scope load) of a workgroup waiting for the other partials of
+ *     its unit; 0 = never wait, the last workgroup to arrive merges the
+ *     whole unit (same results, bit for bit).  2048 is a good default.
+ * The NSPLIT workgroups of a (token, head block) write their partials with
+ * device-coherent stores, then take a ticket with an agent-scope release;
+ * a workgroup that sees every ticket out (an agent-scope acquire) merges
+ * one slice of the output, and the last to arrive merges the slices of any
+ * that stopped waiting, so no wait is unbounded even on a shared device.
  * Same arithmetic as smla_combine; the merge order within a slice is fixed,
  * so results repeat bit for bit.  On MI355X this form is slower than the two
  * launches of smla_decode (its cross-XCD handoffs cost more than a kernel
- * boundary); it serves callers that need a single launch.  Arguments,
- * workspace size and errors as smla_decode.
+ * boundary); it serves callers that need a single launch.  Other arguments,
+ * the workspace and the errors as smla_decode; SMLA_ERR_NULL if the call
+ * merges in the launch and sync is NULL, SMLA_ERR_WORKSPACE if sync_bytes <
+ * SMLA_FUSED_SYNC_BYTES, SMLA_ERR_DIM if merge_polls < 0.
  */
 int smla_decode_fused(const void *q, const void *kv_cache, const int32_t *topk_idx, void *out,
                       float *lse, float scale, int nsplit, int batch, int q_len, int heads,
                       int topk, int64_t kv_rows, void *workspace, size_t workspace_bytes,
-                      void *hip_stream);
+                      uint32_t *sync, size_t sync_bytes, int merge_polls, void *hip_stream);
 
 /*
  * smla_decode over a paged cache, with the page-table lookup done in the
@@ -268,30 +263,28 @@ int smla_combine(const float *part_o, const float *part_lse, void *out, float *l
  * ctx_len and out_pos 4-byte aligned; scores may be NULL when max_ctx == 0.
  * batch, q_len or topk 0 launch nothing.
  *
- * Work split.  Without a workspace (NULL, or smaller than
- * smla_topk_workspace_bytes) one workgroup selects each row.  With one, and
- * when there are fewer rows than twice the CUs and a row spans at least
- * smla_set_topk_min_chunks chunks of 4096 positions (default 12), each row
- * is also cut into chunks over several workgroups (four launches: chunk
- * histograms, a row scan, candidate lists in position order, the
- * selection); same output.  The workspace (256-byte aligned) is
- * scratch: any content on entry, nothing kept after the call.
- * Errors as smla_decode (SMLA_ERR_DEVICE only when a workspace is given and
- * the CU count cannot be read).
+ * Work split (`form`).  SMLA_TOPK_ROWS: one workgroup selects each row.
+ * SMLA_TOPK_CHUNKS: when a workspace of smla_topk_workspace_bytes is given
+ * and a row spans at least two chunks of 4096 positions, each row is cut
+ * into chunks over several workgroups (four launches: chunk histograms, a
+ * row scan, candidate lists in position order, the selection), else as
+ * SMLA_TOPK_ROWS.  SMLA_TOPK_AUTO: the chunked form when it was measured
+ * faster (a workspace is given, there are fewer rows than twice the CUs and
+ * a row spans at least 12 chunks), else one workgroup per row.  Every form
+ * gives the same output.  The workspace (256-byte aligned) is scratch: any
+ * content on entry, nothing kept after the call.
+ * Errors as smla_decode (SMLA_ERR_DEVICE only when SMLA_TOPK_AUTO with a
+ * workspace needs the CU count and it cannot be read; SMLA_ERR_DIM for an
+ * unknown form).
  */
 int smla_topk(const float *scores, const int32_t *ctx_len, int batch, int q_len, int max_ctx,
-              int topk, int32_t *out_pos, void *workspace, size_t workspace_bytes,
+              int topk, int32_t *out_pos, void *workspace, size_t workspace_bytes, int form,
               void *hip_stream);
+
+enum smla_topk_form { SMLA_TOPK_AUTO = 0, SMLA_TOPK_ROWS = 1, SMLA_TOPK_CHUNKS = 2 };
 
 /* Bytes of workspace for smla_topk's multi-workgroup form. */
 size_t smla_topk_workspace_bytes(int batch, int q_len, int max_ctx);
-
-/*
- * The chunk count from which smla_topk cuts rows over several workgroups
- * (0 = never).  Process-wide; applies to calls made after it.  Returns the
- * previous value, or SMLA_ERR_DIM if min_chunks < 0.
- */
-int smla_set_topk_min_chunks(int min_chunks);
 
 /* Static description of a status code (never NULL). */
 const char *smla_status_str(int status);

@@ -20,11 +20,6 @@ static_assert(SMLA_ROW == smla::kRow && SMLA_DV == smla::kDV, "widths out of syn
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];  // 0 = not queried yet
 
-// bound on the polls of a workgroup waiting for its unit's partials in the
-// single-launch merge (each poll: a short sleep and one device-scope load)
-constexpr int kDefaultMergePolls = 2048;
-std::atomic<int> g_merge_polls{kDefaultMergePolls};
-
 // CU count of the current device, queried once per device.
 int device_cus(int* cus) {
   int dev = 0;
@@ -61,11 +56,9 @@ bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0;
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// workspace: [0, SMLA_WS_SYNC_BYTES) single-launch combine words, then part_o,
-// then part_lse
+// workspace: part_o at offset 0, then part_lse at a 256-byte boundary
 size_t lse_offset(int64_t tokens, int heads, int nsplit) {
-  return SMLA_WS_SYNC_BYTES +
-         round_up((size_t)tokens * nsplit * heads * SMLA_DV * sizeof(float), 256);
+  return round_up((size_t)tokens * nsplit * heads * SMLA_DV * sizeof(float), 256);
 }
 
 size_t ws_bytes(int64_t tokens, int heads, int nsplit) {
@@ -95,8 +88,8 @@ bool dense_folds(int q_len, int heads, int max_ctx) {
 }
 
 // Whether a decode call with NSPLIT > 1 merges inside the split launch: its
-// (token, head block) units fit the workspace's sync words, NSPLIT fits the
-// 64-bit claim mask, and the grid fits the device's resident workgroups.
+// (token, head block) units fit the sync words (16 bytes each), NSPLIT fits
+// the 64-bit claim mask, and the grid fits the device's resident workgroups.
 int single_launch(int64_t tokens, int heads, int nsplit, int* single) {
   *single = 0;
   if (nsplit < 2 || nsplit > SMLA_FUSED_MAX_NSPLIT) return SMLA_OK;
@@ -105,20 +98,29 @@ int single_launch(int64_t tokens, int heads, int nsplit, int* single) {
   if (rc != SMLA_OK) return rc;
   const int hpb = smla::split_heads_per_block(heads);
   const int64_t units = tokens * ((heads + hpb - 1) / hpb);
-  *single = units <= SMLA_WS_SYNC_BYTES / 16 &&
+  *single = units <= SMLA_FUSED_SYNC_BYTES / 16 &&
             nsplit * units <= (int64_t)cus * smla::split_blocks_per_cu(heads);
   return SMLA_OK;
 }
 
+// The single-launch merge's arguments (smla_decode_fused).
+struct Fused {
+  uint32_t* sync = nullptr;
+  size_t sync_bytes = 0;
+  int merge_polls = 0;
+};
+
 // Shared by every decode entry point (combine = true) and smla_split
-// (combine = false); fused: merge inside the split launch when single_launch
-// allows it.  topk is the list length (the longest context when dense).
+// (combine = false); fused (non-null): merge inside the split launch when
+// single_launch allows it.  topk is the list length (the longest context
+// when dense).
 int run(const void* q, const void* kv, const Source& so, void* out, float* lse, float scale,
         int nsplit, int batch, int q_len, int heads, int topk, int64_t kv_rows, void* ws,
-        size_t ws_size, void* stream, bool combine, bool fused = false) {
+        size_t ws_size, void* stream, bool combine, const Fused* fused = nullptr) {
   if (!dims_ok(batch, q_len, heads, topk) || kv_rows < 0) return SMLA_ERR_DIM;
   if (so.table && (so.page_size < 1 || so.max_pages < 0)) return SMLA_ERR_DIM;
   if (nsplit < 0 || nsplit > SMLA_MAX_NSPLIT) return SMLA_ERR_NSPLIT;
+  if (fused && fused->merge_polls < 0) return SMLA_ERR_DIM;
   const int64_t tokens = (int64_t)batch * q_len;
   if (tokens == 0) return SMLA_OK;  // nothing to compute, nothing written
 
@@ -162,7 +164,7 @@ int run(const void* q, const void* kv, const Source& so, void* out, float* lse, 
   sp.q_len = q_len;
   sp.out = (uint16_t*)out;
   sp.lse = lse;
-  sp.part_o = partials ? (float*)((char*)ws + SMLA_WS_SYNC_BYTES) : nullptr;
+  sp.part_o = partials ? (float*)ws : nullptr;
   sp.part_lse = partials ? (float*)((char*)ws + lse_offset(tokens, heads, nsplit)) : nullptr;
   sp.kv_rows = kv_rows;
   sp.tokens = (int)tokens;
@@ -175,13 +177,19 @@ int run(const void* q, const void* kv, const Source& so, void* out, float* lse, 
   // be resident at once (so none waits on one that has not started) and the
   // unit count and NSPLIT fit the workspace's sync words; else a second launch
   sp.sync = nullptr;
+  sp.merge_polls = 0;
   if (partials && combine && fused) {
     int single = 0;
     const int rc = single_launch(tokens, heads, nsplit, &single);
     if (rc != SMLA_OK) return rc;
-    if (single) sp.sync = (uint32_t*)ws;
+    if (single) {
+      if (!fused->sync) return SMLA_ERR_NULL;
+      if (!aligned(fused->sync, 4)) return SMLA_ERR_ALIGN;
+      if (fused->sync_bytes < SMLA_FUSED_SYNC_BYTES) return SMLA_ERR_WORKSPACE;
+      sp.sync = fused->sync;
+      sp.merge_polls = fused->merge_polls;
+    }
   }
-  sp.merge_polls = g_merge_polls.load(std::memory_order_relaxed);
   if (smla::launch_split(sp, st) != hipSuccess) {
     (void)hipGetLastError();
     return SMLA_ERR_LAUNCH;
@@ -245,11 +253,6 @@ SMLA_API size_t smla_workspace_bytes(int batch, int q_len, int heads, int nsplit
   return ws_bytes((int64_t)batch * q_len, heads, nsplit);
 }
 
-SMLA_API int smla_set_merge_polls(int polls) {
-  if (polls < 0) return SMLA_ERR_DIM;
-  return g_merge_polls.exchange(polls, std::memory_order_relaxed);
-}
-
 SMLA_API int smla_fused_in_launch(int batch, int q_len, int heads, int nsplit) {
   if (batch < 0 || q_len < 0 || heads < 1 || heads > SMLA_MAX_HEADS) return SMLA_ERR_DIM;
   if (nsplit < 1 || nsplit > SMLA_MAX_NSPLIT) return SMLA_ERR_NSPLIT;
@@ -276,11 +279,16 @@ SMLA_API int smla_decode(const void* q, const void* kv_cache, const int32_t* top
 SMLA_API int smla_decode_fused(const void* q, const void* kv_cache, const int32_t* topk_idx,
                                void* out, float* lse, float scale, int nsplit, int batch,
                                int q_len, int heads, int topk, int64_t kv_rows, void* workspace,
-                               size_t workspace_bytes, void* hip_stream) {
+                               size_t workspace_bytes, uint32_t* sync, size_t sync_bytes,
+                               int merge_polls, void* hip_stream) {
   Source so;
   so.idx = topk_idx;
+  Fused fu;
+  fu.sync = sync;
+  fu.sync_bytes = sync_bytes;
+  fu.merge_polls = merge_polls;
   return run(q, kv_cache, so, out, lse, scale, nsplit, batch, q_len, heads, topk, kv_rows,
-             workspace, workspace_bytes, hip_stream, true, true);
+             workspace, workspace_bytes, hip_stream, true, &fu);
 }
 
 SMLA_API int smla_decode_paged(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -360,15 +368,8 @@ SMLA_API int smla_combine(const float* part_o, const float* part_lse, void* out,
 // alone leave CUs idle and rows are long (measured: 1 x 65536 and 128 rows
 // up to 131072 gain, 64 x 32768 loses)
 constexpr int kTopkMultiMinChunks = 12;  // 45057 positions and more
-std::atomic<int> g_topk_min_chunks{kTopkMultiMinChunks};
-bool topk_multi(int64_t rows, int max_ctx, int cus) {
-  const int m = g_topk_min_chunks.load(std::memory_order_relaxed);
-  return m > 0 && rows < 2 * (int64_t)cus && smla::topk_chunks(max_ctx) >= m;
-}
-
-SMLA_API int smla_set_topk_min_chunks(int min_chunks) {
-  if (min_chunks < 0) return SMLA_ERR_DIM;
-  return g_topk_min_chunks.exchange(min_chunks, std::memory_order_relaxed);
+bool topk_multi_auto(int64_t rows, int max_ctx, int cus) {
+  return rows < 2 * (int64_t)cus && smla::topk_chunks(max_ctx) >= kTopkMultiMinChunks;
 }
 
 SMLA_API size_t smla_topk_workspace_bytes(int batch, int q_len, int max_ctx) {
@@ -378,8 +379,10 @@ SMLA_API size_t smla_topk_workspace_bytes(int batch, int q_len, int max_ctx) {
 
 SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, int q_len,
                        int max_ctx, int topk, int32_t* out_pos, void* workspace,
-                       size_t workspace_bytes, void* hip_stream) {
+                       size_t workspace_bytes, int form, void* hip_stream) {
   if (batch < 0 || q_len < 0 || max_ctx < 0 || topk < 0 || topk > SMLA_MAX_TOPK)
+    return SMLA_ERR_DIM;
+  if (form != SMLA_TOPK_AUTO && form != SMLA_TOPK_ROWS && form != SMLA_TOPK_CHUNKS)
     return SMLA_ERR_DIM;
   const int64_t rows = (int64_t)batch * q_len;
   if (rows == 0 || topk == 0) return SMLA_OK;
@@ -398,12 +401,16 @@ SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, i
   tp.ws = nullptr;
   tp.ws_row_bytes = smla::topk_ws_row_bytes(max_ctx);
   tp.chunks = smla::topk_chunks(max_ctx);
-  if (workspace && workspace_bytes >= (size_t)rows * tp.ws_row_bytes &&
-      rows * tp.chunks <= 0x7fffffffLL) {
-    int cus = 0;
-    const int rc = device_cus(&cus);
-    if (rc != SMLA_OK) return rc;
-    if (topk_multi(rows, max_ctx, cus)) tp.ws = workspace;
+  if (form != SMLA_TOPK_ROWS && workspace && workspace_bytes >= (size_t)rows * tp.ws_row_bytes &&
+      rows * tp.chunks <= 0x7fffffffLL && tp.chunks >= 2) {
+    if (form == SMLA_TOPK_CHUNKS) {
+      tp.ws = workspace;
+    } else {
+      int cus = 0;
+      const int rc = device_cus(&cus);
+      if (rc != SMLA_OK) return rc;
+      if (topk_multi_auto(rows, max_ctx, cus)) tp.ws = workspace;
+    }
   }
   if (smla::launch_topk(tp, (hipStream_t)hip_stream) != hipSuccess) {
     (void)hipGetLastError();

@@ -164,19 +164,24 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
 // Single-launch combine ([SPLITK] "The Split-K Imperative": the partials of
 // the NSPLIT slices are merged by log-sum-exp; here the split workgroups do
 // it themselves instead of a second launch).  The NSPLIT workgroups of a
-// unit (token, head block) share four words in the caller's workspace,
+// unit (token, head block) share four words in the caller's sync buffer,
 // zero between calls: arrive, depart and a 64-bit claim mask.
 //   1. Each workgroup writes its partial with device-coherent stores, waits
-//      until they have completed, and takes an arrival ticket.
+//      until they have completed, passes a workgroup barrier, and takes an
+//      arrival ticket with an agent-scope release (acquire too: the last
+//      arriver reads the others' partials).
 //   2. A workgroup waits, with a bounded number of polls, until all NSPLIT
-//      tickets are out (the last arriver does not wait), then claims its
-//      own slice of the unit's output (claim bit = its split index) and
-//      merges it from the NSPLIT partials.
+//      tickets are out (the last arriver does not wait), takes an
+//      agent-scope acquire fence, then claims its own slice of the unit's
+//      output (claim bit = its split index) and merges it from the NSPLIT
+//      partials.
 //   3. The last arriver then claims every slice still unclaimed and merges
 //      those too: slices of workgroups that gave up waiting (which happens
 //      only if the unit's workgroups are not resident together), so every
 //      slice is merged exactly once and no wait is unbounded.
-//   4. The last workgroup to depart clears the four words for the next call.
+//   4. Each workgroup departs with an agent-scope release; the last to
+//      depart takes an acquire fence and clears the four words for the next
+//      call.
 // A slice is a contiguous range of the unit's (head, 4-column) quads; its
 // merge is the combine kernel's arithmetic: a running maximum over the
 // splits' LSE, weights exp(LSE_s - max), empty splits (LSE = -inf) weight 0.
@@ -302,12 +307,18 @@ __device__ __forceinline__ void fused_combine(const SplitParams& p, int unit, in
   wait_vmcnt<0>();
   __syncthreads();
   if (tid == 0) {
-    const uint32_t t = __hip_atomic_fetch_add(sy, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // release: this workgroup's partial stores (every wave's, ordered before
+    // this by the barrier) happen before the ticket; acquire: the last
+    // arriver's loads of the others' partials happen after their tickets
+    const uint32_t t = __hip_atomic_fetch_add(sy, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     bool ready = t == S - 1;
     for (int i = 0; !ready && i < p.merge_polls; ++i) {
       __builtin_amdgcn_s_sleep(4);
       ready = __hip_atomic_load(sy, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= S;
     }
+    // the poll saw every ticket: the partials' stores happen before the
+    // merge's loads (the workgroup barrier below extends this to every wave)
+    if (ready && t != S - 1) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     uint32_t own = 0;
     if (ready) {
       const uint32_t bit = 1u << (split & 31);
@@ -341,10 +352,11 @@ __device__ __forceinline__ void fused_combine(const SplitParams& p, int unit, in
       todo &= todo - 1;
     }
   }
-  // 4. depart; the last one out clears the words (no workgroup of this call
-  // reads them any more; the next call is ordered after this one)
+  // 4. depart; the last one out clears the words (every other workgroup's
+  // accesses to them happen before its release, so none reads them after
+  // the clear; the next call is ordered after this one)
   if (tid == 0 &&
-      __hip_atomic_fetch_add(sy + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1) {
+      __hip_atomic_fetch_add(sy + 1, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT) == S - 1) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) __hip_atomic_store(sy + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }

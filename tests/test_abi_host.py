@@ -36,9 +36,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["smla_plan_nsplit", "smla_plan_nsplit_cus", "smla_workspace_bytes",
-                            "smla_workspace_lse_offset", "smla_fused_in_launch", "smla_set_merge_polls",
+                            "smla_workspace_lse_offset", "smla_fused_in_launch",
                             "smla_decode", "smla_decode_fused", "smla_topk", "smla_topk_workspace_bytes",
-                            "smla_set_topk_min_chunks",
                             "smla_decode_paged",
                             "smla_decode_dense", "smla_plan_nsplit_dense", "smla_split",
                             "smla_combine", "smla_status_str"]), names
@@ -138,7 +137,7 @@ def test_planner_degenerate(smla):
 def test_workspace_layout(smla, b, lq, h, s):
     t = b * lq
     o_bytes = t * s * h * 512 * 4
-    off = 16384 + -(-o_bytes // 256) * 256  # sync words, then part_o
+    off = -(-o_bytes // 256) * 256  # part_o at 0, then part_lse at a 256-byte boundary
     assert smla.smla_workspace_lse_offset(b, lq, h, s) == off
     want = 0 if s <= 1 else off + t * s * h * 4
     assert smla.smla_workspace_bytes(b, lq, h, s) == want
@@ -155,26 +154,21 @@ def test_single_launch_query(smla):
     assert q(1, 1, 8, 0) == -3 and q(1, 1, 8, 1025) == -3
 
 
-def test_merge_polls_setting(smla):
-    prev = smla.lib.smla_set_merge_polls(7)
-    assert prev >= 0
-    assert smla.lib.smla_set_merge_polls(prev) == 7
-    assert smla.lib.smla_set_merge_polls(-1) == -2
-    assert smla.lib.smla_set_merge_polls(prev) == prev
-
-
 # ----------------------------------------------------------- argument errors
 
 def _call(smla, fn="smla_decode", **kw):
     a = dict(q=0x10000, kv=0x20000, idx=0x30000, out=0x40000, lse=0x50000, scale=0.1,
              nsplit=1, batch=1, q_len=1, heads=8, topk=128, kv_rows=1024, ws=0, ws_bytes=0,
-             stream=0)
+             sync=0x80000, sync_bytes=16384, polls=2048, stream=0)
     a.update(kw)
     f = getattr(smla.lib, fn)
     vp = ctypes.c_void_p
-    return f(vp(a["q"]), vp(a["kv"]), vp(a["idx"]), vp(a["out"]), vp(a["lse"]), a["scale"],
-             a["nsplit"], a["batch"], a["q_len"], a["heads"], a["topk"], a["kv_rows"],
-             vp(a["ws"]), a["ws_bytes"], vp(a["stream"]))
+    args = [vp(a["q"]), vp(a["kv"]), vp(a["idx"]), vp(a["out"]), vp(a["lse"]), a["scale"],
+            a["nsplit"], a["batch"], a["q_len"], a["heads"], a["topk"], a["kv_rows"],
+            vp(a["ws"]), a["ws_bytes"]]
+    if fn == "smla_decode_fused":
+        args += [vp(a["sync"]), a["sync_bytes"], a["polls"]]
+    return f(*args, vp(a["stream"]))
 
 
 @pytest.mark.parametrize("fn", ["smla_decode", "smla_decode_fused", "smla_split"])
@@ -198,6 +192,19 @@ def test_invalid_arguments_rejected_before_launch(smla, fn):
     assert _call(smla, fn, nsplit=4) == -4
     assert _call(smla, fn, nsplit=4, ws=0x60000, ws_bytes=need - 1) == -4
     assert _call(smla, fn, nsplit=4, ws=0x60008, ws_bytes=need) == -5
+
+
+def test_fused_arguments(smla):
+    # a negative poll bound is rejected whatever the shape
+    assert _call(smla, "smla_decode_fused", polls=-1) == -2
+    assert _call(smla, "smla_decode_fused", polls=-1, nsplit=4) == -2
+    # NSPLIT 4 at one token x 8 heads merges in the launch: without a device the
+    # question cannot be answered (SMLA_ERR_DEVICE); with one, the sync words
+    # are checked (NULL, too small, misaligned) -- nothing is launched either way
+    ws = dict(nsplit=4, ws=0x60000, ws_bytes=1 << 24)
+    assert _call(smla, "smla_decode_fused", sync=0, **ws) in (-6, -1)
+    assert _call(smla, "smla_decode_fused", sync_bytes=16383, **ws) in (-6, -4)
+    assert _call(smla, "smla_decode_fused", sync=0x80002, **ws) in (-6, -5)
 
 
 def test_decode_needs_outputs(smla):
@@ -288,6 +295,10 @@ def test_planner_path_without_device(smla):
     assert smla.lib.smla_fused_in_launch(1, 1, 8, 4) == -6
     # a valid fused call with NSPLIT > 1 asks the device whether to merge in-launch
     assert _call(smla, "smla_decode_fused", nsplit=4, ws=0x60000, ws_bytes=1 << 24) == -6
+    # an explicit top-k form needs no device; AUTO with a workspace asks for the CU count
+    f = smla.lib.smla_topk
+    vp = ctypes.c_void_p
+    assert f(vp(0x10000), None, 1, 1, 65536, 8, vp(0x30000), vp(0x40000), 1 << 30, 0, None) == -6
 
 
 def test_topk_arguments(smla):
@@ -295,18 +306,20 @@ def test_topk_arguments(smla):
     f = smla.lib.smla_topk
     vp = ctypes.c_void_p
     sc, ctx, out = vp(0x10000), vp(0x20000), vp(0x30000)
-    assert f(sc, ctx, -1, 1, 100, 8, out, None, 0, None) == -2
-    assert f(sc, ctx, 1, -1, 100, 8, out, None, 0, None) == -2
-    assert f(sc, ctx, 1, 1, -5, 8, out, None, 0, None) == -2
-    assert f(sc, ctx, 1, 1, 100, -1, out, None, 0, None) == -2
-    assert f(sc, ctx, 1, 1, 100, (1 << 24) + 1, out, None, 0, None) == -2
-    assert f(sc, ctx, 1, 1, 100, 8, None, None, 0, None) == -1
-    assert f(None, ctx, 1, 1, 100, 8, out, None, 0, None) == -1
-    assert f(vp(0x10002), ctx, 1, 1, 100, 8, out, None, 0, None) == -5
-    assert f(sc, ctx, 1, 1, 100, 8, vp(0x30001), None, 0, None) == -5
-    assert f(sc, ctx, 1, 1, 100, 8, out, vp(0x40010), 1 << 20, None) == -5  # workspace 256-aligned
-    assert f(sc, ctx, 0, 1, 100, 8, out, None, 0, None) == 0   # no rows
-    assert f(sc, ctx, 1, 1, 100, 0, out, None, 0, None) == 0   # topk 0
+    assert f(sc, ctx, -1, 1, 100, 8, out, None, 0, 0, None) == -2
+    assert f(sc, ctx, 1, -1, 100, 8, out, None, 0, 0, None) == -2
+    assert f(sc, ctx, 1, 1, -5, 8, out, None, 0, 0, None) == -2
+    assert f(sc, ctx, 1, 1, 100, -1, out, None, 0, 0, None) == -2
+    assert f(sc, ctx, 1, 1, 100, (1 << 24) + 1, out, None, 0, 0, None) == -2
+    assert f(sc, ctx, 1, 1, 100, 8, out, None, 0, 3, None) == -2   # unknown form
+    assert f(sc, ctx, 1, 1, 100, 8, out, None, 0, -1, None) == -2
+    assert f(sc, ctx, 1, 1, 100, 8, None, None, 0, 0, None) == -1
+    assert f(None, ctx, 1, 1, 100, 8, out, None, 0, 0, None) == -1
+    assert f(vp(0x10002), ctx, 1, 1, 100, 8, out, None, 0, 0, None) == -5
+    assert f(sc, ctx, 1, 1, 100, 8, vp(0x30001), None, 0, 0, None) == -5
+    assert f(sc, ctx, 1, 1, 100, 8, out, vp(0x40010), 1 << 20, 0, None) == -5  # workspace 256-aligned
+    assert f(sc, ctx, 0, 1, 100, 8, out, None, 0, 0, None) == 0   # no rows
+    assert f(sc, ctx, 1, 1, 100, 0, out, None, 0, 0, None) == 0   # topk 0
 
 
 def test_topk_workspace_size(smla):
@@ -319,9 +332,3 @@ def test_topk_workspace_size(smla):
         assert f(3, 2, m) == 6 * (-(-row // 256) * 256), m
     assert f(-1, 1, 10) == 0
 
-
-def test_topk_min_chunks_setting(smla):
-    prev = smla.lib.smla_set_topk_min_chunks(3)
-    assert prev >= 0
-    assert smla.lib.smla_set_topk_min_chunks(prev) == 3
-    assert smla.lib.smla_set_topk_min_chunks(-1) == -2

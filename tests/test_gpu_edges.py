@@ -234,9 +234,7 @@ def test_poisoned_buffers(smla, edge, nsplit):
     inp, dev, (o_r, l_r) = edge
     ws = smla.workspace(inp.batch, inp.q_len, inp.heads, nsplit, "cuda")
     if ws is not None:
-        # every fp32 word of the partials is a NaN; the synchronisation words
-        # at the workspace's head must be zero, as the library requires
-        ws[smla.WS_SYNC_BYTES:].fill_(0xFF)
+        ws.fill_(0xFF)  # every fp32 word of the partials is a NaN
     out, lse, _ = _decode(smla, inp, dev, nsplit, fill=float("nan"), ws=ws)
     _parity(*_host(out, lse), o_r, l_r, f"poisoned nsplit={nsplit}")
 

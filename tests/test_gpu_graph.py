@@ -119,16 +119,19 @@ def test_graph_paged_and_fused(smla):
     out2, lse2 = _bufs(inp)
     ws = smla.workspace(inp.batch, inp.q_len, inp.heads, 4, "cuda")
     ws2 = smla.workspace(inp.batch, inp.q_len, inp.heads, 4, "cuda")
+    sync = smla.fused_sync("cuda")
 
     def fn():
         smla.smla_decode_paged(dev["q"], dev["kv"], table, 64, pos, out, lse, inp.scale, 4, ws)
-        smla.smla_decode_fused(dev["q"], dev["kv"], dev["idx"], out2, lse2, inp.scale, 4, ws2)
+        smla.smla_decode_fused(dev["q"], dev["kv"], dev["idx"], out2, lse2, inp.scale, 4, ws2,
+                               sync=sync)
 
     def disturb():
-        smla.smla_decode_fused(dev["q"], dev["kv"], dev["idx"], out2, lse2, inp.scale, 4, ws2)
+        smla.smla_decode_fused(dev["q"], dev["kv"], dev["idx"], out2, lse2, inp.scale, 4, ws2,
+                               sync=sync)
     assert smla.smla_fused_in_launch(inp.batch, inp.q_len, inp.heads, 4)
     _replays(fn, [out, lse, out2, lse2], disturb)
-    assert torch.count_nonzero(ws2[:smla.WS_SYNC_BYTES]).item() == 0
+    assert torch.count_nonzero(sync).item() == 0
 
 
 def test_graph_dense(smla):

@@ -98,10 +98,42 @@ def test_paged_batched_full_size(smla, batched, nsplit):
     ref, used_rows = _rows_call(smla, inp, dev, inp.idx, nsplit)
     assert used == used_rows
     _same_bits((out, lse), ref, f"paged batched nsplit={nsplit}")
-    seqs = [0, 33, 63]
-    q_s, kv_s, idx_s = oracle_view(inp, dev["kv"], seqs)
+    o_r, l_r = batched_ref(inp, dev)
+    _parity(*_host(out, lse), o_r, l_r, f"paged batched nsplit={nsplit} (used {used}), all 64 sequences")
+
+
+_REF = {}
+
+
+def batched_ref(inp, dev):
+    """The oracle over all 64 sequences (the rows the lists select, copied from
+    the device), computed once."""
+    if "batched" not in _REF:
+        q_s, kv_s, idx_s = oracle_view(inp, dev["kv"])
+        _REF["batched"] = oracle.decode(q_s, kv_s, idx_s, inp.scale)
+    return _REF["batched"]
+
+
+def test_paged_ragged_full_size(smla):
+    """The ragged workload (128 x 128 heads, ~9.8 GB pool, page tables of up
+    to 2048 pages: wider than the LDS stage) through the in-kernel page map,
+    with -1 padding at shuffled positions in the first 16 lists."""
+    import torch
+    inp = workload("ragged", ragged_pad=True, pad_shuffle=True)
+    dev = to_device(inp, "cuda")
+    table = torch.from_numpy(block_table(inp)).cuda()
+    pos = torch.from_numpy(np.ascontiguousarray(inp.pos)).cuda()
+    out, lse = _outputs(inp, dev["q"].device)
+    used = smla.smla_decode_paged(dev["q"], dev["kv"], table, 64, pos, out, lse, inp.scale, 0)
+    torch.cuda.synchronize()
+    ref, used_rows = _rows_call(smla, inp, dev, inp.idx, 0)
+    assert used == used_rows
+    _same_bits((out, lse), ref, "paged ragged")
+    q_s, kv_s, idx_s = oracle_view(inp, dev["kv"])
     o_r, l_r = oracle.decode(q_s, kv_s, idx_s, inp.scale)
-    _parity(*_host(out[seqs], lse[seqs]), o_r, l_r, f"paged batched nsplit={nsplit} (used {used})")
+    _parity(*_host(out, lse), o_r, l_r, f"paged ragged (used {used}), all 128 sequences")
+    del dev
+    torch.cuda.empty_cache()
 
 
 # heads, topk, pages per sequence, page ids drawn, pages inside the cache,
@@ -152,7 +184,7 @@ def test_paged_edges(smla, case):
 
 # ------------------------------------------------------------------ dense
 
-@pytest.mark.parametrize("ctx", [4096, 16384])
+@pytest.mark.parametrize("ctx", [4096, 16384, 65536])
 @pytest.mark.parametrize("nsplit", [16, 64, 0])
 def test_dense_verify(smla, ctx, nsplit):
     """The verify shape: 9 query tokens, 8 heads, every row of a flat cache."""

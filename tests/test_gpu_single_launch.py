@@ -6,11 +6,11 @@ The two-launch form (smla_split, then smla_combine) is the reference form of
 the merge; both are held to the oracle with the tolerances of the other
 parity tests.  Covered: NSPLIT 2 .. 64 on the 16-, 32- and 64-head kernels
 (the last with two and with three tile buffers), partial head blocks,
-several tokens, splits that are empty, topk 0; the
-synchronisation words back at zero after every call; one workspace reused
-across shapes; the wait-free form (merge polls 0: the last arriving
-workgroup merges every slice), which must give the same bits; bit-exact
-repeats.
+several tokens, splits that are empty, topk 0; the synchronisation words
+back at zero after every call; one workspace and one set of synchronisation
+words reused across shapes; the wait-free form (merge polls 0: the last
+arriving workgroup merges every slice), which must give the same bits;
+bit-exact repeats.
 """
 from __future__ import annotations
 
@@ -24,8 +24,6 @@ from workloads import (bf16_bits_to_f32, flat_inputs, oracle_view, to_device, to
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
-
-SYNC = 16384  # SMLA_WS_SYNC_BYTES
 
 
 @pytest.fixture(scope="module")
@@ -54,18 +52,19 @@ def _parity(o_g, l_g, o_r, l_r, what):
     assert ok, f"{what}: {m['reasons']}"
 
 
-def _sync_zero(ws, what):
+def _sync_zero(sync, what):
     import torch
-    assert torch.count_nonzero(ws[:SYNC]).item() == 0, f"{what}: sync words left non-zero"
+    assert torch.count_nonzero(sync).item() == 0, f"{what}: sync words left non-zero"
 
 
-def _single(smla, inp, dev, nsplit, ws):
-    """smla_decode with the partials area poisoned first (NaN words): a merge
-    that read a partial before its writer's stores landed would show it."""
+def _single(smla, inp, dev, nsplit, ws, sync, polls=2048):
+    """smla_decode_fused with the partials area poisoned first (NaN words): a
+    merge that read a partial before its writer's stores landed would show it."""
     import torch
-    ws[SYNC:].fill_(0xFF)
+    ws.fill_(0xFF)
     out, lse = _outputs(inp, dev["q"].device)
-    smla.smla_decode_fused(dev["q"], dev["kv"], dev["idx"], out, lse, inp.scale, nsplit, workspace_t=ws)
+    smla.smla_decode_fused(dev["q"], dev["kv"], dev["idx"], out, lse, inp.scale, nsplit,
+                           workspace_t=ws, sync=sync, merge_polls=polls)
     torch.cuda.synchronize()
     return out, lse
 
@@ -103,15 +102,16 @@ def test_single_launch_parity(smla, case):
     inp = flat_inputs("single_" + name, 9100 + h + k, b, lq, h, rows, k)
     dev = to_device(inp, "cuda")
     o_r, l_r = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
+    sync = smla.fused_sync("cuda")
     for ns in nsplits:
         assert smla.smla_fused_in_launch(b, lq, h, ns), f"{name} nsplit={ns} not single launch"
         ws = smla.workspace(b, lq, h, ns, "cuda")
-        one = _single(smla, inp, dev, ns, ws)
-        _sync_zero(ws, f"{name} nsplit={ns}")
+        one = _single(smla, inp, dev, ns, ws, sync)
+        _sync_zero(sync, f"{name} nsplit={ns}")
         _parity(*_host(*one), o_r, l_r, f"{name} single nsplit={ns}")
         two = _two(smla, inp, dev, ns, ws)
         _parity(*_host(*two), o_r, l_r, f"{name} two-launch nsplit={ns}")
-        again = _single(smla, inp, dev, ns, ws)
+        again = _single(smla, inp, dev, ns, ws, sync)
         _same_bits(one, again, f"{name} single nsplit={ns} repeat")
 
 
@@ -120,9 +120,10 @@ def test_topk_zero_forced_split(smla):
     inp = flat_inputs("single_k0", 9300, 2, 1, 8, 512, 0)
     dev = to_device(inp, "cuda")
     ws = smla.workspace(2, 1, 8, 4, "cuda")
-    out, lse = _single(smla, inp, dev, 4, ws)
+    sync = smla.fused_sync("cuda")
+    out, lse = _single(smla, inp, dev, 4, ws, sync)
     assert torch.all(out == 0).item() and torch.all(torch.isneginf(lse)).item()
-    _sync_zero(ws, "topk 0")
+    _sync_zero(sync, "topk 0")
 
 
 @pytest.mark.parametrize("name,nsplit", [("long", 64), ("batched", 4), ("spec", 0)])
@@ -135,13 +136,10 @@ def test_wait_free_merge_same_bits(smla, name, nsplit):
         nsplit = smla.smla_plan_nsplit(inp.batch, inp.q_len, inp.heads, inp.topk)
     assert smla.smla_fused_in_launch(inp.batch, inp.q_len, inp.heads, nsplit)
     ws = smla.workspace(inp.batch, inp.q_len, inp.heads, nsplit, "cuda")
-    ref = _single(smla, inp, dev, nsplit, ws)
-    prev = smla.smla_set_merge_polls(0)
-    try:
-        free = _single(smla, inp, dev, nsplit, ws)
-    finally:
-        smla.smla_set_merge_polls(prev)
-    _sync_zero(ws, f"{name} wait-free")
+    sync = smla.fused_sync("cuda")
+    ref = _single(smla, inp, dev, nsplit, ws, sync)
+    free = _single(smla, inp, dev, nsplit, ws, sync, polls=0)
+    _sync_zero(sync, f"{name} wait-free")
     _same_bits(ref, free, f"{name} wait-free nsplit={nsplit}")
     seqs = list(range(min(inp.batch, 3)))
     q_s, kv_s, idx_s = oracle_view(inp, dev["kv"], seqs)
@@ -150,17 +148,18 @@ def test_wait_free_merge_same_bits(smla, name, nsplit):
 
 
 def test_workspace_reused_across_shapes(smla):
-    """One workspace, zeroed once, serves calls of different shapes in turn."""
+    """One workspace and one set of sync words, zeroed once, serve calls of
+    different shapes in turn."""
     shapes = [(1, 1, 8, 2048, 65536, 64), (4, 1, 64, 700, 16384, 5), (2, 1, 24, 300, 4096, 4),
               (1, 1, 8, 2048, 65536, 64)]
     size = max(smla.smla_workspace_bytes(b, lq, h, ns) for b, lq, h, _, _, ns in shapes)
     import torch
     ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+    sync = smla.fused_sync("cuda")
     for i, (b, lq, h, k, rows, ns) in enumerate(shapes):
         inp = flat_inputs("single_reuse", 9400 + i, b, lq, h, rows, k)
         dev = to_device(inp, "cuda")
-        ws[SYNC:].fill_(0xFF)  # partials from whatever ran before: NaN words
-        out = _single(smla, inp, dev, ns, ws)
-        _sync_zero(ws, f"reuse {i}")
+        out = _single(smla, inp, dev, ns, ws[: smla.smla_workspace_bytes(b, lq, h, ns)], sync)
+        _sync_zero(sync, f"reuse {i}")
         o_r, l_r = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
         _parity(*_host(*out), o_r, l_r, f"reuse {i}: b{b} h{h} nsplit={ns}")

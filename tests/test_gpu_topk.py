@@ -48,12 +48,8 @@ def _run(smla, scores, topk, ctx=None, multi=True):
     if multi:
         n = smla.smla_topk_workspace_bytes(scores.shape[0], scores.shape[1], scores.shape[2])
         ws = torch.full((max(n, 256),), 0xA5, dtype=torch.uint8, device="cuda")
-    prev = smla.smla_set_topk_min_chunks(2 if multi else 0)
-    try:
-        smla.smla_topk(s, topk, out, c, workspace_t=ws)
-        torch.cuda.synchronize()
-    finally:
-        smla.smla_set_topk_min_chunks(prev)
+    smla.smla_topk(s, topk, out, c, workspace_t=ws, form=smla.TOPK_CHUNKS if multi else smla.TOPK_ROWS)
+    torch.cuda.synchronize()
     return out.cpu().numpy()
 
 

@@ -223,13 +223,17 @@ WORKLOADS = ("tiny", "long", "batched", "spec", "ragged", "verify")
 
 
 def workload(name: str, *, spec_ctx: int = 65536, with_kv: Optional[bool] = None,
-             ragged_pad: bool = False, batch: Optional[int] = None) -> Inputs:
+             ragged_pad: bool = False, pad_shuffle: bool = False,
+             batch: Optional[int] = None) -> Inputs:
     """Inputs of a named workload.
 
     with_kv: build the cache on the host (default: only when it is small).
     batch: keep only the first `batch` sequences (sampling for the oracle).
     ragged_pad: the ragged workload with its first 16 sequences shorter than
       the list (contexts in [1, 2047]) so their lists end in -1 padding.
+    pad_shuffle: with ragged_pad, each list of those 16 sequences is shuffled
+      (seeded), so the -1 entries sit at random positions of the list rather
+      than at its tail.
     """
     if name == "tiny":
         return flat_inputs(name, 1000, 1, 1, 8, 1024, 128, with_kv=True if with_kv is None else with_kv)
@@ -253,6 +257,14 @@ def workload(name: str, *, spec_ctx: int = 65536, with_kv: Optional[bool] = None
             ctx[:16] = rng.integers(1, 2047, size=16, endpoint=True)
         inp = paged_inputs("ragged_pad" if ragged_pad else name, 5000, 128, 2048, ctx,
                            with_kv=bool(with_kv))
+        if ragged_pad and pad_shuffle:
+            rng_s = np.random.default_rng(5000 + SUB_IDX + 100)
+            for b in range(16):
+                for i in range(inp.q_len):
+                    order = rng_s.permutation(inp.topk)
+                    inp.idx[b, i] = inp.idx[b, i, order]
+                    inp.pos[b, i] = inp.pos[b, i, order]
+            inp = dataclasses.replace(inp, name="ragged_pad_shuffled")
         return _first_sequences(inp, 128 if batch is None else batch)
     raise KeyError(name)
 

@@ -388,6 +388,14 @@ def smla_combine(part_o: torch.Tensor, part_lse: torch.Tensor, out: torch.Tensor
                              ("lse", lse, torch.float32, (t, h))):
         if x is None:
             raise ValueError(f"{name} is required")
+        if name != "part_o" and x.dim() > len(shp):
+            # leading dims [batch, q_len, ...] whose product is the token count
+            lead = x.shape[: x.dim() - len(shp) + 1]
+            n = 1
+            for d in lead:
+                n *= d
+            if n == t:
+                shp = tuple(lead) + shp[1:]
         _check_one(name, x, dt, shp)
     _check_devices(part_lse.device, part_o=part_o, out=out, lse=lse)
     rc = _lib_handle().smla_combine(_ptr(part_o), _ptr(part_lse), _ptr(out), _ptr(lse), t, h, s,

@@ -102,8 +102,13 @@ def test_combine_rejects(smla):
         smla.smla_combine(po[:, :3], pl, out, lse)
     with pytest.raises(TypeError, match="part_lse must be"):
         smla.smla_combine(po, pl.double(), out, lse)
+    with pytest.raises(ValueError, match="out must be"):
+        smla.smla_combine(po, pl, out.view(1, t, h, 512)[:, :2], lse)
     with pytest.raises(ValueError, match="GPU"):
         smla.smla_combine(po, pl, out, lse)
+    # [batch, q_len, heads, ...] outputs with batch * q_len tokens are accepted
+    with pytest.raises(ValueError, match="GPU"):
+        smla.smla_combine(po, pl, out.view(3, 1, h, 512), lse.view(1, 3, h))
 
 
 def test_topk_rejects(smla):

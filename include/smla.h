@@ -82,6 +82,7 @@ enum smla_status {
 #define SMLA_MAX_TOPK (1 << 24)
 #define SMLA_FUSED_SYNC_BYTES 16384  /* synchronisation words of smla_decode_fused */
 #define SMLA_FUSED_MAX_NSPLIT 64     /* largest NSPLIT merged inside the split launch */
+#define SMLA_NOALLOC_SCRATCH_BYTES (64 << 20) /* partials area of smla_decode_noalloc */
 
 /*
  * NSPLIT the planner picks for a call of this shape on the current device
@@ -128,6 +129,24 @@ int smla_fused_in_launch(int batch, int q_len, int heads, int nsplit);
 int smla_decode(const void *q, const void *kv_cache, const int32_t *topk_idx, void *out,
                 float *lse, float scale, int nsplit, int batch, int q_len, int heads, int topk,
                 int64_t kv_rows, void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/*
+ * smla_decode for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): no
+ * workspace argument.  The partials of a call with NSPLIT > 1 go to a static
+ * device array of SMLA_NOALLOC_SCRATCH_BYTES per device, which the library
+ * holds until the process ends; a call whose partials need more
+ * (smla_workspace_bytes above that) returns SMLA_ERR_WORKSPACE and launches
+ * nothing.  Every call on a device shares that device's array, which keeps
+ * the last call's partials: calls that overlap on one device (on different
+ * streams, or from host threads with no order between them) race.  The first
+ * call on a device looks up the array's device address (SMLA_ERR_DEVICE if
+ * that fails).  Allocates and frees nothing.  Other arguments, results and
+ * errors as smla_decode.
+ */
+int smla_decode_noalloc(const void *q, const void *kv_cache, const int32_t *topk_idx, void *out,
+                        float *lse, float scale, int nsplit, int batch, int q_len, int heads,
+                        int topk, int64_t kv_rows, void *hip_stream);
 
 /*
  * smla_decode with the log-sum-exp merge inside the split launch (one kernel

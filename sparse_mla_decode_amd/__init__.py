@@ -10,7 +10,8 @@ without the built library raises ImportError.
 Functions carry the C names: smla_plan_nsplit, smla_plan_nsplit_cus,
 smla_workspace_bytes, smla_workspace_lse_offset, smla_decode, smla_decode_fused,
 smla_fused_in_launch, smla_decode_paged, smla_decode_dense, smla_plan_nsplit_dense,
-smla_split, smla_combine, smla_topk, smla_topk_workspace_bytes, smla_status_str.
+smla_split, smla_combine, smla_topk, smla_topk_workspace_bytes, smla_decode_noalloc,
+smla_status_str.
 
 Every tensor argument is checked before the library is called: dtype,
 contiguity, shape, and that it lives on the same GPU as q (the C ABI takes
@@ -31,6 +32,7 @@ DV = 512
 MAX_NSPLIT = 1024
 MAX_HEADS = 4096
 FUSED_SYNC_BYTES = 16384  # SMLA_FUSED_SYNC_BYTES
+NOALLOC_SCRATCH_BYTES = 64 << 20  # SMLA_NOALLOC_SCRATCH_BYTES
 DEFAULT_MERGE_POLLS = 2048
 TOPK_AUTO, TOPK_ROWS, TOPK_CHUNKS = 0, 1, 2  # smla_topk_form
 
@@ -65,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.smla_decode.argtypes = call
     lib.smla_decode.restype = i32
     lib.smla_decode_fused.argtypes = call[:-1] + [vp, sz, i32, vp]
+    lib.smla_decode_noalloc.argtypes = call[:-3] + [vp]
+    lib.smla_decode_noalloc.restype = i32
     lib.smla_decode_fused.restype = i32
     lib.smla_split.argtypes = call
     lib.smla_split.restype = i32
@@ -260,6 +264,25 @@ def smla_decode(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int = 0,
     """
     return _call(_lib_handle().smla_decode, "smla_decode", q, kv_cache, topk_idx, out, lse, scale, nsplit,
                  workspace_t, stream)[0]
+
+
+def smla_decode_noalloc(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int = 0,
+                        stream=None) -> int:
+    """smla_decode with its partials in the library's static per-device
+    scratch array (no workspace, nothing allocated: see include/smla.h).
+    Returns the NSPLIT used."""
+    _check_tensors(q, kv_cache, topk_idx, out, lse)
+    if topk_idx is None:
+        raise ValueError("topk_idx is required")
+    b, lq, h, k = _shape(q, topk_idx)
+    if nsplit == 0 and b * lq > 0:
+        nsplit = smla_plan_nsplit(b, lq, h, k)
+    rc = _lib_handle().smla_decode_noalloc(_ptr(q), _ptr(kv_cache), _ptr(topk_idx), _ptr(out), _ptr(lse),
+                                           float(scale), int(nsplit), b, lq, h, k, kv_cache.shape[0],
+                                           _stream(stream))
+    if rc != 0:
+        raise SmlaError(rc, "smla_decode_noalloc")
+    return nsplit
 
 
 def smla_decode_fused(q, kv_cache, topk_idx, out, lse, scale: float, nsplit: int = 0,

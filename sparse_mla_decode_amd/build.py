@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsmla.so")
 SOURCES = [os.path.join(CSRC, "smla_kernels.hip"), os.path.join(CSRC, "smla_topk.hip"),
-           os.path.join(CSRC, "smla_api.cpp")]
+           os.path.join(CSRC, "smla_noalloc.hip"), os.path.join(CSRC, "smla_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed-fp32 VALU ops stay disabled in every device compile.  Kernel-argument

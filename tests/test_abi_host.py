@@ -37,7 +37,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     assert names == sorted(["smla_plan_nsplit", "smla_plan_nsplit_cus", "smla_workspace_bytes",
                             "smla_workspace_lse_offset", "smla_fused_in_launch",
-                            "smla_decode", "smla_decode_fused", "smla_topk", "smla_topk_workspace_bytes",
+                            "smla_decode", "smla_decode_fused", "smla_decode_noalloc",
+                            "smla_topk", "smla_topk_workspace_bytes",
                             "smla_decode_paged",
                             "smla_decode_dense", "smla_plan_nsplit_dense", "smla_split",
                             "smla_combine", "smla_status_str"]), names
@@ -205,6 +206,22 @@ def test_fused_arguments(smla):
     assert _call(smla, "smla_decode_fused", sync=0, **ws) in (-6, -1)
     assert _call(smla, "smla_decode_fused", sync_bytes=16383, **ws) in (-6, -4)
     assert _call(smla, "smla_decode_fused", sync=0x80002, **ws) in (-6, -5)
+
+
+def test_noalloc_arguments(smla):
+    """smla_decode_noalloc: errors before any launch and before the scratch
+    array is looked up (fake pointers; nothing may be launched)."""
+    f = smla.lib.smla_decode_noalloc
+    vp = ctypes.c_void_p
+    ok = (vp(0x10000), vp(0x20000), vp(0x30000), vp(0x40000), vp(0x50000), 0.1)
+    assert f(*ok, -1, 1, 1, 8, 128, 1024, None) == -3
+    assert f(*ok, 1025, 1, 1, 8, 128, 1024, None) == -3
+    # partials above SMLA_NOALLOC_SCRATCH_BYTES (64 MiB): 64 tokens x 128 heads x 64 splits
+    assert smla.smla_workspace_bytes(64, 1, 128, 64) > smla.NOALLOC_SCRATCH_BYTES
+    assert f(*ok, 64, 64, 1, 128, 2048, 1024, None) == -4
+    # NSPLIT 1 needs no scratch: plain argument errors come from the decode checks
+    assert f(vp(0), *ok[1:], 1, 1, 1, 8, 128, 1024, None) == -1
+    assert f(*ok, 1, 1, 1, 0, 128, 1024, None) == -2
 
 
 def test_decode_needs_outputs(smla):

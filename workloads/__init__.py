@@ -393,7 +393,9 @@ def rotation(inp: Inputs, min_bytes: int = 512 << 20, seed: int = 77, positions:
     ctx = np.asarray(inp.ctx)
     valid = int((inp.idx >= 0).sum())
     need = -(-min_bytes // max(1, valid * ROW_BYTES))
-    n_sets = max(1, min(need, int(max(1, (ctx // K).min()))))
+    # each sequence draws disjoint sets while its context allows it (a short
+    # context repeats some rows across sets; the batch as a whole does not)
+    n_sets = max(1, need)
     sets, pos_sets = [], []
     for s in range(n_sets):
         idx = np.empty((B, Lq, K), np.int32)

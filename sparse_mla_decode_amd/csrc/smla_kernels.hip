@@ -25,14 +25,16 @@
 //     so that each lane owns one head: the online-softmax max needs two
 //     cross-lane exchanges per tile and the running sum none until the end.
 //     In 16-head blocks the waves of the group pair up along K (even / odd
-//     K-steps) and add their halves through LDS.  In 64-head blocks four
-//     waves share a pair of head groups along K (one K-step residue mod 4
-//     each), reduce-scatter the partial scores through LDS, and each then
-//     owns the softmax of 8 heads; the bf16 weights go back through LDS.
+//     K-steps) and add their halves through LDS.  In 64-head blocks each of
+//     eight waves computes one head group's scores for one half of the tile
+//     rows over all of K ("row halves"); the two halves of a head agree on
+//     the running max through LDS, and the bf16 weights go to LDS for the PV
+//     of every wave.
 //   * O^T += V^T * P^T on the same MFMA; the softmax output is already laid
 //     out as the B operand (no shuffles; in 64-head blocks it is written to
-//     LDS in that layout), V^T comes from LDS transpose reads; the waves of
-//     a head group split the 512 value columns.
+//     LDS in that layout), V^T comes from LDS transpose reads; the waves
+//     split the 512 value columns (in 64-head blocks each wave holds O of
+//     all 64 heads over one eighth of the columns).
 //   * masked entries (-1, out of range, past the slice end) load a static
 //     all-zero row, so their V contribution is exactly zero, and get a score
 //     of -inf.
@@ -371,14 +373,16 @@ __device__ __forceinline__ void fused_combine(const SplitParams& p, int unit, in
 //   KS = 1: every wave computes all of QK^T for its head groups;
 //   KS = 2: the K-steps of one parity, the two parities adding their halves
 //           through LDS, after which both waves hold all of S;
-//   KS = 4 (GPW = 2, NCS = 4): the four waves of a head pair take the
-//           K-steps of one residue mod 4 each, for both head groups; a
-//           reduce-scatter through LDS leaves each wave the full scores of
-//           8 heads x all tile rows, whose softmax it owns (running max,
-//           sum, rescale factor), and the bf16 weights go back through LDS
-//           as the PV operands of all four.  Each LDS operand read feeds two
-//           MFMAs (one per head group) with no duplicated softmax, at about
-//           220 registers: two waves per SIMD.
+//   KS = 1 with GPW = 4 (HG = 4, NCS = 8: "row halves", eight waves, two
+//           per SIMD): wave w = (kq, rh) holds Q of head group kq for all 18
+//           K-steps and computes the scores of tile rows 16 rh .. 16 rh + 15
+//           for those 16 heads, with no exchange of partial scores; a head's
+//           rows are split over the two row halves, whose waves agree on the
+//           running max through LDS.  Each wave holds O of all 64 heads for
+//           one eighth of the value columns, so each V^T read feeds four
+//           MFMAs.  Per tile: two workgroup barriers in the usual case (tile
+//           landed, weights written) and no exchange of partial scores;
+//           about 250 registers, two waves per SIMD.
 // TR rows per tile, NBUF tile buffers: NBUF - 1 tiles are in flight while one
 // is computed.
 // ---------------------------------------------------------------------------
@@ -451,7 +455,7 @@ struct SplitTail {
 
 template <int HG, int NCS, int GPW, int TR, int KS, int NBUF, int SRC>
 __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
-__attribute__((amdgpu_waves_per_eu(GPW == 1 || KS == 4 ? 2 : 1)))
+__attribute__((amdgpu_waves_per_eu(2)))  // every class: two waves per SIMD, at most 256 registers
 void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_kv, int64_t a_kv_rows,
                   int a_topk, int a_per_split, int a_nsplit, int a_heads, int a_tokens, int a_q_len,
                   SplitTail tl) {
@@ -479,14 +483,14 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   p.merge_polls = tl.merge_polls;
   p.scale_log2 = tl.scale_log2;
   static_assert(HG % GPW == 0, "whole head groups per wave");
-  static_assert(KS == 1 || KS == 2 || KS == 4, "K-split factor");
-  constexpr bool KSPLIT = KS == 2;  // K-split pairs
-  constexpr bool KQ = KS == 4;      // K-split quads with the softmax owned per 8 heads
+  constexpr bool KSPLIT = KS == 2;          // K-split pairs
+  constexpr bool KRH = KS == 1 && GPW == 4;  // row halves: one head group's scores a wave
+  static_assert(KS == 1 || KS == 2, "K-split factor");
   static_assert(!KSPLIT || NCS % 2 == 0, "K-split pairs waves of opposite parity");
-  static_assert(!KQ || (NCS == 4 && GPW == 2 && TR == 32), "K-split quad shape");
-  // tile buffers: two, or for quads over long slices three (two tiles in
-  // flight while one is computed)
-  static_assert(NBUF == 2 || (NBUF == 3 && KQ), "tile buffers");
+  static_assert(!KRH || (HG == 4 && NCS == 8 && TR == 32), "row-half shape: 8 waves x 2 row blocks");
+  // tile buffers: two, or for row halves over long slices three (two tiles
+  // in flight while one is computed)
+  static_assert(NBUF == 2 || (NBUF == 3 && KRH), "tile buffers");
   constexpr int NT = 64 * (HG / GPW) * NCS;
   // waves that issue the tile loads: all of them, or half of them when the
   // tile's wave loads do not split evenly (36 per 32-row tile: not over 8)
@@ -497,9 +501,8 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   constexpr int L = TR * kRowGran / NTD;      // DMA instructions per loading thread per tile
   constexpr int kTileBytes = TR * kRow * 2;
   constexpr int CB = (kDV / 16) / NCS;        // 16-column blocks of O per wave
-  // QK^T K-steps per wave: all 18, with K-split pairs the 9 of one parity,
-  // with quads those of one residue mod 4 (5 or 4)
-  constexpr int KSW = KSPLIT ? kKSteps / 2 : KQ ? (kKSteps + 3) / 4 : kKSteps;
+  // QK^T K-steps per wave: all 18, with K-split pairs the 9 of one parity
+  constexpr int KSW = KSPLIT ? kKSteps / 2 : kKSteps;
   static_assert(TR * kRowGran % NTD == 0, "tile must split evenly over the loading threads");
   static_assert(TR % 32 == 0, "tile shape");
   // list entries staged at a time (the K-split 16-head workgroup stages
@@ -518,15 +521,18 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb2[NBUF > 2 ? kTileBytes : 16];
   __shared__ __attribute__((aligned(16))) int list_s[LCAP];
-  // K-split pairs: partial S^T per (head group, parity) slot: [slot][gi][rb][lane];
-  // quads: every wave's partial S^T, [wave][gi][rb][lane ^ 8*rb]
-  __shared__ __attribute__((aligned(16)))
-  floatx4 xs[KSPLIT ? kXsSlots * GPW * RB * 64 : KQ ? (NT / 64) * GPW * RB * 64 : 1];
-  // quads: the bf16 weights P^T as PV B operands, [head pair][gi][g][head][8],
-  // the owners' rescale factors per head, and their final sums
-  __shared__ __attribute__((aligned(16))) u32x4 ps[KQ ? (HG / GPW) * GPW * 64 : 1];
-  __shared__ float alpha_s[KQ ? HG * 16 : 1];
-  __shared__ float fin_l[KQ ? HG * 16 : 1];
+  // K-split pairs: partial S^T per (head group, parity) slot: [slot][gi][rb][lane]
+  __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? kXsSlots * GPW * RB * 64 : 1];
+  // row halves: the bf16 weights P^T as PV B operands, [head group][g][head][8]
+  // (each row half writing its 4 slots), and the rescale factors per head
+  __shared__ __attribute__((aligned(16))) u32x4 ps[KRH ? HG * 64 : 1];
+  __shared__ float alpha_s[KRH ? HG * 16 : 1];
+  // row halves: each wave's per-head maximum over its row half and its
+  // share of the final sums, [wave][head]; whether a wave's heads need
+  // their running max moved in this tile, [wave]
+  __shared__ float rmax_s[KRH ? (NT / 64) * 16 : 1];
+  __shared__ float rsum_s[KRH ? (NT / 64) * 16 : 1];
+  __shared__ __attribute__((aligned(16))) int rflag_s[KRH ? NT / 64 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -535,20 +541,10 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   const int l16 = lane & 15;  // MFMA row / column within a 16-wide block
   const int hg0 = (wave / NCS) * GPW;  // first head group of this wave
   const int cs = wave % NCS;
-  // K-split quads: head pair hp = wave / NCS; the wave's QK^T K-steps are
-  // those of residue kr = (cs + 2 hp) mod 4 (five for kr < 2, else four, so
-  // the two waves of a SIMD under round-robin placement, cs and cs + 4, get
-  // one of each); it owns the softmax of heads 8a .. 8a + 7 of the pair's
-  // head group go (go = cs / 2, a = cs % 2)
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const int hp = wave_u / NCS, cs_u = wave_u % NCS;
-  const int kr = (cs_u + 2 * hp) & 3;
-  const int go = cs_u >> 1, own_a = cs_u & 1;
-  // a quad owner's lane holds head 8a + (l16 & 7) of group go, tile rows
-  // 16 rbl + 4g .. +3: the lanes of the wave's own half (l16 / 8 = a) take
-  // row block 0, the others row block 1
-  const int rbl = (l16 >> 3) != own_a;
-  const int own_j = 8 * own_a + (l16 & 7);
+  // row halves: wave = (kq, rh) -- scores of head group kq, tile rows
+  // 16 rh .. +15; wave (kq, 1 - rh) holds the group's other rows
+  const int kq = wave_u & 3, rh = wave_u >> 2;
 
   // workgroup -> (token, head block, split), splits fastest, in the XCD-
   // contiguous numbering: a token's head blocks and splits share one XCD, so
@@ -604,7 +600,10 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   // exactly half a CU's LDS each, so they keep the direct lookup.)
   constexpr int kTabStage = 512;
   constexpr int TI = (kTabStage + NT - 1) / NT;
-  const bool tab_lds = SRC == kSrcPositions && KQ && tab != nullptr && p.max_pages <= kTabStage;
+  const bool tab_lds =
+      SRC == kSrcPositions && KRH && tab != nullptr && p.max_pages <= kTabStage;
+  // the table's LDS stage: the weights' buffer, idle whenever the list is staged
+  int32_t* const tab_stage = (int32_t*)ps;
   int tv[TI];
   if (tab_lds) {
 #pragma unroll
@@ -628,21 +627,26 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   // Q^T as the B operand of S^T = KV * Q^T: lane (g, l16) holds
   // q[h][32*ks + 8*g .. +7] for each of the wave's K-steps ks (zeros for
   // padding heads, read from the zero row: 72 granules cover 18 K-steps x 4
-  // groups): all 18, with K-split pairs 2k + (cs & 1), with quads kr + 4k
-  bf16x8 qb[GPW][KSW];
+  // groups): all 18, with K-split pairs 2k + (cs & 1)
+  // row halves: Q of head group kq, all 18 K-steps
+  bf16x8 qf[KRH ? kKSteps : 1];
+  if constexpr (KRH) {
+    const int hq_ = hblk * kHeadsPerBlock + kq * 16 + l16;
+    const u32x4* qrow = hq_ < p.heads ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + hq_) * kRow) + g
+                                      : g_zero_row + g;
 #pragma unroll
-  for (int gi = 0; gi < GPW; ++gi) {
+    for (int k = 0; k < kKSteps; ++k) qf[k] = __builtin_bit_cast(bf16x8, qrow[4 * k]);
+  }
+  bf16x8 qb[KRH ? 1 : GPW][KRH ? 1 : KSW];
+#pragma unroll
+  for (int gi = 0; gi < (KRH ? 0 : GPW); ++gi) {
     const u32x4* qrow = h_ok[gi]
                             ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + h[gi]) * kRow) + g
                             : g_zero_row + g;
     if (KSPLIT) qrow += 4 * (cs & 1);
-    if (KQ) qrow += 4 * kr;
 #pragma unroll
     for (int k = 0; k < KSW; ++k) {
-      if (KQ && k == KSW - 1 && kr >= 2)
-        qb[gi][k] = bf16x8{};  // K-step kr + 16 is past the row: never used
-      else
-        qb[gi][k] = __builtin_bit_cast(bf16x8, qrow[k * 4 * (KSPLIT ? 2 : KQ ? 4 : 1)]);
+      qb[gi][k] = __builtin_bit_cast(bf16x8, qrow[k * 4 * (KSPLIT ? 2 : 1)]);
     }
   }
 
@@ -653,8 +657,8 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   const int qk_odd = l16 * 128 + ((g ^ hq) ^ 4) * 16;
   // K-split: K-step 2k + par is block k, in-block half par (par = cs & 1)
   const int qk_half = (cs & 1) ? qk_odd : qk_even;
-  // quads: K-step kr + 4k is block kr / 2 + 2k, in-block half kr & 1
-  const int qk_quad = ((kr & 1) ? qk_odd : qk_even) + (kr >> 1) * TR * 128;
+  // row halves: rows 16 rh + l16, K-steps of either parity
+  const int qk_rh_e = qk_even + rh * 16 * 128, qk_rh_o = qk_odd + rh * 16 * 128;
   // V^T transpose read: source lane (e, s') of group g reads row 4g + e
   // (+16 for slots 4-7, +32 per PV K-step), columns 16*cb + 4s' .. +3 =
   // granule 2cb + b0 (b0 = s' >> 1) at byte 8*b1 (b1 = s' & 1); in-block
@@ -711,135 +715,91 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
     return (uint64_t)(uintptr_t)src;
   };
 
-  // Consume tile t held in T, K-split quads; refill() issues the step's tile
-  // loads once this wave's QK^T operand reads are done (LDS-DMA writes
-  // landing in LDS hold off the waves' LDS reads).
-  auto compute_quad = [&](const uint8_t* T, int t, auto&& refill) __attribute__((always_inline)) {
-    if constexpr (KQ) {
-      // ---- partial S^T = KV_tile * Q^T over the wave's K-steps kr + 4k, for
-      // both head groups of the pair (each operand read feeds two MFMAs)
-      const bool five = kr < 2;  // wave-uniform: a fifth K-step
-      bf16x8 av[KSW][RB];
+  // Consume tile t held in T, row halves; refill() issues the step's tile
+  // loads once this wave's QK^T operand reads are done.
+  auto compute_rh = [&](const uint8_t* T, int t, auto&& refill) __attribute__((always_inline)) {
+    if constexpr (KRH) {
+      // ---- S^T of rows 16 rh .. +15, head group kq, all 18 K-steps (two
+      // accumulation chains)
+      floatx4 a2[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int k = 0; k < KSW - 1; ++k)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          av[k][rb] = *(const bf16x8*)(T + qk_quad + 2 * k * TR * 128 + rb * 16 * 128);
-      if (five) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          av[KSW - 1][rb] =
-              *(const bf16x8*)(T + qk_quad + 2 * (KSW - 1) * TR * 128 + rb * 16 * 128);
+      for (int k = 0; k < kKSteps; ++k) {
+        const bf16x8 a = *(const bf16x8*)(T + ((k & 1) ? qk_rh_o : qk_rh_e) + (k >> 1) * TR * 128);
+        a2[k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[k], a2[k & 1], 0, 0, 0);
       }
-      floatx4 acc[GPW][RB];
-#pragma unroll
-      for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb) acc[gi][rb] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < KSW - 1; ++k)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int gi = 0; gi < GPW; ++gi)
-            acc[gi][rb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[k][rb], qb[gi][k], acc[gi][rb], 0, 0, 0);
-      if (five) {
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-#pragma unroll
-          for (int gi = 0; gi < GPW; ++gi)
-            acc[gi][rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[KSW - 1][rb], qb[gi][KSW - 1],
-                                                                  acc[gi][rb], 0, 0, 0);
-      }
-
-      // ---- reduce-scatter through LDS: every wave stores its four blocks
-      // (row block 1 at lane ^ 8, so that each owner lane reads its own
-      // position); the owner adds the pair's other three waves to its own part
-      // (block (go, 0) of this lane, or block (go, 1) of lane ^ 8)
-#pragma unroll
-      for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-        for (int rb = 0; rb < RB; ++rb)
-          xs[((wave_u * GPW + gi) * RB + rb) * 64 + (lane ^ (8 * rb))] = acc[gi][rb];
       refill();
-      barrier_lds();
-      const floatx4 own0 = go ? acc[1][0] : acc[0][0];
-      const floatx4 own1 = go ? acc[1][1] : acc[0][1];
-      floatx4 sv;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = ror8_lanes(own1[i]);
-        sv[i] = rbl ? x : own0[i];
-      }
-#pragma unroll
-      for (int c = 1; c < NCS; ++c) {
-        const int src = hp * NCS + ((cs_u + c) & (NCS - 1));
-        sv += xs[((src * GPW + go) * RB + rbl) * 64 + lane];
-      }
+      const floatx4 sv = a2[0] + a2[1];
 
-      // ---- online softmax of the owned head: 4 rows here, 32 over the 8
-      // lanes l16, l16 ^ 8 of the four lane groups
-      const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rbl + 4 * g);
-      float s4[4];
+      // ---- online softmax over this row half; a head's two row halves
+      // must use the same running max, so the weights are computed against
+      // the current one and redone, in every wave, in the rare tile where
+      // some head's maximum grows by more than 2^8 (the first tile always)
+      const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rh + 4 * g);
+      float sc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s4[i] = r4[i] >= 0 ? sv[i] * p.scale_log2 : -__builtin_inff();
-      float mx = fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]));
-      mx = max4_lanes(mx);
-      mx = fmaxf(mx, ror8_lanes(mx));
-      // lazy rescaling as below; the factor goes to every wave holding O of
-      // this head (exactly 1 when the max stays)
-      float alpha = 1.f;
-      if (mx > m_run[0] + kRescaleLog2) {
-        const float m_new = fmaxf(m_run[0], mx);
-        alpha = __builtin_amdgcn_exp2f(m_run[0] - m_new);  // 0 while m_run = -inf
-        l_run[0] *= alpha;
-        m_run[0] = m_new;
-      }
-      const float m_use = m_run[0] == -__builtin_inff() ? 0.f : m_run[0];
+      for (int i = 0; i < 4; ++i) sc[i] = r4[i] >= 0 ? sv[i] * p.scale_log2 : -__builtin_inff();
+      const float mxh = max4_lanes(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])));
       float pw[4];
+      // weights against the running max, written as the rows 16 rh + 4 g + i
+      // = K slots 4 rh + i of the PV B operand of lane group g, head l16
+      auto weights = [&]() __attribute__((always_inline)) {
+        const float m_use = m_run[0] == -__builtin_inff() ? 0.f : m_run[0];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        pw[i] = __builtin_amdgcn_exp2f(s4[i] - m_use);
-        l_run[0] += pw[i];
-      }
-      // P^T for PV K slots 4 rbl .. +3 of lane group g, head own_j (the slot
-      // order of the V^T transpose reads below)
-      *(u32x2*)((uint8_t*)ps + (((hp * GPW + go) * 4 + g) * 16 + own_j) * 16 + 8 * rbl) =
-          u32x2{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3])};
-      if (g == 0 && !rbl) alpha_s[hp * GPW * 16 + go * 16 + own_j] = alpha;
+        for (int i = 0; i < 4; ++i) pw[i] = __builtin_amdgcn_exp2f(sc[i] - m_use);
+        *(u32x2*)((uint8_t*)ps + (kq * 64 + lane) * 16 + 8 * rh) =
+            u32x2{pack_bf16x2(pw[0], pw[1]), pack_bf16x2(pw[2], pw[3])};
+      };
+      weights();
+      const int need_w = __any(mxh > m_run[0] + kRescaleLog2);
+      if (lane == 0) rflag_s[wave_u] = need_w;
+      if (g == 0) rmax_s[wave_u * 16 + l16] = mxh;
       barrier_lds();
+      const i32x4 fa = *(const i32x4*)rflag_s;
+      const i32x4 fb = *(const i32x4*)(rflag_s + 4);
+      if ((fa[0] | fa[1] | fa[2] | fa[3]) | (fb[0] | fb[1] | fb[2] | fb[3])) {  // the same in every wave
+        // both row halves of a head take the same decision from the same
+        // two maxima: move the running max when the tile's exceeds it by
+        // more than 2^8 (alpha exactly 1 otherwise)
+        const float mt = fmaxf(mxh, rmax_s[(wave_u ^ 4) * 16 + l16]);
+        float alpha = 1.f;
+        if (mt > m_run[0] + kRescaleLog2) {
+          const float m_new = fmaxf(m_run[0], mt);
+          alpha = __builtin_amdgcn_exp2f(m_run[0] - m_new);  // 0 while m_run = -inf
+          l_run[0] *= alpha;
+          m_run[0] = m_new;
+        }
+        if (rh == 0 && g == 0) alpha_s[kq * 16 + l16] = alpha;
+        weights();
+        barrier_lds();
+        float al[HG];
+        bool scale = false;
+#pragma unroll
+        for (int gi = 0; gi < HG; ++gi) {
+          al[gi] = alpha_s[gi * 16 + l16];
+          scale |= al[gi] != 1.f;
+        }
+        if (__any(scale)) {
+#pragma unroll
+          for (int gi = 0; gi < HG; ++gi)
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) oacc[gi][cb] *= al[gi];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run[0] += pw[i];
 
-      // ---- O^T += V^T * P^T over this wave's column quarter, both head groups
-      float al[GPW];
-      bool scale = false;
+      // ---- O^T += V^T * P^T over this wave's eighth of the columns, all
+      // four head groups (each V^T operand feeds four MFMAs)
+      bf16x8 pq[HG];
 #pragma unroll
-      for (int gi = 0; gi < GPW; ++gi) {
-        al[gi] = alpha_s[hp * GPW * 16 + gi * 16 + l16];
-        scale |= al[gi] != 1.f;
-      }
-      if (__any(scale)) {
-#pragma unroll
-        for (int gi = 0; gi < GPW; ++gi)
-#pragma unroll
-          for (int cb = 0; cb < CB; ++cb) oacc[gi][cb] *= al[gi];
-      }
-      bf16x8 pq[GPW];
-#pragma unroll
-      for (int gi = 0; gi < GPW; ++gi)
-        pq[gi] = __builtin_bit_cast(bf16x8, ps[(hp * GPW + gi) * 64 + g * 16 + l16]);
-      shortx4 vt[CB][2];
+      for (int gi = 0; gi < HG; ++gi) pq[gi] = __builtin_bit_cast(bf16x8, ps[gi * 64 + lane]);
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const int off = pv_base[cb & 3] + (cb >> 2) * TR * 128;
-        vt[cb][0] = lds_tr16(T + off);
-        vt[cb][1] = lds_tr16(T + off + 16 * 128);
-      }
+        const shortx4 vt[2] = {lds_tr16(T + off), lds_tr16(T + off + 16 * 128)};
+        const bf16x8 a8 = __builtin_bit_cast(bf16x8, vt);
 #pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const bf16x8 a8 = __builtin_bit_cast(bf16x8, vt[cb]);
-#pragma unroll
-        for (int gi = 0; gi < GPW; ++gi)
+        for (int gi = 0; gi < HG; ++gi)
           oacc[gi][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, pq[gi], oacc[gi][cb], 0, 0, 0);
       }
     }
@@ -847,6 +807,7 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
 
   // Consume tile t held in T.
   auto compute = [&](const uint8_t* T, int t) __attribute__((always_inline)) {
+   if constexpr (!KRH) {
     // ---- S^T = KV_tile * Q^T: RB 16-row blocks, 18 K-steps of 32 columns
     floatx4 sacc[GPW][RB];
     if constexpr (KSPLIT) {
@@ -1014,6 +975,7 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
         }
       }
     }
+   }
   };
 
   // Software pipeline over the tiles of each staged chunk of the list.
@@ -1024,7 +986,7 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   const uint32_t kv32 = rows32(p.kv_rows);
   auto store_list = [&](int n_ent) __attribute__((always_inline)) {
     if (tab_lds) {  // uniform: stage the table, then map the positions through it
-      int32_t* ts = (int32_t*)xs;
+      int32_t* ts = tab_stage;
 #pragma unroll
       for (int u = 0; u < TI; ++u) {
         const int i = u * NT + tid;
@@ -1085,16 +1047,16 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
         if (NBUF > 2 || n + 1 < ntiles)
           addr[bn] = issue(buf(std::integral_constant<int, bn>{}), n + NBUF - 1, ntiles);
       };
-      if constexpr (KQ && NBUF > 2) {
+      if constexpr (KRH && NBUF > 2) {
         // the refill goes out after the tile's QK^T (it still has two steps
         // to land); a step past the last tile only refills
         if (n < ntiles)
-          compute_quad(buf(bconst), n, refill);
+          compute_rh(buf(bconst), n, refill);
         else
           refill();
-      } else if constexpr (KQ) {
+      } else if constexpr (KRH) {
         refill();
-        compute_quad(buf(bconst), n, [] {});
+        compute_rh(buf(bconst), n, [] {});
       } else {
         refill();
         compute(buf(bconst), n);
@@ -1128,22 +1090,21 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   float inv[GPW], lse_v[GPW];
   int lse_h[GPW];
   bool lse_w[GPW];
-  if constexpr (KQ) {
-    // the owner sums its head over the 8 lanes (x + partner is the same sum
-    // in both lanes) and hands l to the waves holding the head's O
-    float l_tot = sum4_lanes(l_run[0]);
-    l_tot += ror8_lanes(l_tot);
-    const float lse_own =
-        l_tot > 0.f ? m_run[0] * kLn2 + __logf(l_tot) : -__builtin_inff();
-    if (g == 0 && !rbl) fin_l[hp * GPW * 16 + go * 16 + own_j] = l_tot;
+  if constexpr (KRH) {
+    // a row half's share of its owned head's sum (its four lane groups),
+    // then the two halves added in the same order by every wave, which
+    // needs all four groups' sums for its eighth of O's columns
+    const float lh = sum4_lanes(l_run[0]);
+    if (g == 0) rsum_s[wave_u * 16 + l16] = lh;
     barrier_lds();
 #pragma unroll
     for (int gi = 0; gi < GPW; ++gi) {
-      const float l = fin_l[hp * GPW * 16 + gi * 16 + l16];
+      // owners of group gi: waves gi (rows 0-15) and gi + 4 (rows 16-31)
+      const float l = rsum_s[gi * 16 + l16] + rsum_s[(gi + 4) * 16 + l16];
       inv[gi] = l > 0.f ? 1.f / l : 0.f;
-      lse_v[gi] = lse_own;
-      lse_h[gi] = hblk * kHeadsPerBlock + hp * GPW * 16 + go * 16 + own_j;
-      lse_w[gi] = gi == 0 && g == 0 && !rbl;
+      lse_v[gi] = l > 0.f ? m_run[0] * kLn2 + __logf(l) : -__builtin_inff();
+      lse_h[gi] = h[gi];
+      lse_w[gi] = gi == kq && rh == 0 && g == 0;
     }
   } else {
 #pragma unroll
@@ -1372,17 +1333,15 @@ void combine_wide_kernel(const float* a_part_o, const float* a_part_lse, uint16_
 // ---------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------
-// LDS of one split workgroup: the tile buffers (two, or three for K-split
-// quads over long slices), the staged index list, with K-split pairs the exchange slots of
-// partial scores (one 16-row block of 16 heads = 1 KiB per slot, head group
-// and row block), with quads every wave's partial scores, the bf16 weights
-// and two floats per head
+// LDS of one split workgroup: the tile buffers (two, or three for 64-head
+// blocks over long slices), the staged index list, with K-split pairs the
+// exchange slots of partial scores (one 16-row block of 16 heads = 1 KiB per
+// slot, head group and row block), with row halves the bf16 weights, the
+// rescale factors and two floats and a flag per (wave, owned head)
 constexpr int split_lds_bytes(int waves, int ncs, int gpw, int ks, int nbuf = 2) {
   return nbuf * kTileRows * kRow * 2 + split_list_cap(ncs, ks) * 4 +
          (ks == 2 ? (waves / ncs) * 2 * gpw * (kTileRows / 16) * 64 * 16 : 0) +
-         (ks == 4 ? waves * gpw * (kTileRows / 16) * 64 * 16 + (waves / ncs) * gpw * 64 * 16 +
-                        2 * (waves / ncs) * gpw * 16 * 4
-                  : 0);
+         (ks == 1 && gpw == 4 ? gpw * 64 * 16 + gpw * 16 * 4 + 2 * waves * 16 * 4 + waves * 4 : 0);
 }
 constexpr int kCuLdsBytes = 160 * 1024;
 
@@ -1434,27 +1393,27 @@ static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t 
 //    two workgroups per CU;
 //  * up to 32 heads: 4 waves = 2 head groups x 2 column halves, each wave
 //    all of QK^T; two workgroups per CU;
-//  * more (64-head blocks): 8 waves = 2 head pairs x 4 column quarters in
-//    K-split quads (QK^T for both groups of a pair, softmax owned per 8
-//    heads); one workgroup per CU (about 230 registers: two waves per SIMD,
-//    i.e. 8 waves per CU), with a third tile buffer over long slices.
+//  * more (64-head blocks): 8 waves in row halves (each wave the scores of
+//    one head group over half the tile rows and all of K, and O of all 64
+//    heads over an eighth of the value columns); one workgroup per CU (about
+//    250 registers: two waves per SIMD), with a third tile buffer over long
+//    slices.
 static_assert(kCuLdsBytes / split_lds_bytes(4, 4, 1, 2) == 2, "two 16-head workgroups per CU");
 static_assert(kCuLdsBytes / split_lds_bytes(4, 2, 1, 1) == 2, "two 32-head workgroups per CU");
-static_assert(split_lds_bytes(8, 4, 2, 4, 3) <= kCuLdsBytes, "one 64-head workgroup per CU");
+static_assert(split_lds_bytes(8, 8, 4, 1, 3) <= kCuLdsBytes, "one 64-head workgroup per CU");
 
 // 64-head blocks over slices of at least this many tiles take three tile
-// buffers.  Measured: 128 x 128 heads with 64-tile slices 111 against 115 us;
-// 64 x 64 heads with 16-tile slices unchanged; dense verify with 4- to
-// 16-tile slices 4-7% slower (the rounds of three steps pad the tail).
-constexpr int kDeepTiles = 32;
+// buffers (the rounds of three steps pad a short slice's tail).  Measured:
+// 64 x 64 heads with 16-tile slices 39.4 us at 4 against 40.1 us at 32.
+constexpr int kDeepTiles = 4;
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
   if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, 2>(p, 1, st);
   if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, 1>(p, 1, st);
   const int hblocks = (p.heads + 63) / 64;
   if ((p.per_split + kTileRows - 1) / kTileRows >= kDeepTiles)
-    return launch_split_t<4, 4, 2, 32, 4, 3>(p, hblocks, st);
-  return launch_split_t<4, 4, 2, 32, 4, 2>(p, hblocks, st);
+    return launch_split_t<4, 8, 4, 32, 1, 3>(p, hblocks, st);
+  return launch_split_t<4, 8, 4, 32, 1, 2>(p, hblocks, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }

@@ -719,6 +719,8 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   // loads once this wave's QK^T operand reads are done.
   auto compute_rh = [&](const uint8_t* T, int t, auto&& refill) __attribute__((always_inline)) {
     if constexpr (KRH) {
+      // validity of this lane's rows, read ahead of the QK^T
+      const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rh + 4 * g);
       // ---- S^T of rows 16 rh .. +15, head group kq, all 18 K-steps (two
       // accumulation chains)
       floatx4 a2[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
@@ -734,7 +736,6 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
       // must use the same running max, so the weights are computed against
       // the current one and redone, in every wave, in the rare tile where
       // some head's maximum grows by more than 2^8 (the first tile always)
-      const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rh + 4 * g);
       float sc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) sc[i] = r4[i] >= 0 ? sv[i] * p.scale_log2 : -__builtin_inff();
@@ -754,8 +755,21 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
       if (lane == 0) rflag_s[wave_u] = need_w;
       if (g == 0) rmax_s[wave_u * 16 + l16] = mxh;
       barrier_lds();
+      // the flags, the weights of all four head groups and this wave's V^T
+      // operands in one LDS round trip (the weights are read again if the
+      // rare path below rewrites them)
       const i32x4 fa = *(const i32x4*)rflag_s;
       const i32x4 fb = *(const i32x4*)(rflag_s + 4);
+      bf16x8 pq[HG];
+#pragma unroll
+      for (int gi = 0; gi < HG; ++gi) pq[gi] = __builtin_bit_cast(bf16x8, ps[gi * 64 + lane]);
+      bf16x8 vt[CB];
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb) {
+        const int off = pv_base[cb & 3] + (cb >> 2) * TR * 128;
+        const shortx4 v2[2] = {lds_tr16(T + off), lds_tr16(T + off + 16 * 128)};
+        vt[cb] = __builtin_bit_cast(bf16x8, v2);
+      }
       if ((fa[0] | fa[1] | fa[2] | fa[3]) | (fb[0] | fb[1] | fb[2] | fb[3])) {  // the same in every wave
         // both row halves of a head take the same decision from the same
         // two maxima: move the running max when the tile's exceeds it by
@@ -777,6 +791,7 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
         for (int gi = 0; gi < HG; ++gi) {
           al[gi] = alpha_s[gi * 16 + l16];
           scale |= al[gi] != 1.f;
+          pq[gi] = __builtin_bit_cast(bf16x8, ps[gi * 64 + lane]);
         }
         if (__any(scale)) {
 #pragma unroll
@@ -790,18 +805,11 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
 
       // ---- O^T += V^T * P^T over this wave's eighth of the columns, all
       // four head groups (each V^T operand feeds four MFMAs)
-      bf16x8 pq[HG];
 #pragma unroll
-      for (int gi = 0; gi < HG; ++gi) pq[gi] = __builtin_bit_cast(bf16x8, ps[gi * 64 + lane]);
-#pragma unroll
-      for (int cb = 0; cb < CB; ++cb) {
-        const int off = pv_base[cb & 3] + (cb >> 2) * TR * 128;
-        const shortx4 vt[2] = {lds_tr16(T + off), lds_tr16(T + off + 16 * 128)};
-        const bf16x8 a8 = __builtin_bit_cast(bf16x8, vt);
+      for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
         for (int gi = 0; gi < HG; ++gi)
-          oacc[gi][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a8, pq[gi], oacc[gi][cb], 0, 0, 0);
-      }
+          oacc[gi][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt[cb], pq[gi], oacc[gi][cb], 0, 0, 0);
     }
   };
 

@@ -525,6 +525,12 @@ def main():
                 ("; positions mapped through page tables in the kernel" if mode == "paged" else "")
             secondary[key] = dict(w2.summary(ns2, 512, 256), planner=True, workload=f"{name}: {desc}",
                                   entry_point=ENTRY[w2.kind])
+            if w2.fused_in_launch(ns2):
+                fu = w2.time_graph(w2.graph_of(w2.fused_fn(ns2)), 512)[0]
+                secondary[key]["single_launch"] = {
+                    "us_per_step": round(fu, 3), "steps_per_s": round(1e6 / fu, 2),
+                    "entry_point": "smla_decode_fused",
+                    "method": "graph replay of smla_decode_fused steps (one kernel per step)"}
             log(f"[bench] secondary {key} (planner nsplit={ns2}): {secondary[key]['us_per_step']:.2f} us/step, "
                 f"split {secondary[key]['split_us']:.2f} us ({secondary[key]['split_roofline_frac']:.3f} of HBM), "
                 f"{time.time() - t0:.1f} s")

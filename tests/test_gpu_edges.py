@@ -10,7 +10,9 @@ classes, list lengths and split counts; the combine kernel alone on synthetic
 partials (both its few-pair and many-pair forms, with NaN in the slots of
 empty splits); bit-exact repeatability; output and workspace buffers
 poisoned with NaN beforehand; a non-default stream; the limits (4096 heads,
-NSPLIT 1024, a list over all 65536 rows of a cache).
+NSPLIT 1024, a list over all 65536 rows of a cache); outlier rows that raise
+some heads' running maximum part-way through a slice, in either half of a
+tile's rows.
 """
 from __future__ import annotations
 
@@ -20,8 +22,8 @@ import pytest
 import oracle
 from oracle.compare import check
 from tests.conftest import gpu_available
-from workloads import (bf16_bits_to_f32, edge_inputs, flat_inputs, partials_inputs, to_device,
-                       torch_to_bits, workload)
+from workloads import (bf16_bits_to_f32, edge_inputs, flat_inputs, partials_inputs, spike_inputs,
+                       to_device, torch_to_bits, workload)
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not gpu_available(), reason="needs an MI355X GPU")]
@@ -249,3 +251,31 @@ def test_side_stream(smla, edge):
         smla.smla_decode(dev["q"], dev["kv"], dev["idx"], out, lse, inp.scale, 0, stream=s)
     s.synchronize()
     _parity(*_host(out, lse), o_r, l_r, "side stream")
+
+
+# Outlier rows (token, list position, head, factor): each raises that head's
+# running maximum part-way through a long slice, most by far more than the
+# lazy-rescale threshold (2^8), so the rescale of the accumulated O and sum
+# runs after the first tile; factor 4 stays near the threshold, and factor 120
+# lifts the score by 150-210 in base 2, past fp32's exp2 range for weights taken
+# against the old maximum.  List position p sits in tile p // 32 at row
+# p % 32: rows 0-15 and 16-31 of a tile are the two row halves of the 64-head
+# blocks, whose waves must agree on the new maximum.  Positions 1500 and 1501
+# spike two heads in one tile; head 3 and head 5 spike twice, the second time
+# higher.
+SPIKES = [(0, 610, 3, 4.0), (0, 700, 3, 14.0), (0, 1040, 17, 12.0), (0, 1500, 40, 12.0),
+          (0, 1501, 41, 120.0), (0, 1999, 63, 12.0), (1, 33, 5, 12.0), (1, 1200, 5, 20.0)]
+
+
+@pytest.mark.parametrize("heads", [8, 24, 64, 128])
+@pytest.mark.parametrize("nsplit", [1, 2, 0])
+def test_running_max_grows_mid_slice(smla, heads, nsplit):
+    spikes = [(t, pos, h % heads, f) for t, pos, h, f in SPIKES]
+    inp = spike_inputs(9800 + heads, 2, heads, 8192, 2048, spikes)
+    dev = to_device(inp, "cuda")
+    o_r, l_r = oracle.decode(inp.q, inp.kv, inp.idx, inp.scale)
+    # each spiked head's LSE is about its outlier's score, above the ordinary ~8
+    for t, _, h, _ in spikes:
+        assert l_r[t, 0, h] > 10.0
+    out, lse, used = _decode(smla, inp, dev, nsplit, fill=float("nan"))
+    _parity(*_host(out, lse), o_r, l_r, f"spikes heads={heads} nsplit={nsplit} (used {used})")

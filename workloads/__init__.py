@@ -436,6 +436,29 @@ def edge_inputs(seed: int = 4242, kv_rows: int = 4096, heads: int = 16, topk: in
     return inp
 
 
+def spike_inputs(seed: int, batch: int, heads: int, kv_rows: int, topk: int, spikes) -> Inputs:
+    """A flat workload whose lists hold a few outlier rows.
+
+    spikes: (token, list position, head, factor) tuples.  The cache row at that
+    list position of that token gets rope part factor * q_rope[token, head]
+    (bf16), so its score for that head rises by about
+    factor * scale * |q_rope|^2 (|q_rope|^2 ~ 64) above the ordinary scores
+    (standard deviation ~1) while its scores for the other heads stay
+    ordinary.  Its latent part is the row's own, quartered, so the head's
+    output (nearly that row's V) stays within [-2, 2], where bf16's rounding
+    error is below 2^-8.  A later, larger spike for the same head raises the
+    running maximum again part-way through a split's slice.
+    """
+    inp = flat_inputs("spikes", seed, batch, 1, heads, kv_rows, topk)
+    q32 = bf16_bits_to_f32(inp.q)
+    for tok, pos, head, factor in spikes:
+        row = int(inp.idx[tok, 0, pos])
+        lat = 0.25 * bf16_bits_to_f32(inp.kv[row, :DV])
+        inp.kv[row, :DV] = f32_to_bf16_bits(lat)
+        inp.kv[row, DV:] = f32_to_bf16_bits(np.float32(factor) * q32[tok, 0, head, DV:])
+    return inp
+
+
 def partials_inputs(seed: int, tokens: int, nsplit: int, heads: int, empty_frac: float = 0.2):
     """Synthetic combine inputs: part_o [T, S, H, 512] fp32 ~ N(0, 0.5) and
     part_lse [T, S, H] fp32 ~ U(-20, 20), with about `empty_frac` of the

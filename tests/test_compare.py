@@ -153,3 +153,23 @@ def test_shape_mismatch_is_an_error():
     o, l = ref()
     with pytest.raises(AssertionError):
         check(o[:, :2], l, o, l)
+
+
+def test_bar_no_looser_than_pages():
+    # The pages report their split-K MMA kernel agreeing with the per-head
+    # SIMT kernel to a relative error of at most 6.7e-3 (page "The Moment of
+    # Truth: Validating Split-K Parallelization for Blackwell MLA Decode",
+    # section "The Results Unfold in Real Time"); the relative bar here must
+    # not be looser than that.
+    import json
+    import os
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "pages_numbers.json")))
+    assert REL_L2 <= g["tolerance_context"]["value"]
+    # and an error of the pages' size is rejected by the bar
+    o, lse = ref()
+    rng = np.random.default_rng(3)
+    d = rng.normal(0.0, 1.0, o.shape)
+    d[2, 3] = 0.0
+    d *= g["tolerance_context"]["value"] * np.linalg.norm(o) / np.linalg.norm(d)
+    ok, m = check(o + d, lse, o, lse, max_abs=np.inf)
+    assert not ok and abs(m["rel_l2"] - g["tolerance_context"]["value"]) < 1e-9

@@ -406,8 +406,11 @@ __device__ __forceinline__ int xcd_contiguous(int bid, int n) {
 // than one temporary each (a register that a load in flight reads must not be
 // reused until the load completes, which would force waits on every load).
 //
-// The LDS destination is passed through an empty asm statement, so the
-// compiler no longer knows which buffer a load writes.  Its own wait
+// The LDS destination (wave-uniform) is passed through an empty asm
+// statement in a scalar register, so the compiler no longer knows which
+// buffer a load writes, and M0 is set from it directly (held in vector
+// registers it took one register per load and buffer, and a readfirstlane
+// before every load).  Its own wait
 // insertion would otherwise guard reads of one buffer against loads in flight
 // into another, and at some control-flow joins it loses track of which is
 // which and waits for every outstanding load, draining the pipeline.  The
@@ -420,7 +423,7 @@ __device__ __forceinline__ void dma_one(const u32x4* src, uint8_t* lds) {
   constexpr int off = 128 * STEP * IT;
   static_assert(off < 4096, "immediate offset range");
   auto* dst = (__attribute__((address_space(3))) uint8_t*)(lds + 16 * NT * IT - off);
-  asm volatile("" : "+v"(dst));
+  asm volatile("" : "+s"(dst));
   __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
                                    (__attribute__((address_space(3))) void*)dst, 16, off, 0);
 }
@@ -716,7 +719,7 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
     const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
     const u32x4* src = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran[0];
     if (wave < DW)
-      dma_tile<NTD, WPB / RG>(src, buf + wave * 64 * 16, std::make_integer_sequence<int, L>{});
+      dma_tile<NTD, WPB / RG>(src, buf + wave_u * 64 * 16, std::make_integer_sequence<int, L>{});
     return (uint64_t)(uintptr_t)src;
   };
 
@@ -727,12 +730,23 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
       // validity of this lane's rows, read ahead of the QK^T
       const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rh + 4 * g);
       // ---- S^T of rows 16 rh .. +15, head group kq, all 18 K-steps (two
-      // accumulation chains)
+      // accumulation chains).  The operand reads run D ahead of their MFMAs,
+      // in this order (scheduling barriers): left to itself the compiler kept
+      // two to four in flight, and the phase waited on LDS latency (8 ahead:
+      // 64 x 128 heads 102.5 -> 100 us per launch)
       floatx4 a2[2] = {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}};
+      constexpr int D = 8;
+      bf16x8 op[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k)
+        op[k] = *(const bf16x8*)(T + ((k & 1) ? qk_rh_o : qk_rh_e) + (k >> 1) * TR * 128);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kKSteps; ++k) {
-        const bf16x8 a = *(const bf16x8*)(T + ((k & 1) ? qk_rh_o : qk_rh_e) + (k >> 1) * TR * 128);
-        a2[k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[k], a2[k & 1], 0, 0, 0);
+        a2[k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[k % D], qf[k], a2[k & 1], 0, 0, 0);
+        if (k + D < kKSteps)
+          op[k % D] = *(const bf16x8*)(T + (((k + D) & 1) ? qk_rh_o : qk_rh_e) + ((k + D) >> 1) * TR * 128);
+        __builtin_amdgcn_sched_barrier(0);
       }
       refill();
       const floatx4 sv = a2[0] + a2[1];

@@ -406,6 +406,15 @@ def topk_figure(w, steps):
             "entry_point": "smla_topk"}
 
 
+def split_kernel_name(w, nsplit):
+    """The split kernel the library launches for this shape: blocks of more
+    than 32 heads over slices of at least four 32-row tiles take the
+    role-specialised 64-head kernel."""
+    heads = w.H * (w.Lq if w.kind == "dense" and w.K >= 8192 else 1)  # dense verify folds tokens into heads
+    per_split = -(-w.K // nsplit)
+    return "split64_kernel" if heads > 32 and -(-per_split // 32) >= 4 else "split_kernel"
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -572,7 +581,7 @@ def main():
                        "eager_step": round(eager_us, 3)},
         "roofline": {
             "bound": "hbm",
-            "kernel": "split_kernel (gather + QK^T + online softmax + PV)",
+            "kernel": split_kernel_name(w, nsplit) + " (gather + QK^T + online softmax + PV)",
             "achieved": round(achieved, 2),
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",

@@ -25,16 +25,18 @@
 //     so that each lane owns one head: the online-softmax max needs two
 //     cross-lane exchanges per tile and the running sum none until the end.
 //     In 16-head blocks the waves of the group pair up along K (even / odd
-//     K-steps) and add their halves through LDS.  In 64-head blocks each of
-//     eight waves computes one head group's scores for one half of the tile
-//     rows over all of K ("row halves"); the two halves of a head agree on
-//     the running max through LDS, and the bf16 weights go to LDS for the PV
-//     of every wave.
+//     K-steps) and add their halves through LDS.  64-head blocks over long
+//     slices specialise their waves (split64_kernel): four compute scores,
+//     each holding Q of two head groups for one half of the tile rows (one
+//     operand read feeds two MFMAs), and four hold O and accumulate the PV
+//     of the previous tile beside them, one of each kind per SIMD; over
+//     short slices every wave does both ("row halves").  The two halves of
+//     a head agree on the running max through LDS, and the bf16 weights go
+//     to LDS for the PV.
 //   * O^T += V^T * P^T on the same MFMA; the softmax output is already laid
 //     out as the B operand (no shuffles; in 64-head blocks it is written to
 //     LDS in that layout), V^T comes from LDS transpose reads; the waves
-//     split the 512 value columns (in 64-head blocks each wave holds O of
-//     all 64 heads over one eighth of the columns).
+//     split the 512 value columns.
 //   * masked entries (-1, out of range, past the slice end) load a static
 //     all-zero row, so their V contribution is exactly zero, and get a score
 //     of -inf.
@@ -381,10 +383,11 @@ __device__ __forceinline__ void fused_combine(const SplitParams& p, int unit, in
 //           running max through LDS.  Each wave holds O of all 64 heads for
 //           one eighth of the value columns, so each V^T read feeds four
 //           MFMAs.  Per tile: two workgroup barriers in the usual case (tile
-//           landed, weights written) and no exchange of partial scores;
-//           about 250 registers, two waves per SIMD.
-// TR rows per tile, NBUF tile buffers: NBUF - 1 tiles are in flight while one
-// is computed.
+//           landed, weights written) and no exchange of partial scores.
+//           Used over slices of fewer than kDeepTiles tiles; longer slices
+//           take split64_kernel (role-specialised waves, below).
+// TR rows per tile, two tile buffers: tile n+1 loads while tile n is
+// computed.
 // ---------------------------------------------------------------------------
 // The dispatcher hands workgroup i to XCD i % kXcds (round robin over the
 // eight XCDs, each with its own L2).  This renumbering gives every XCD a
@@ -456,7 +459,7 @@ struct SplitTail {
   float scale_log2;
 };
 
-template <int HG, int NCS, int GPW, int TR, int KS, int NBUF, int SRC>
+template <int HG, int NCS, int GPW, int TR, int KS, int SRC>
 __global__ __launch_bounds__(64 * (HG / GPW) * NCS)
 __attribute__((amdgpu_waves_per_eu(2)))  // every class: two waves per SIMD, at most 256 registers
 void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_kv, int64_t a_kv_rows,
@@ -491,9 +494,6 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   static_assert(KS == 1 || KS == 2, "K-split factor");
   static_assert(!KSPLIT || NCS % 2 == 0, "K-split pairs waves of opposite parity");
   static_assert(!KRH || (HG == 4 && NCS == 8 && TR == 32), "row-half shape: 8 waves x 2 row blocks");
-  // tile buffers: two, or for row halves over long slices three (two tiles
-  // in flight while one is computed)
-  static_assert(NBUF == 2 || (NBUF == 3 && KRH), "tile buffers");
   constexpr int NT = 64 * (HG / GPW) * NCS;
   // waves that issue the tile loads: all of them, or half of them when the
   // tile's wave loads do not split evenly (36 per 32-row tile: not over 8)
@@ -522,7 +522,6 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   // for every outstanding load before each LDS read).
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
   __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t tb2[NBUF > 2 ? kTileBytes : 16];
   __shared__ __attribute__((aligned(16))) int list_s[LCAP];
   // K-split pairs: partial S^T per (head group, parity) slot: [slot][gi][rb][lane]
   __shared__ __attribute__((aligned(16))) floatx4 xs[KSPLIT ? kXsSlots * GPW * RB * 64 : 1];
@@ -723,9 +722,8 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
     return (uint64_t)(uintptr_t)src;
   };
 
-  // Consume tile t held in T, row halves; refill() issues the step's tile
-  // loads once this wave's QK^T operand reads are done.
-  auto compute_rh = [&](const uint8_t* T, int t, auto&& refill) __attribute__((always_inline)) {
+  // Consume tile t held in T, row halves.
+  auto compute_rh = [&](const uint8_t* T, int t) __attribute__((always_inline)) {
     if constexpr (KRH) {
       // validity of this lane's rows, read ahead of the QK^T
       const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rh + 4 * g);
@@ -748,7 +746,6 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
           op[k % D] = *(const bf16x8*)(T + (((k + D) & 1) ? qk_rh_o : qk_rh_e) + ((k + D) >> 1) * TR * 128);
         __builtin_amdgcn_sched_barrier(0);
       }
-      refill();
       const floatx4 sv = a2[0] + a2[1];
 
       // ---- online softmax over this row half; a head's two row halves
@@ -1041,69 +1038,34 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   if (lo < hi) store_list(min(hi - lo, LCAP));
   auto buf = [&](auto bconst) __attribute__((always_inline)) -> uint8_t* {
     constexpr int b = decltype(bconst)::value;
-    return b == 0 ? tb0 : b == 1 ? tb1 : tb2;
+    return b == 0 ? tb0 : tb1;
   };
-  // With three buffers q has landed before the first tile loads go out: the
-  // compiler otherwise waits, at the entry of the tile loop (whose MFMAs read
-  // q), for every load outstanding, the two tiles in flight included.
-  if constexpr (NBUF > 2) wait_vmcnt<0>();
   for (int clo = lo; clo < hi; clo += LCAP) {
     const int n_ent = min(hi - clo, LCAP);
     const int ntiles = (n_ent + TR - 1) / TR;
-    // NBUF buffers: tiles n+1 .. n+NBUF-1 load while tile n is computed.
-    // With two, the refill past the last tile is skipped.  With three, every
-    // step issues one refill (a tile past the last loads the zero row) and
-    // the steps come in unconditional rounds of three, whose steps past the
-    // last tile only wait, pass the barrier and refill: the number of loads
-    // in flight is then the same at every wait, and no branch joins paths
-    // with different loads outstanding (at such joins the compiler waits for
-    // all of them, draining the pipeline).
-    uint64_t addr[NBUF] = {};  // per buffer: the address its last loads read
+    // two buffers: tile n+1 loads while tile n is computed (the refill past
+    // the last tile is skipped)
+    uint64_t addr[2] = {};  // per buffer: the address its last loads read
     addr[0] = issue(tb0, 0, ntiles);
-    if constexpr (NBUF > 2) addr[1] = issue(tb1, 1, ntiles);
     // one pipeline step on buffer b (a compile-time constant)
     auto step = [&](auto bconst, int n) __attribute__((always_inline)) {
-      constexpr int b = decltype(bconst)::value;
-      // tile n landed (with three buffers tile n+1's L loads may still be out)
-      wait_vmcnt<(NBUF - 2) * L>();
+      constexpr int b = decltype(bconst)::value, bn = b ^ 1;
+      wait_vmcnt<0>();  // tile n landed
       keep_live(addr[b]);  // its loads are done: their address may go
       barrier_raw();
       // refill the buffer every wave finished with in the previous step
-      constexpr int bn = (b + NBUF - 1) % NBUF;
-      auto refill = [&]() __attribute__((always_inline)) {
-        if (NBUF > 2 || n + 1 < ntiles)
-          addr[bn] = issue(buf(std::integral_constant<int, bn>{}), n + NBUF - 1, ntiles);
-      };
-      if constexpr (KRH && NBUF > 2) {
-        // the refill goes out after the tile's QK^T (it still has two steps
-        // to land); a step past the last tile only refills
-        if (n < ntiles)
-          compute_rh(buf(bconst), n, refill);
-        else
-          refill();
-      } else if constexpr (KRH) {
-        refill();
-        compute_rh(buf(bconst), n, [] {});
-      } else {
-        refill();
+      if (n + 1 < ntiles) addr[bn] = issue(buf(std::integral_constant<int, bn>{}), n + 1, ntiles);
+      if constexpr (KRH)
+        compute_rh(buf(bconst), n);
+      else
         compute(buf(bconst), n);
-      }
     };
-    if constexpr (NBUF > 2) {
-      for (int n0 = 0; n0 < ntiles; n0 += 3) {
-        step(std::integral_constant<int, 0>{}, n0);
-        step(std::integral_constant<int, 1>{}, n0 + 1);
-        step(std::integral_constant<int, 2>{}, n0 + 2);
-      }
-      wait_vmcnt<0>();  // the refills past the last tile
-    } else {
-      for (int n0 = 0; n0 < ntiles; n0 += 2) {
-        step(std::integral_constant<int, 0>{}, n0);
-        if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
-      }
+    for (int n0 = 0; n0 < ntiles; n0 += 2) {
+      step(std::integral_constant<int, 0>{}, n0);
+      if (n0 + 1 < ntiles) step(std::integral_constant<int, 1>{}, n0 + 1);
     }
-#pragma unroll
-    for (int b = 0; b < NBUF; ++b) keep_live(addr[b]);
+    keep_live(addr[0]);
+    keep_live(addr[1]);
     barrier_raw();  // list_s and the buffers are reused by the next chunk
     const int nxt = clo + LCAP;
     if (nxt < hi) {
@@ -1186,6 +1148,449 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
     fused_combine<NT>(p, unit, tok, hblk * kHeadsPerBlock,
                       min(kHeadsPerBlock, p.heads - hblk * kHeadsPerBlock), split, tb0,
                       (uint32_t*)tb1);
+}
+
+// ---------------------------------------------------------------------------
+// 64-head blocks with role-specialised waves.  Of the eight waves, four
+// (waves 0-3) compute scores: wave (hp, rh) holds Q of head groups 2hp and
+// 2hp+1 over all 576 columns and computes their scores for tile rows
+// 16 rh .. +15, each operand read feeding two MFMAs; the other four (waves
+// 4-7) hold O of all 64 heads over 128 of the 512 value columns, accumulate
+// the PV and issue the tile loads.  A SIMD carries one wave of each kind, so
+// tile n+1's scores and tile n's PV run side by side.  Per tile step n (one
+// barrier): the score waves settle tile n's weights (the rare rescale when a
+// head's maximum grows by more than 2^8, agreed between the two row halves)
+// and compute tile n+1's; the PV waves apply tile n's rescale factors and
+// accumulate its PV, and refill the buffer tile n-1 left with tile n+3.
+// Weights, flags and half maxima are double-buffered by tile parity; four
+// tile buffers keep two tiles in flight.  The two kinds run separate loops
+// with the same sequence of barriers, so neither holds the other's registers.
+// ---------------------------------------------------------------------------
+template <int SRC>
+__global__ __launch_bounds__(512)
+__attribute__((amdgpu_waves_per_eu(2)))
+void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_kv, int64_t a_kv_rows,
+                    int a_topk, int a_per_split, int a_nsplit, int a_heads, int a_tokens, int a_q_len,
+                    SplitTail tl) {
+  SplitParams p;
+  p.idx = a_idx;
+  p.q = a_q;
+  p.kv = a_kv;
+  p.kv_rows = a_kv_rows;
+  p.topk = a_topk;
+  p.per_split = a_per_split;
+  p.nsplit = a_nsplit;
+  p.heads = a_heads;
+  p.tokens = a_tokens;
+  p.q_len = a_q_len;
+  p.table = tl.table;
+  p.ctx = tl.ctx;
+  p.out = tl.out;
+  p.lse = tl.lse;
+  p.part_o = tl.part_o;
+  p.part_lse = tl.part_lse;
+  p.sync = tl.sync;
+  p.src = tl.src;
+  p.max_pages = tl.max_pages;
+  p.page_size = tl.page_size;
+  p.merge_polls = tl.merge_polls;
+  p.scale_log2 = tl.scale_log2;
+  constexpr int NT = 512, TR = kTileRows, HG = 4;
+  constexpr int kTileBytes = TR * kRow * 2;
+  constexpr int LCAP = 1024;  // list entries staged at a time, beside four tile buffers
+  constexpr int LI = LCAP / NT;
+  constexpr int NTD = 256;                      // loading threads: the four PV waves
+  constexpr int L = TR * kRowGran / NTD;        // 9 loads per loading lane per tile
+  constexpr int CBP = 8;                        // 16-column blocks of O per PV wave
+  static_assert(TR == 32 && L == 9, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tb2[kTileBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t tb3[kTileBytes];
+  __shared__ __attribute__((aligned(16))) int list_s[LCAP];
+  // bf16 weights as PV B operands [parity][head group][g][head][8]
+  __shared__ __attribute__((aligned(16))) u32x4 ps[2 * HG * 64];
+  // half maxima [parity][group][row half][head], flags [parity][score wave]
+  __shared__ float rmax_s[2 * HG * 2 * 16];
+  __shared__ __attribute__((aligned(16))) int rflag_s[2 * 4];
+  __shared__ float alpha_s[HG * 16];
+  __shared__ float rsum_s[HG * 2 * 16];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int l16 = lane & 15;
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int wg = xcd_contiguous(blockIdx.x, gridDim.x);
+  constexpr int kHeadsPerBlock = 64;
+  const int hblocks = (p.heads + kHeadsPerBlock - 1) / kHeadsPerBlock;
+  const bool hb_fast = p.per_split >= 8 * TR;
+  const int hblk = hb_fast ? wg % hblocks : (wg / p.nsplit) % hblocks;
+  const int split = hb_fast ? (wg / hblocks) % p.nsplit : wg % p.nsplit;
+  const int tok = wg / hblocks / p.nsplit;
+  const int unit = tok * hblocks + hblk;
+
+  const int lo = min(split * p.per_split, p.topk);
+  const int hi = min(lo + p.per_split, p.topk);
+  const int32_t* idx_row = p.idx ? p.idx + (int64_t)tok * p.topk : nullptr;
+  const int seq = SRC == kSrcRows ? 0 : tok / p.q_len;
+  int ctx_seq = 0;
+  if (SRC == kSrcDense) ctx_seq = p.ctx[seq];
+  const int32_t* tab = SRC != kSrcRows && p.table ? p.table + (int64_t)seq * p.max_pages : nullptr;
+  auto entry = [&](int e) __attribute__((always_inline)) -> int32_t {
+    if constexpr (SRC == kSrcRows) return idx_row[e];
+    const int32_t pos = SRC == kSrcDense ? (e < ctx_seq ? e : -1) : idx_row[e];
+    if (!tab || pos < 0) return pos;
+    const int pg_i = pos / p.page_size;
+    if (pg_i >= p.max_pages) return -1;
+    const int32_t pg = tab[pg_i];
+    if (pg < 0) return -1;
+    const int64_t row = (int64_t)pg * p.page_size + (pos - pg_i * p.page_size);
+    return row < p.kv_rows && row <= 0x7fffffff ? (int32_t)row : -1;
+  };
+  // the sequence's page-table slice staged in LDS (in the weights area, idle
+  // whenever the list is staged) when it fits
+  constexpr int kTabStage = 512;
+  constexpr int TI = (kTabStage + NT - 1) / NT;
+  const bool tab_lds = SRC == kSrcPositions && tab != nullptr && p.max_pages <= kTabStage;
+  int32_t* const tab_stage = (int32_t*)ps;
+  int tv[TI];
+  if (tab_lds) {
+#pragma unroll
+    for (int u = 0; u < TI; ++u) {
+      const int i = u * NT + tid;
+      tv[u] = i < p.max_pages ? tab[i] : -1;
+    }
+  }
+  int lv[LI];
+  auto load_list = [&](int clo, int n_ent) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < LI; ++u) {
+      const int e = clo + min(u * NT + tid, n_ent - 1);
+      lv[u] = tab_lds ? idx_row[e] : entry(e);
+    }
+  };
+  if (lo < hi) load_list(lo, min(hi - lo, LCAP));
+  const uint32_t kv32 = rows32(p.kv_rows);
+  auto store_list = [&](int n_ent) __attribute__((always_inline)) {
+    if (tab_lds) {
+      int32_t* ts = tab_stage;
+#pragma unroll
+      for (int u = 0; u < TI; ++u) {
+        const int i = u * NT + tid;
+        if (i < kTabStage) ts[i] = tv[u];
+      }
+      barrier_lds();
+#pragma unroll
+      for (int u = 0; u < LI; ++u) {
+        const int32_t pos = lv[u];
+        const int pg_i = pos / p.page_size;
+        const bool in_tab = pos >= 0 && pg_i < p.max_pages;
+        const int32_t pg_s = ts[in_tab ? pg_i : 0];
+        const int32_t pg = in_tab ? pg_s : -1;
+        const int64_t row = (int64_t)pg * p.page_size + (pos - pg_i * p.page_size);
+        lv[u] = pg >= 0 && row < p.kv_rows && row <= 0x7fffffff ? (int32_t)row : -1;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < LI; ++u) {
+      const int e = u * NT + tid;
+      list_s[e] = (e < n_ent && (uint32_t)lv[u] < kv32) ? lv[u] : -1;
+    }
+    barrier_lds();
+  };
+  auto buf = [&](auto bconst) __attribute__((always_inline)) -> uint8_t* {
+    constexpr int b = decltype(bconst)::value;
+    return b == 0 ? tb0 : b == 1 ? tb1 : b == 2 ? tb2 : tb3;
+  };
+  // a chunk's list is restaged between chunks by every wave, the same way in
+  // both roles (barriers included)
+  auto next_chunk = [&](int clo) __attribute__((always_inline)) {
+    barrier_lds();
+    const int nxt = clo + LCAP;
+    if (nxt < hi) {
+      load_list(nxt, min(hi - nxt, LCAP));
+      store_list(min(hi - nxt, LCAP));
+    }
+  };
+
+  float lse_out = -__builtin_inff();  // score waves: the LSE of this lane's head (rows 0-15 waves)
+  bool lse_w = false;
+  int lse_h = 0;
+
+  if (wave_u < 4) {
+    // ============================ score waves ============================
+    const int hp = wave_u & 1, rh = wave_u >> 1;
+    bf16x8 qf[2][kKSteps];
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const int hq = hblk * kHeadsPerBlock + (2 * hp + gi) * 16 + l16;
+      const u32x4* qrow = hq < p.heads ? (const u32x4*)(p.q + ((int64_t)tok * p.heads + hq) * kRow) + g
+                                       : g_zero_row + g;
+#pragma unroll
+      for (int k = 0; k < kKSteps; ++k) qf[gi][k] = __builtin_bit_cast(bf16x8, qrow[4 * k]);
+    }
+    if (lo < hi) store_list(min(hi - lo, LCAP));
+    const int hq = hsw(l16);
+    const int qk_e = l16 * 128 + (g ^ hq) * 16 + rh * 16 * 128;
+    const int qk_o = l16 * 128 + ((g ^ hq) ^ 4) * 16 + rh * 16 * 128;
+    float m_run[2] = {-__builtin_inff(), -__builtin_inff()}, l_run[2] = {0.f, 0.f};
+    float sc[2][4], pw[2][4], mxh[2] = {0.f, 0.f};
+    auto weights = [&](u32x4* wb) __attribute__((always_inline)) {
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const float m_use = m_run[gi] == -__builtin_inff() ? 0.f : m_run[gi];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pw[gi][i] = __builtin_amdgcn_exp2f(sc[gi][i] - m_use);
+        *(u32x2*)((uint8_t*)wb + ((2 * hp + gi) * 64 + lane) * 16 + 8 * rh) =
+            u32x2{pack_bf16x2(pw[gi][0], pw[gi][1]), pack_bf16x2(pw[gi][2], pw[gi][3])};
+      }
+    };
+    // scores of tile t into weights wb, flag fb, half maxima mb
+    auto qk = [&](const uint8_t* T, int t, u32x4* wb, float* mb, int* fb) __attribute__((always_inline)) {
+      floatx4 acc[2][2] = {{floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}},
+                           {floatx4{0.f, 0.f, 0.f, 0.f}, floatx4{0.f, 0.f, 0.f, 0.f}}};
+      constexpr int D = 6;
+      bf16x8 op[D];
+#pragma unroll
+      for (int k = 0; k < D; ++k)
+        op[k] = *(const bf16x8*)(T + ((k & 1) ? qk_o : qk_e) + (k >> 1) * TR * 128);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int k = 0; k < kKSteps; ++k) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi)
+          acc[gi][k & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(op[k % D], qf[gi][k], acc[gi][k & 1], 0, 0, 0);
+        if (k + D < kKSteps)
+          op[k % D] = *(const bf16x8*)(T + (((k + D) & 1) ? qk_o : qk_e) + ((k + D) >> 1) * TR * 128);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rh + 4 * g);
+      bool grow = false;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const floatx4 sv = acc[gi][0] + acc[gi][1];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[gi][i] = r4[i] >= 0 ? sv[i] * p.scale_log2 : -__builtin_inff();
+        mxh[gi] = max4_lanes(fmaxf(fmaxf(sc[gi][0], sc[gi][1]), fmaxf(sc[gi][2], sc[gi][3])));
+        grow |= mxh[gi] > m_run[gi] + kRescaleLog2;
+      }
+      weights(wb);
+      const int need_w = __any(grow);
+      if (lane == 0) fb[wave_u] = need_w;
+      if (g == 0) {
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) mb[((2 * hp + gi) * 2 + rh) * 16 + l16] = mxh[gi];
+      }
+    };
+    // tile n's weights settled (rare path with its barrier), its share of
+    // the sums taken
+    auto settle = [&](u32x4* wb, const float* mb, const int* fb) __attribute__((always_inline)) {
+      const i32x4 fa = *(const i32x4*)fb;
+      if (fa[0] | fa[1] | fa[2] | fa[3]) {  // the same in every wave
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          const float mt = fmaxf(mxh[gi], mb[((2 * hp + gi) * 2 + (rh ^ 1)) * 16 + l16]);
+          float alpha = 1.f;
+          if (mt > m_run[gi] + kRescaleLog2) {
+            const float m_new = fmaxf(m_run[gi], mt);
+            alpha = __builtin_amdgcn_exp2f(m_run[gi] - m_new);
+            l_run[gi] *= alpha;
+            m_run[gi] = m_new;
+          }
+          if (rh == 0 && g == 0) alpha_s[(2 * hp + gi) * 16 + l16] = alpha;
+        }
+        weights(wb);
+        barrier_lds();
+      }
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) l_run[gi] += pw[gi][i];
+    };
+    for (int clo = lo; clo < hi; clo += LCAP) {
+      const int ntiles = (min(hi - clo, LCAP) + TR - 1) / TR;
+      barrier_raw();  // tile 0 landed
+      qk(tb0, 0, ps, rmax_s, rflag_s);
+      auto step = [&](auto jc, int n) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value, b1 = (j + 1) % 4, pb = j & 1;
+        barrier_lds();
+        if (n < ntiles) settle(ps + pb * HG * 64, rmax_s + pb * HG * 32, rflag_s + pb * 4);
+        if (n + 1 < ntiles)
+          qk(buf(std::integral_constant<int, b1>{}), n + 1, ps + (pb ^ 1) * HG * 64,
+             rmax_s + (pb ^ 1) * HG * 32, rflag_s + (pb ^ 1) * 4);
+      };
+      for (int n0 = 0; n0 < ntiles; n0 += 4) {
+        step(std::integral_constant<int, 0>{}, n0);
+        step(std::integral_constant<int, 1>{}, n0 + 1);
+        step(std::integral_constant<int, 2>{}, n0 + 2);
+        step(std::integral_constant<int, 3>{}, n0 + 3);
+      }
+      next_chunk(clo);
+    }
+    // this row half's share of each head's sum, then the LSE (rows 0-15 waves)
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const float lh = sum4_lanes(l_run[gi]);
+      if (g == 0) rsum_s[((2 * hp + gi) * 2 + rh) * 16 + l16] = lh;
+    }
+    barrier_lds();
+    if (rh == 0 && g == 0) {
+      // two heads per lane: groups 2hp and 2hp+1; the second is written below
+      const float l0 = rsum_s[((2 * hp) * 2) * 16 + l16] + rsum_s[((2 * hp) * 2 + 1) * 16 + l16];
+      const float l1 = rsum_s[((2 * hp + 1) * 2) * 16 + l16] + rsum_s[((2 * hp + 1) * 2 + 1) * 16 + l16];
+      const int h0 = hblk * kHeadsPerBlock + (2 * hp) * 16 + l16;
+      const float lse0 = l0 > 0.f ? m_run[0] * kLn2 + __logf(l0) : -__builtin_inff();
+      lse_out = l1 > 0.f ? m_run[1] * kLn2 + __logf(l1) : -__builtin_inff();
+      lse_h = h0 + 16;
+      lse_w = true;
+      if (h0 < p.heads) {
+        const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + h0;
+        if (p.nsplit == 1)
+          p.lse[(int64_t)tok * p.heads + h0] = lse0;
+        else if (p.sync)
+          __hip_atomic_store(p.part_lse + slot, lse0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+          p.part_lse[slot] = lse0;
+      }
+    }
+  } else {
+    // ============================== PV waves ==============================
+    const int c = wave_u - 4;  // value columns 128 c .. +127
+    floatx4 oacc[HG][CBP];
+#pragma unroll
+    for (int gi = 0; gi < HG; ++gi)
+#pragma unroll
+      for (int cb = 0; cb < CBP; ++cb) oacc[gi][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
+    if (lo < hi) store_list(min(hi - lo, LCAP));
+    const int tr_e = l16 >> 2, tr_b0 = (l16 >> 1) & 1, tr_b1 = l16 & 1;
+    const int tr_h = hsw(4 * g + tr_e);
+    int pv_base[4];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      pv_base[q4] = (4 * g + tr_e) * 128 + ((2 * q4 + tr_b0) ^ tr_h) * 16 + 8 * tr_b1 + 2 * c * TR * 128;
+    // tile loads: this wave's rows 8c .. 8c+7 of the tile, granule lane%8
+    const int dma_row = 8 * c + (lane >> 3);
+    const int dma_gran = (lane & 7) ^ hsw(dma_row);
+    auto issue = [&](uint8_t* bp, int t, int ntiles) __attribute__((always_inline)) -> uint64_t {
+      const int32_t r = t < ntiles ? list_s[min(t * TR + dma_row, LCAP - 1)] : -1;
+      const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
+      const u32x4* src = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran;
+      dma_tile<NTD, 1>(src, bp + c * 64 * 16, std::make_integer_sequence<int, L>{});
+      return (uint64_t)(uintptr_t)src;
+    };
+    auto pv = [&](const uint8_t* T, const u32x4* wb) __attribute__((always_inline)) {
+      bf16x8 pq[HG];
+#pragma unroll
+      for (int gi = 0; gi < HG; ++gi) pq[gi] = __builtin_bit_cast(bf16x8, wb[gi * 64 + lane]);
+#pragma unroll
+      for (int cb = 0; cb < CBP; ++cb) {
+        const int off = pv_base[cb & 3] + (cb >> 2) * TR * 128;
+        const shortx4 v2[2] = {lds_tr16(T + off), lds_tr16(T + off + 16 * 128)};
+        const bf16x8 vt = __builtin_bit_cast(bf16x8, v2);
+#pragma unroll
+        for (int gi = 0; gi < HG; ++gi)
+          oacc[gi][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vt, pq[gi], oacc[gi][cb], 0, 0, 0);
+      }
+    };
+    // the rescale factors of tile n when the score waves moved a maximum
+    auto settle = [&](const int* fb) __attribute__((always_inline)) {
+      const i32x4 fa = *(const i32x4*)fb;
+      if (fa[0] | fa[1] | fa[2] | fa[3]) {  // the same in every wave
+        barrier_lds();
+        float al[HG];
+        bool scale = false;
+#pragma unroll
+        for (int gi = 0; gi < HG; ++gi) {
+          al[gi] = alpha_s[gi * 16 + l16];
+          scale |= al[gi] != 1.f;
+        }
+        if (__any(scale)) {
+#pragma unroll
+          for (int gi = 0; gi < HG; ++gi)
+#pragma unroll
+            for (int cb = 0; cb < CBP; ++cb) oacc[gi][cb] *= al[gi];
+        }
+      }
+    };
+    for (int clo = lo; clo < hi; clo += LCAP) {
+      const int ntiles = (min(hi - clo, LCAP) + TR - 1) / TR;
+      uint64_t addr[4] = {};
+      addr[0] = issue(tb0, 0, ntiles);
+      addr[1] = issue(tb1, 1, ntiles);
+      addr[2] = issue(tb2, 2, ntiles);
+      wait_vmcnt<2 * L>();  // tile 0 landed
+      keep_live(addr[0]);
+      barrier_raw();
+      auto step = [&](auto jc, int n) __attribute__((always_inline)) {
+        constexpr int j = decltype(jc)::value, b1 = (j + 1) % 4, bf = (j + 3) % 4, pb = j & 1;
+        wait_vmcnt<L>();  // tile n+1 landed (tile n+2's loads may be out)
+        keep_live(addr[b1]);
+        barrier_lds();
+        addr[bf] = issue(buf(std::integral_constant<int, bf>{}), n + 3, ntiles);
+        if (n < ntiles) {
+          settle(rflag_s + pb * 4);
+          pv(buf(jc), ps + pb * HG * 64);
+        }
+      };
+      for (int n0 = 0; n0 < ntiles; n0 += 4) {
+        step(std::integral_constant<int, 0>{}, n0);
+        step(std::integral_constant<int, 1>{}, n0 + 1);
+        step(std::integral_constant<int, 2>{}, n0 + 2);
+        step(std::integral_constant<int, 3>{}, n0 + 3);
+      }
+      wait_vmcnt<0>();  // the refills past the last tile
+#pragma unroll
+      for (int b = 0; b < 4; ++b) keep_live(addr[b]);
+      next_chunk(clo);
+    }
+    barrier_lds();  // the score waves' sums are in
+#pragma unroll
+    for (int gi = 0; gi < HG; ++gi) {
+      const float l = rsum_s[(gi * 2) * 16 + l16] + rsum_s[(gi * 2 + 1) * 16 + l16];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      const int h = hblk * kHeadsPerBlock + gi * 16 + l16;
+      if (h >= p.heads) continue;
+      const int64_t th = (int64_t)tok * p.heads + h;
+      if (p.nsplit == 1) {
+        uint16_t* orow = p.out + th * kDV;
+#pragma unroll
+        for (int cb = 0; cb < CBP; ++cb) {
+          const int c0 = (c * CBP + cb) * 16 + 4 * g;
+          const floatx4 o = oacc[gi][cb] * inv;
+          *(u32x2*)(orow + c0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+        }
+      } else {
+        const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + h;
+        float* orow = p.part_o + slot * kDV;
+        if (p.sync) {
+#pragma unroll
+          for (int cb = 0; cb < CBP; ++cb) st_agent(orow + (c * CBP + cb) * 16 + 4 * g, oacc[gi][cb] * inv);
+        } else {
+#pragma unroll
+          for (int cb = 0; cb < CBP; ++cb) {
+            const int c0 = (c * CBP + cb) * 16 + 4 * g;
+            *(floatx4*)(orow + c0) = oacc[gi][cb] * inv;
+          }
+        }
+      }
+    }
+  }
+  // the second head of each score lane (group 2hp+1)
+  if (lse_w && lse_h < p.heads) {
+    const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + lse_h;
+    if (p.nsplit == 1)
+      p.lse[(int64_t)tok * p.heads + lse_h] = lse_out;
+    else if (p.sync)
+      __hip_atomic_store(p.part_lse + slot, lse_out, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+      p.part_lse[slot] = lse_out;
+  }
+  if (p.sync && p.nsplit > 1)  // single launch: merge the unit's partials here
+    fused_combine<NT>(p, unit, tok, hblk * kHeadsPerBlock, min(kHeadsPerBlock, p.heads - hblk * kHeadsPerBlock),
+                      split, tb0, (uint32_t*)tb1);
 }
 
 // The workgroup's index in the combine grid.  With at least as many tokens as
@@ -1365,8 +1770,8 @@ void combine_wide_kernel(const float* a_part_o, const float* a_part_lse, uint16_
 // exchange slots of partial scores (one 16-row block of 16 heads = 1 KiB per
 // slot, head group and row block), with row halves the bf16 weights, the
 // rescale factors and two floats and a flag per (wave, owned head)
-constexpr int split_lds_bytes(int waves, int ncs, int gpw, int ks, int nbuf = 2) {
-  return nbuf * kTileRows * kRow * 2 + split_list_cap(ncs, ks) * 4 +
+constexpr int split_lds_bytes(int waves, int ncs, int gpw, int ks) {
+  return 2 * kTileRows * kRow * 2 + split_list_cap(ncs, ks) * 4 +
          (ks == 2 ? (waves / ncs) * 2 * gpw * (kTileRows / 16) * 64 * 16 : 0) +
          (ks == 1 && gpw == 4 ? gpw * 64 * 16 + gpw * 16 * 4 + 2 * waves * 16 * 4 + waves * 4 : 0);
 }
@@ -1389,7 +1794,7 @@ static SplitTail split_tail(const SplitParams& p) {
   return t;
 }
 
-template <int HG, int NCS, int GPW, int TR, int KS, int NB = 2>
+template <int HG, int NCS, int GPW, int TR, int KS>
 static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t st) {
   static_assert(TR == kTileRows, "the planner's tile");
   const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
@@ -1397,17 +1802,17 @@ static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t 
   const SplitTail t = split_tail(p);
   switch (p.src) {
     case kSrcPositions:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcPositions>), grid, block, 0,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcPositions>), grid, block, 0,
                          st, p.idx, p.q, p.kv, p.kv_rows, p.topk, p.per_split, p.nsplit, p.heads,
                          p.tokens, p.q_len, t);
       break;
     case kSrcDense:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcDense>), grid, block, 0, st,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcDense>), grid, block, 0, st,
                          p.idx, p.q, p.kv, p.kv_rows, p.topk, p.per_split, p.nsplit, p.heads,
                          p.tokens, p.q_len, t);
       break;
     default:
-      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, NB, kSrcRows>), grid, block, 0, st,
+      hipLaunchKernelGGL((split_kernel<HG, NCS, GPW, TR, KS, kSrcRows>), grid, block, 0, st,
                          p.idx, p.q, p.kv, p.kv_rows, p.topk, p.per_split, p.nsplit, p.heads,
                          p.tokens, p.q_len, t);
   }
@@ -1420,27 +1825,50 @@ static hipError_t launch_split_t(const SplitParams& p, int hblocks, hipStream_t 
 //    two workgroups per CU;
 //  * up to 32 heads: 4 waves = 2 head groups x 2 column halves, each wave
 //    all of QK^T; two workgroups per CU;
-//  * more (64-head blocks): 8 waves in row halves (each wave the scores of
-//    one head group over half the tile rows and all of K, and O of all 64
-//    heads over an eighth of the value columns); one workgroup per CU (about
-//    250 registers: two waves per SIMD), with a third tile buffer over long
-//    slices.
+//  * more (64-head blocks): over slices of at least kDeepTiles tiles,
+//    split64_kernel (four score waves holding Q of two head groups each and
+//    four PV waves holding O, four tile buffers); over shorter slices 8
+//    waves in row halves (each wave the scores of one head group over half
+//    the tile rows and all of K, and O of all 64 heads over an eighth of the
+//    value columns).  Either is one workgroup per CU (two waves per SIMD).
 static_assert(kCuLdsBytes / split_lds_bytes(4, 4, 1, 2) == 2, "two 16-head workgroups per CU");
 static_assert(kCuLdsBytes / split_lds_bytes(4, 2, 1, 1) == 2, "two 32-head workgroups per CU");
-static_assert(split_lds_bytes(8, 8, 4, 1, 3) <= kCuLdsBytes, "one 64-head workgroup per CU");
+static_assert(split_lds_bytes(8, 8, 4, 1) <= kCuLdsBytes, "one 64-head workgroup per CU");
 
-// 64-head blocks over slices of at least this many tiles take three tile
-// buffers (the rounds of three steps pad a short slice's tail).  Measured:
-// 64 x 64 heads with 16-tile slices 39.4 us at 4 against 40.1 us at 32.
+// 64-head blocks over slices of at least this many tiles take split64_kernel
+// (its rounds of four steps pad a short slice's tail with refills past the
+// end).  Measured against the row halves: 128 x 128 heads with 64-tile
+// slices 103 -> 90 us per launch; 72 folded heads over 16384 positions
+// (4-tile slices) 21.6 -> 20.7 us; over 4096 (1-tile slices) equal; 64 x 64
+// heads with 2-tile slices 139 -> 159 us.
 constexpr int kDeepTiles = 4;
+
+static hipError_t launch_split64(const SplitParams& p, int hblocks, hipStream_t st) {
+  const int64_t nwg = (int64_t)p.nsplit * p.tokens * hblocks;
+  const dim3 grid((unsigned)nwg), block(512);
+  const SplitTail t = split_tail(p);
+  switch (p.src) {
+    case kSrcPositions:
+      hipLaunchKernelGGL((split64_kernel<kSrcPositions>), grid, block, 0, st, p.idx, p.q, p.kv, p.kv_rows,
+                         p.topk, p.per_split, p.nsplit, p.heads, p.tokens, p.q_len, t);
+      break;
+    case kSrcDense:
+      hipLaunchKernelGGL((split64_kernel<kSrcDense>), grid, block, 0, st, p.idx, p.q, p.kv, p.kv_rows,
+                         p.topk, p.per_split, p.nsplit, p.heads, p.tokens, p.q_len, t);
+      break;
+    default:
+      hipLaunchKernelGGL((split64_kernel<kSrcRows>), grid, block, 0, st, p.idx, p.q, p.kv, p.kv_rows,
+                         p.topk, p.per_split, p.nsplit, p.heads, p.tokens, p.q_len, t);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_split(const SplitParams& p, hipStream_t st) {
   if (p.heads <= 16) return launch_split_t<1, 4, 1, 32, 2>(p, 1, st);
   if (p.heads <= 32) return launch_split_t<2, 2, 1, 32, 1>(p, 1, st);
   const int hblocks = (p.heads + 63) / 64;
-  if ((p.per_split + kTileRows - 1) / kTileRows >= kDeepTiles)
-    return launch_split_t<4, 8, 4, 32, 1, 3>(p, hblocks, st);
-  return launch_split_t<4, 8, 4, 32, 1, 2>(p, hblocks, st);
+  if ((p.per_split + kTileRows - 1) / kTileRows >= kDeepTiles) return launch_split64(p, hblocks, st);
+  return launch_split_t<4, 8, 4, 32, 1>(p, hblocks, st);
 }
 
 int split_heads_per_block(int heads) { return heads <= 16 ? 16 : heads <= 32 ? 32 : 64; }

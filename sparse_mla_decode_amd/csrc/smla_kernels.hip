@@ -1197,7 +1197,13 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
   p.scale_log2 = tl.scale_log2;
   constexpr int NT = 512, TR = kTileRows, HG = 4;
   constexpr int kTileBytes = TR * kRow * 2;
-  constexpr int LCAP = 1024;  // list entries staged at a time, beside four tile buffers
+  // the list stage is a ring of LCAP entries (32 tiles) beside four tile
+  // buffers: the score waves load the entries of tiles n+16 .. n+31 at step
+  // n (n a multiple of 16) and store them one step later (two for positions,
+  // whose page-table lookup is a second load) into the slots of tiles
+  // n-16 .. n-1, which every wave is done with; so a slice of any length
+  // streams through without draining the tile pipeline
+  constexpr int LCAP = 1024;
   constexpr int LI = LCAP / NT;
   constexpr int NTD = 256;                      // loading threads: the four PV waves
   constexpr int L = TR * kRowGran / NTD;        // 9 loads per loading lane per tile
@@ -1305,16 +1311,10 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
     constexpr int b = decltype(bconst)::value;
     return b == 0 ? tb0 : b == 1 ? tb1 : b == 2 ? tb2 : tb3;
   };
-  // a chunk's list is restaged between chunks by every wave, the same way in
-  // both roles (barriers included)
-  auto next_chunk = [&](int clo) __attribute__((always_inline)) {
-    barrier_lds();
-    const int nxt = clo + LCAP;
-    if (nxt < hi) {
-      load_list(nxt, min(hi - nxt, LCAP));
-      store_list(min(hi - nxt, LCAP));
-    }
-  };
+  const int n_all = hi - lo;                  // entries of the slice
+  const int ntiles = (n_all + TR - 1) / TR;   // its tiles
+  // the ring slot of entry e (tile-aligned: a tile never wraps)
+  auto ring = [&](int e) __attribute__((always_inline)) -> int { return e & (LCAP - 1); };
 
   float lse_out = -__builtin_inff();  // score waves: the LSE of this lane's head (rows 0-15 waves)
   bool lse_w = false;
@@ -1332,7 +1332,41 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
 #pragma unroll
       for (int k = 0; k < kKSteps; ++k) qf[gi][k] = __builtin_bit_cast(bf16x8, qrow[4 * k]);
     }
-    if (lo < hi) store_list(min(hi - lo, LCAP));
+    if (lo < hi) store_list(min(n_all, LCAP));
+    // ring refill: two entries per score lane (256 lanes, 16 tiles)
+    int rv[2] = {-1, -1}, rt[2] = {-1, -1};
+    auto ring_load = [&](int n) __attribute__((always_inline)) {  // tiles n+16 .. n+31
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = (n + 16) * TR + u * 256 + tid;
+        if constexpr (SRC == kSrcDense)
+          rv[u] = e < n_all && lo + e < ctx_seq ? lo + e : -1;
+        else
+          rv[u] = e < n_all ? idx_row[lo + e] : -1;
+      }
+    };
+    auto ring_table = [&]() __attribute__((always_inline)) {  // positions: their page ids
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int pos = rv[u];
+        const int pg_i = pos >= 0 ? pos / p.page_size : 0;
+        rt[u] = tab && pos >= 0 && pg_i < p.max_pages ? tab[pg_i] : -1;
+      }
+    };
+    auto ring_store = [&](int n) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int e = (n + 16) * TR + u * 256 + tid;
+        int32_t v = rv[u];
+        if constexpr (SRC != kSrcRows) {  // a position: mapped through the page table, if any
+          const int pos = rv[u];
+          const int pg_i = pos >= 0 ? pos / p.page_size : 0;
+          const int64_t row = (int64_t)rt[u] * p.page_size + (pos - pg_i * p.page_size);
+          v = !tab ? pos : (rt[u] >= 0 && pos >= 0 && row < p.kv_rows && row <= 0x7fffffff ? (int32_t)row : -1);
+        }
+        list_s[ring(e)] = (e < n_all && (uint32_t)v < kv32) ? v : -1;
+      }
+    };
     const int hq = hsw(l16);
     const int qk_e = l16 * 128 + (g ^ hq) * 16 + rh * 16 * 128;
     const int qk_o = l16 * 128 + ((g ^ hq) ^ 4) * 16 + rh * 16 * 128;
@@ -1367,7 +1401,7 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
           op[k % D] = *(const bf16x8*)(T + (((k + D) & 1) ? qk_o : qk_e) + ((k + D) >> 1) * TR * 128);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const i32x4 r4 = *(const i32x4*)(list_s + t * TR + 16 * rh + 4 * g);
+      const i32x4 r4 = *(const i32x4*)(list_s + ring(t * TR) + 16 * rh + 4 * g);
       bool grow = false;
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {
@@ -1410,13 +1444,23 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
 #pragma unroll
         for (int i = 0; i < 4; ++i) l_run[gi] += pw[gi][i];
     };
-    for (int clo = lo; clo < hi; clo += LCAP) {
-      const int ntiles = (min(hi - clo, LCAP) + TR - 1) / TR;
+    if (lo < hi) {
       barrier_raw();  // tile 0 landed
       qk(tb0, 0, ps, rmax_s, rflag_s);
       auto step = [&](auto jc, int n) __attribute__((always_inline)) {
         constexpr int j = decltype(jc)::value, b1 = (j + 1) % 4, pb = j & 1;
         barrier_lds();
+        // ring refill (uniform conditions)
+        const int nr = n & ~15;
+        if (nr >= 16 && (nr + 16) * TR < n_all) {
+          if (n == nr) ring_load(nr);
+          if constexpr (SRC != kSrcRows) {
+            if (n == nr + 1) ring_table();
+            if (n == nr + 2) ring_store(nr);
+          } else {
+            if (n == nr + 1) ring_store(nr);
+          }
+        }
         if (n < ntiles) settle(ps + pb * HG * 64, rmax_s + pb * HG * 32, rflag_s + pb * 4);
         if (n + 1 < ntiles)
           qk(buf(std::integral_constant<int, b1>{}), n + 1, ps + (pb ^ 1) * HG * 64,
@@ -1428,7 +1472,7 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
         step(std::integral_constant<int, 2>{}, n0 + 2);
         step(std::integral_constant<int, 3>{}, n0 + 3);
       }
-      next_chunk(clo);
+      barrier_lds();
     }
     // this row half's share of each head's sum, then the LSE (rows 0-15 waves)
 #pragma unroll
@@ -1464,7 +1508,7 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
     for (int gi = 0; gi < HG; ++gi)
 #pragma unroll
       for (int cb = 0; cb < CBP; ++cb) oacc[gi][cb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    if (lo < hi) store_list(min(hi - lo, LCAP));
+    if (lo < hi) store_list(min(n_all, LCAP));
     const int tr_e = l16 >> 2, tr_b0 = (l16 >> 1) & 1, tr_b1 = l16 & 1;
     const int tr_h = hsw(4 * g + tr_e);
     int pv_base[4];
@@ -1474,8 +1518,8 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
     // tile loads: this wave's rows 8c .. 8c+7 of the tile, granule lane%8
     const int dma_row = 8 * c + (lane >> 3);
     const int dma_gran = (lane & 7) ^ hsw(dma_row);
-    auto issue = [&](uint8_t* bp, int t, int ntiles) __attribute__((always_inline)) -> uint64_t {
-      const int32_t r = t < ntiles ? list_s[min(t * TR + dma_row, LCAP - 1)] : -1;
+    auto issue = [&](uint8_t* bp, int t) __attribute__((always_inline)) -> uint64_t {
+      const int32_t r = t < ntiles ? list_s[ring(t * TR) + dma_row] : -1;
       const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
       const u32x4* src = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran;
       dma_tile<NTD, 1>(src, bp + c * 64 * 16, std::make_integer_sequence<int, L>{});
@@ -1515,12 +1559,11 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
         }
       }
     };
-    for (int clo = lo; clo < hi; clo += LCAP) {
-      const int ntiles = (min(hi - clo, LCAP) + TR - 1) / TR;
+    if (lo < hi) {
       uint64_t addr[4] = {};
-      addr[0] = issue(tb0, 0, ntiles);
-      addr[1] = issue(tb1, 1, ntiles);
-      addr[2] = issue(tb2, 2, ntiles);
+      addr[0] = issue(tb0, 0);
+      addr[1] = issue(tb1, 1);
+      addr[2] = issue(tb2, 2);
       wait_vmcnt<2 * L>();  // tile 0 landed
       keep_live(addr[0]);
       barrier_raw();
@@ -1529,7 +1572,7 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
         wait_vmcnt<L>();  // tile n+1 landed (tile n+2's loads may be out)
         keep_live(addr[b1]);
         barrier_lds();
-        addr[bf] = issue(buf(std::integral_constant<int, bf>{}), n + 3, ntiles);
+        addr[bf] = issue(buf(std::integral_constant<int, bf>{}), n + 3);
         if (n < ntiles) {
           settle(rflag_s + pb * 4);
           pv(buf(jc), ps + pb * HG * 64);
@@ -1544,7 +1587,7 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
       wait_vmcnt<0>();  // the refills past the last tile
 #pragma unroll
       for (int b = 0; b < 4; ++b) keep_live(addr[b]);
-      next_chunk(clo);
+      barrier_lds();
     }
     barrier_lds();  // the score waves' sums are in
 #pragma unroll

@@ -228,6 +228,31 @@ def test_dense_paged_ragged(smla, nsplit):
     _same_bits((out, lse), ref, f"dense paged nsplit={nsplit}")
 
 
+@pytest.mark.parametrize("nsplit", [1, 2, 0])
+def test_dense_paged_long_contexts(smla, nsplit):
+    """Paged dense, 64 heads, contexts of thousands of positions (one slice
+    streams its list through the stage in several refills, each position
+    mapped through the page table inside the loop), one context empty."""
+    import torch
+    inp = dense_inputs("dense_paged_long", 8250, 3, 1, 64, [3000, 1500, 0], paged=True)
+    dev = to_device(inp, "cuda")
+    table = torch.from_numpy(block_table(inp)).cuda()
+    ctx_len = torch.tensor(inp.ctx, dtype=torch.int32, device="cuda")
+    max_ctx = int(inp.ctx.max())
+    out, lse = _outputs(inp, dev["q"].device)
+    used = smla.smla_decode_dense(dev["q"], dev["kv"], ctx_len, max_ctx, out, lse, inp.scale,
+                                  nsplit, block_table=table, page_size=64)
+    torch.cuda.synchronize()
+    rows = oracle.rows_of_positions(block_table(inp), 64,
+                                    oracle.dense_positions(inp.ctx, max_ctx, inp.q_len), inp.kv_rows)
+    o_r, l_r = oracle.decode(inp.q, inp.kv, rows, inp.scale)
+    assert np.isneginf(l_r[2]).all()
+    _parity(*_host(out, lse), o_r, l_r, f"dense paged long nsplit={nsplit} (used {used})")
+    ref, _ = _rows_call(smla, inp, dev, inp.idx, nsplit,
+                        fold=smla.dense_folds(inp.q_len, inp.heads, max_ctx))
+    _same_bits((out, lse), ref, f"dense paged long nsplit={nsplit}")
+
+
 def test_dense_context_beyond_max(smla):
     """A context longer than max_ctx is attended only up to max_ctx."""
     import torch

@@ -6,7 +6,8 @@ times with the program's own eager work and device synchronisations between
 replays (other calls on the same buffers, fills of the outputs with NaN),
 and checks every replay bit for bit against the eager result of the same
 call.  Covered: smla_decode at NSPLIT 1 and 4 (split and combine kernels),
-and over 64-head slices long enough for three tile buffers,
+and over 64-head slices long enough for the role-specialised kernel (its
+list ring refilled during the call),
 smla_decode_paged, smla_decode_dense (folded), smla_decode_fused (single
 launch, with its synchronisation words) and smla_topk.
 """
@@ -89,9 +90,10 @@ def test_graph_decode(smla, nsplit):
     _replays(fn, [out, lse], disturb)
 
 
-def test_graph_decode_three_buffers(smla):
-    """64 heads over slices of 79 tiles: the three-buffer pipeline (refills
-    of tiles past the last load the zero row) replayed."""
+def test_graph_decode_long_slices(smla):
+    """64 heads over slices of 79 tiles: the role-specialised kernel (four
+    tile buffers, refills past the last tile load the zero row, the list ring
+    refilled every 16 tiles) replayed."""
     inp = flat_inputs("graph3", 9510, 1, 1, 64, 65536, 5000)
     dev = to_device(inp, "cuda")
     out, lse = _bufs(inp)

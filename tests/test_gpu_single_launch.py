@@ -5,7 +5,7 @@ form.
 The two-launch form (smla_split, then smla_combine) is the reference form of
 the merge; both are held to the oracle with the tolerances of the other
 parity tests.  Covered: NSPLIT 2 .. 64 on the 16-, 32- and 64-head kernels
-(the last with two and with three tile buffers), partial head blocks,
+(the last in both its forms: row halves and role-specialised), partial head blocks,
 several tokens, splits that are empty, topk 0; the synchronisation words
 back at zero after every call; one workspace and one set of synchronisation
 words reused across shapes; the wait-free form (merge polls 0: the last
@@ -90,7 +90,7 @@ CASES = [  # name, batch, q_len, heads, topk, kv_rows, nsplits
     ("h8_ragged", 3, 1, 8, 1000, 8192, [7, 33]),
     ("h24", 2, 1, 24, 300, 4096, [4, 10]),
     ("h64", 4, 1, 64, 700, 16384, [2, 5]),
-    ("h64_long", 1, 1, 72, 5000, 65536, [2, 3]),  # slices of 53-79 tiles: three tile buffers
+    ("h64_long", 1, 1, 72, 5000, 65536, [2, 3]),  # slices of 53-79 tiles: the role-specialised kernel
     ("h130", 1, 2, 130, 100, 4096, [4]),
     ("empty_splits", 2, 1, 8, 33, 4096, [64]),   # 1 entry per split: 31 empty splits
 ]

@@ -369,7 +369,19 @@ SMLA_API int smla_combine(const float* part_o, const float* part_lse, void* out,
 // up to 131072 gain, 64 x 32768 loses)
 constexpr int kTopkMultiMinChunks = 12;  // 45057 positions and more
 bool topk_multi_auto(int64_t rows, int max_ctx, int cus) {
-  return rows < 2 * (int64_t)cus && smla::topk_chunks(max_ctx) >= kTopkMultiMinChunks;
+  return rows < 2 * (int64_t)cus && smla::topk_chunks(max_ctx, 1) >= kTopkMultiMinChunks;
+}
+// sub-chunks per chunk workgroup: as many as keep about kTopkChunkWgPerCu
+// chunk workgroups per CU (one when a few rows need every chunk to fill the
+// device)
+#ifndef SMLA_TOPK_WG_PER_CU
+#define SMLA_TOPK_WG_PER_CU 4
+#endif
+constexpr int kTopkChunkWgPerCu = SMLA_TOPK_WG_PER_CU;
+int topk_sub(int64_t rows, int max_ctx, int cus) {
+  const int64_t subs = rows * smla::topk_chunks(max_ctx, 1);
+  const int64_t s = subs / ((int64_t)kTopkChunkWgPerCu * cus);
+  return (int)(s < 1 ? 1 : s > 8 ? 8 : s);
 }
 
 SMLA_API size_t smla_topk_workspace_bytes(int batch, int q_len, int max_ctx) {
@@ -400,16 +412,21 @@ SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, i
   tp.topk = topk;
   tp.ws = nullptr;
   tp.ws_row_bytes = smla::topk_ws_row_bytes(max_ctx);
-  tp.chunks = smla::topk_chunks(max_ctx);
+  tp.sub = 1;
+  tp.chunks = smla::topk_chunks(max_ctx, 1);
   if (form != SMLA_TOPK_ROWS && workspace && workspace_bytes >= (size_t)rows * tp.ws_row_bytes &&
       rows * tp.chunks <= 0x7fffffffLL && tp.chunks >= 2) {
     if (form == SMLA_TOPK_CHUNKS) {
-      tp.ws = workspace;
+      tp.ws = workspace;  // one sub-chunk per chunk: every chunk a workgroup
     } else {
       int cus = 0;
       const int rc = device_cus(&cus);
       if (rc != SMLA_OK) return rc;
-      if (topk_multi_auto(rows, max_ctx, cus)) tp.ws = workspace;
+      if (topk_multi_auto(rows, max_ctx, cus)) {
+        tp.ws = workspace;
+        tp.sub = topk_sub(rows, max_ctx, cus);
+        tp.chunks = smla::topk_chunks(max_ctx, tp.sub);
+      }
     }
   }
   if (smla::launch_topk(tp, (hipStream_t)hip_stream) != hipSuccess) {

@@ -71,11 +71,12 @@ struct TopkParams {
   void* ws;             // multi-workgroup form: rows x ws_row_bytes, or null
   size_t ws_row_bytes;
   int chunks;           // chunks of a max_ctx row (multi-workgroup form)
+  int sub;              // sub-chunks of 4096 positions per chunk
 };
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 size_t topk_ws_row_bytes(int max_ctx);  // workspace of one row (multi-workgroup form)
-int topk_chunks(int max_ctx);
+int topk_chunks(int max_ctx, int sub);
 hipError_t launch_split(const SplitParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, hipStream_t st);
 int split_heads_per_block(int heads);

@@ -508,9 +508,9 @@ __device__ void topk_row(const TopkParams& p, int64_t row, int n, TopkSmem& sm) 
 // workgroup's first score loads wait on no read of the argument segment.
 #define SMLA_TOPK_ARGS                                                                       \
   const float *a_scores, const int32_t *a_ctx, int32_t *a_out, int64_t a_rows, int a_q_len, \
-      int a_max_ctx, int a_topk, void *a_ws, size_t a_ws_row_bytes, int a_chunks
+      int a_max_ctx, int a_topk, void *a_ws, size_t a_ws_row_bytes, int a_chunks, int a_sub
 #define SMLA_TOPK_PARAMS \
-  { a_scores, a_ctx, a_out, a_rows, a_q_len, a_max_ctx, a_topk, a_ws, a_ws_row_bytes, a_chunks }
+  { a_scores, a_ctx, a_out, a_rows, a_q_len, a_max_ctx, a_topk, a_ws, a_ws_row_bytes, a_chunks, a_sub }
 
 template <bool V4>
 __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SMLA_TOPK_ARGS) {
@@ -527,8 +527,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SMLA_TOPK_ARGS) {
 
 // ---------------------------------------------------------------------------
 // Multi-workgroup form for few long rows (one workgroup per row would leave
-// most CUs idle).  Four launches, each row cut into chunks of kChunk
+// most CUs idle).  Four launches, each row cut into chunks of sub x kSub
 // positions; no atomics in device memory, no waits between workgroups:
+// A chunk is `sub` sub-chunks of kSub positions, one workgroup looping over
+// them (the next sub-chunk's loads issued before the current one is
+// counted): the host takes sub > 1 when many rows would otherwise give
+// several chunk workgroups per CU, which cuts the histograms written and
+// summed.
 //   1. topk_hist_kernel (row x chunk): the chunk's first-digit histogram,
 //      all 2048 bins written to the workspace;
 //   2. topk_scan_kernel (row): the row's histogram (sum over its chunks), the
@@ -544,7 +549,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(SMLA_TOPK_ARGS) {
 //      holds takes the one-workgroup path (topk_row) instead.
 // ---------------------------------------------------------------------------
 constexpr int kChunkThreads = 256;
-constexpr int kChunk = kChunkThreads * kPer;  // 4096 positions per chunk workgroup
+constexpr int kSub = kChunkThreads * kPer;  // 4096 positions per sub-chunk
 
 enum : uint32_t { kMetaTrivial = 1u, kMetaFallback = 2u };
 
@@ -571,15 +576,25 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(SMLA_TOPK_ARGS
   const int64_t row = blockIdx.x / p.chunks;
   const int c = blockIdx.x % p.chunks;
   const int n = row_len(p, row);
-  if (n <= p.topk || c * kChunk >= n) return;  // trivial row, or past its end
+  const int base = c * p.sub * kSub;
+  if (n <= p.topk || base >= n) return;  // trivial row, or past its end
   const TopkWs w = row_ws(p, row);
   for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
+  const float* sc = p.scores + row * p.max_ctx;
+  uint32_t k[kPer], valid, kn[kPer], vn = 0;
+  load_chunk<V4>(sc, base + kPer * threadIdx.x, n, k, valid);
   __syncthreads();
-  uint32_t k[kPer], valid;
-  load_chunk<V4>(p.scores + row * p.max_ctx, c * kChunk + kPer * threadIdx.x, n, k, valid);
+  for (int g = 0; g < p.sub; ++g) {
+    const int nb = base + (g + 1) * kSub;
+    if (g + 1 < p.sub && nb < n) load_chunk<V4>(sc, nb + kPer * threadIdx.x, n, kn, vn);
 #pragma unroll
-  for (int e = 0; e < kPer; ++e)
-    if (valid >> e & 1) atomicAdd(&hist[k[e] >> 21], 1u);
+    for (int e = 0; e < kPer; ++e)
+      if (valid >> e & 1) atomicAdd(&hist[k[e] >> 21], 1u);
+    if (g + 1 >= p.sub || nb >= n) break;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) k[e] = kn[e];
+    valid = vn;
+  }
   __syncthreads();
   uint32_t* dst = w.hist + (size_t)c * kBins;
   for (int i = threadIdx.x; i < kBins; i += kChunkThreads) dst[i] = hist[i];
@@ -599,7 +614,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_scan_kernel(SMLA_TOPK_ARGS)
     if (tid == 0) w.meta[0] = kMetaTrivial;
     return;
   }
-  const int nch = (n + kChunk - 1) / kChunk;
+  const int nch = (n + p.sub * kSub - 1) / (p.sub * kSub);
   // (loads are issued 16 at a time: a loop of dependent sums would cost one
   // memory round trip per chunk)
   for (int i = tid; i < kBins; i += kTopkThreads) {
@@ -658,22 +673,34 @@ __global__ __launch_bounds__(kChunkThreads) void topk_cand_kernel(SMLA_TOPK_ARGS
   const int64_t row = blockIdx.x / p.chunks;
   const int c = blockIdx.x % p.chunks;
   const int n = row_len(p, row);
-  if (n <= p.topk || c * kChunk >= n) return;
+  const int base = c * p.sub * kSub;
+  if (n <= p.topk || base >= n) return;
   const TopkWs w = row_ws(p, row);
-  const int p0 = c * kChunk + kPer * threadIdx.x;
-  uint32_t k[kPer], valid;
-  load_chunk<V4>(p.scores + row * p.max_ctx, p0, n, k, valid);  // in flight with the reads below
-  const uint32_t flags = w.meta[0], b1 = w.meta[1], off = w.off[c];
+  const float* sc = p.scores + row * p.max_ctx;
+  uint32_t k[kPer], valid, kn[kPer], vn = 0;
+  load_chunk<V4>(sc, base + kPer * threadIdx.x, n, k, valid);  // in flight with the reads below
+  const uint32_t flags = w.meta[0], b1 = w.meta[1];
+  uint32_t off = w.off[c];
   if (flags != 0u) return;  // trivial or fallback row
-  uint32_t m = 0;
+  for (int g = 0; g < p.sub; ++g) {
+    const int p0 = base + g * kSub + kPer * threadIdx.x;
+    const int nb = base + (g + 1) * kSub;
+    if (g + 1 < p.sub && nb < n) load_chunk<V4>(sc, nb + kPer * threadIdx.x, n, kn, vn);
+    uint32_t m = 0;
 #pragma unroll
-  for (int e = 0; e < kPer; ++e) m |= (uint32_t)((valid >> e & 1) && (k[e] >> 21) >= b1) << e;
-  uint32_t tot;
-  uint32_t o = off + scan_excl<kChunkThreads>((uint32_t)__builtin_popcount(m), sw, &tot);
-  if (m) {
+    for (int e = 0; e < kPer; ++e) m |= (uint32_t)((valid >> e & 1) && (k[e] >> 21) >= b1) << e;
+    uint32_t tot;
+    uint32_t o = off + scan_excl<kChunkThreads>((uint32_t)__builtin_popcount(m), sw, &tot);
+    if (m) {
 #pragma unroll
-    for (int e = 0; e < kPer; ++e)
-      if (m >> e & 1) w.cand[o++] = make_uint2(k[e], (uint32_t)(p0 + e));
+      for (int e = 0; e < kPer; ++e)
+        if (m >> e & 1) w.cand[o++] = make_uint2(k[e], (uint32_t)(p0 + e));
+    }
+    off += tot;
+    if (g + 1 >= p.sub || nb >= n) break;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) k[e] = kn[e];
+    valid = vn;
   }
 }
 
@@ -717,16 +744,18 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(SMLA_TOPK_ARG
 
 }  // namespace
 
+// sized for one sub-chunk per chunk, the most chunks any call uses
 size_t topk_ws_row_bytes(int max_ctx) {
-  const size_t chunks = ((size_t)max_ctx + kChunk - 1) / kChunk;
+  const size_t chunks = ((size_t)max_ctx + kSub - 1) / kSub;
   const size_t b = kCandCap * sizeof(uint2) + (chunks * kBins + chunks + 1 + 4) * sizeof(uint32_t);
   return (b + 255) / 256 * 256;
 }
 
-int topk_chunks(int max_ctx) { return (max_ctx + kChunk - 1) / kChunk; }
+int topk_chunks(int max_ctx, int sub) { return (max_ctx + sub * kSub - 1) / (sub * kSub); }
 
 #define SMLA_TOPK_PASS(p) \
-  (p).scores, (p).ctx, (p).out, (p).rows, (p).q_len, (p).max_ctx, (p).topk, (p).ws, (p).ws_row_bytes, (p).chunks
+  (p).scores, (p).ctx, (p).out, (p).rows, (p).q_len, (p).max_ctx, (p).topk, (p).ws, (p).ws_row_bytes, (p).chunks, \
+      (p).sub
 
 template <bool V4>
 static hipError_t launch_topk_t(const TopkParams& p, hipStream_t st) {

@@ -114,6 +114,29 @@ def test_topk_ragged_contexts(smla):
         _same(_run(smla, scores, 2048, ctx, multi), want, f"ragged contexts multi={multi}")
 
 
+def test_topk_auto_many_long_rows(smla):
+    """The automatic form on 96 rows of ragged contexts up to 131072
+    positions: chunked, and with this many rows each chunk workgroup takes
+    several 4096-position sub-chunks (three on a 256-CU device), including
+    chunks that end inside a sub-chunk."""
+    import torch
+    rng = np.random.default_rng(7250)
+    rows = 96
+    ctx = rng.integers(2048, 131073, size=rows).tolist()
+    ctx[0], ctx[1], ctx[2] = 131072, 1000, 4096 * 3 + 17
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert rows * (131072 // 4096) // (4 * cus) >= 2, "this shape must take more than one sub-chunk"
+    scores = index_scores(7251, rows, 1, 131072, "normal")
+    s = torch.from_numpy(scores).cuda()
+    out = torch.full((rows, 1, 2048), 12345, dtype=torch.int32, device="cuda")
+    n = smla.smla_topk_workspace_bytes(rows, 1, 131072)
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    smla.smla_topk(s, 2048, out, torch.tensor(ctx, dtype=torch.int32, device="cuda"), workspace_t=ws,
+                   form=smla.TOPK_AUTO)
+    torch.cuda.synchronize()
+    _same(out.cpu().numpy(), oracle.topk_positions(scores, ctx, 2048), "auto form, 96 long rows")
+
+
 def test_topk_feeds_paged_decode(smla):
     """scores -> smla_topk -> smla_decode_paged, against the oracle's own
     selection, page mapping and decode."""

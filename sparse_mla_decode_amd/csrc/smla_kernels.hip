@@ -100,13 +100,12 @@ __device__ __forceinline__ uint32_t rows32(int64_t kv_rows) {
   return (uint32_t)(kv_rows < 0x7fffffffLL ? kv_rows : 0x7fffffffLL);
 }
 
-// Round to bf16 (nearest even) and pack two values.
+// Round two values to bf16 (nearest even) and pack them, a in the low half
+// (one v_cvt_pk_bf16_f32).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  __bf16 x = (__bf16)a, y = (__bf16)b;
-  uint16_t ux, uy;
-  __builtin_memcpy(&ux, &x, 2);
-  __builtin_memcpy(&uy, &y, 2);
-  return (uint32_t)ux | ((uint32_t)uy << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
 }
 
 // Tile layout in LDS: the row is cut into 9 blocks of 8 granules (16 bytes
@@ -191,9 +190,10 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
 // splits' LSE, weights exp(LSE_s - max), empty splits (LSE = -inf) weight 0.
 // The partials travel between XCDs, whose L2 caches are not coherent with
 // each other for ordinary accesses: they are written and read with
-// agent-scope atomic accesses (8 bytes each), which the L2 keeps coherent,
-// so no cache-wide writeback or invalidate is needed (those serialise per
-// XCD and cost more than the merge itself).
+// agent-scope atomic accesses (8 bytes each), which the L2 keeps coherent.
+// The ticket's agent-scope release and acquire still cost an L2 writeback
+// and invalidate on this target (the compiler's implementation of those
+// orderings), part of why the single launch is slower than two.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void st_agent(float* p, floatx4 v) {
   const u32x4 u = __builtin_bit_cast(u32x4, v);
@@ -713,7 +713,7 @@ void split_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a_k
   // keeps it live until the loads are known to be complete.
   static_assert(DP == 1, "one row per lane per tile");
   auto issue = [&](uint8_t* buf, int t, int ntiles) __attribute__((always_inline)) -> uint64_t {
-    // a tile past the last (three buffers refill every step) loads the zero row
+    // a masked entry loads the zero row (every call has t < ntiles)
     const int32_t r = t < ntiles ? list_s[min(t * TR + dma_row[0], LCAP - 1)] : -1;
     const uintptr_t hit = (uintptr_t)(p.kv + (int64_t)r * kRow);
     const u32x4* src = (const u32x4*)(r >= 0 ? hit : (uintptr_t)g_zero_row) + dma_gran[0];
@@ -1391,6 +1391,9 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
 #pragma unroll
       for (int k = 0; k < D; ++k)
         op[k] = *(const bf16x8*)(T + ((k & 1) ? qk_o : qk_e) + (k >> 1) * TR * 128);
+      // validity of this lane's rows, read with the first operands (after the
+      // MFMAs its LDS round trip would wait in front of the softmax)
+      const i32x4 r4 = *(const i32x4*)(list_s + ring(t * TR) + 16 * rh + 4 * g);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int k = 0; k < kKSteps; ++k) {
@@ -1401,7 +1404,6 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
           op[k % D] = *(const bf16x8*)(T + (((k + D) & 1) ? qk_o : qk_e) + ((k + D) >> 1) * TR * 128);
         __builtin_amdgcn_sched_barrier(0);
       }
-      const i32x4 r4 = *(const i32x4*)(list_s + ring(t * TR) + 16 * rh + 4 * g);
       bool grow = false;
 #pragma unroll
       for (int gi = 0; gi < 2; ++gi) {

@@ -287,7 +287,14 @@ int smla_combine(const float *part_o, const float *part_lse, void *out, float *l
  * and a row spans at least two chunks of 4096 positions, each row is cut
  * into chunks over several workgroups (four launches: chunk histograms, a
  * row scan, candidate lists in position order, the selection), else as
- * SMLA_TOPK_ROWS.  SMLA_TOPK_AUTO: the chunked form when it was measured
+ * SMLA_TOPK_ROWS.  SMLA_TOPK_SAMPLED: as SMLA_TOPK_CHUNKS, but in two
+ * launches that read the scores once: each chunk workgroup takes a
+ * threshold from a fixed sample of its row and writes its keys at or above
+ * it, and one workgroup per row selects among them (rows where the
+ * threshold proves too high or a chunk's share of the candidate list
+ * overflows are selected by one workgroup from the whole row, so the output
+ * is exact); rows longer than 1048576 positions take the four launches.
+ * SMLA_TOPK_AUTO: the sampled form when the chunked forms were measured
  * faster (a workspace is given, there are fewer rows than twice the CUs and
  * a row spans at least 12 chunks), else one workgroup per row.  Every form
  * gives the same output.  The workspace (256-byte aligned) is scratch: any
@@ -300,7 +307,7 @@ int smla_topk(const float *scores, const int32_t *ctx_len, int batch, int q_len,
               int topk, int32_t *out_pos, void *workspace, size_t workspace_bytes, int form,
               void *hip_stream);
 
-enum smla_topk_form { SMLA_TOPK_AUTO = 0, SMLA_TOPK_ROWS = 1, SMLA_TOPK_CHUNKS = 2 };
+enum smla_topk_form { SMLA_TOPK_AUTO = 0, SMLA_TOPK_ROWS = 1, SMLA_TOPK_CHUNKS = 2, SMLA_TOPK_SAMPLED = 3 };
 
 /* Bytes of workspace for smla_topk's multi-workgroup form. */
 size_t smla_topk_workspace_bytes(int batch, int q_len, int max_ctx);

@@ -34,7 +34,7 @@ MAX_HEADS = 4096
 FUSED_SYNC_BYTES = 16384  # SMLA_FUSED_SYNC_BYTES
 NOALLOC_SCRATCH_BYTES = 64 << 20  # SMLA_NOALLOC_SCRATCH_BYTES
 DEFAULT_MERGE_POLLS = 2048
-TOPK_AUTO, TOPK_ROWS, TOPK_CHUNKS = 0, 1, 2  # smla_topk_form
+TOPK_AUTO, TOPK_ROWS, TOPK_CHUNKS, TOPK_SAMPLED = 0, 1, 2, 3  # smla_topk_form
 
 STATUS = {0: "SMLA_OK", -1: "SMLA_ERR_NULL", -2: "SMLA_ERR_DIM", -3: "SMLA_ERR_NSPLIT",
           -4: "SMLA_ERR_WORKSPACE", -5: "SMLA_ERR_ALIGN", -6: "SMLA_ERR_DEVICE",
@@ -438,7 +438,7 @@ def smla_topk(scores: torch.Tensor, topk: int, out_pos: torch.Tensor, ctx_len=No
     (all when ctx_len is None), ascending, -1 padded (ranking as in
     include/smla.h).  workspace_t: "auto" allocates the multi-workgroup
     form's workspace, None runs one workgroup per row, or a uint8 tensor.
-    form: TOPK_AUTO, TOPK_ROWS or TOPK_CHUNKS (the work split)."""
+    form: TOPK_AUTO, TOPK_ROWS, TOPK_CHUNKS or TOPK_SAMPLED (the work split)."""
     _check_one("scores", scores, torch.float32)
     if scores is None or scores.dim() != 3:
         raise ValueError("scores must be a float32 [batch, q_len, max_ctx] tensor")

@@ -378,6 +378,10 @@ bool topk_multi_auto(int64_t rows, int max_ctx, int cus) {
 #define SMLA_TOPK_WG_PER_CU 4
 #endif
 constexpr int kTopkChunkWgPerCu = SMLA_TOPK_WG_PER_CU;
+#ifndef SMLA_TOPK_AUTO_SAMPLED
+#define SMLA_TOPK_AUTO_SAMPLED 1
+#endif
+constexpr bool kTopkAutoSampled = SMLA_TOPK_AUTO_SAMPLED != 0;
 int topk_sub(int64_t rows, int max_ctx, int cus) {
   const int64_t subs = rows * smla::topk_chunks(max_ctx, 1);
   const int64_t s = subs / ((int64_t)kTopkChunkWgPerCu * cus);
@@ -394,7 +398,8 @@ SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, i
                        size_t workspace_bytes, int form, void* hip_stream) {
   if (batch < 0 || q_len < 0 || max_ctx < 0 || topk < 0 || topk > SMLA_MAX_TOPK)
     return SMLA_ERR_DIM;
-  if (form != SMLA_TOPK_AUTO && form != SMLA_TOPK_ROWS && form != SMLA_TOPK_CHUNKS)
+  if (form != SMLA_TOPK_AUTO && form != SMLA_TOPK_ROWS && form != SMLA_TOPK_CHUNKS &&
+      form != SMLA_TOPK_SAMPLED)
     return SMLA_ERR_DIM;
   const int64_t rows = (int64_t)batch * q_len;
   if (rows == 0 || topk == 0) return SMLA_OK;
@@ -414,10 +419,29 @@ SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, i
   tp.ws_row_bytes = smla::topk_ws_row_bytes(max_ctx);
   tp.sub = 1;
   tp.chunks = smla::topk_chunks(max_ctx, 1);
+  tp.sampled = 0;
+  // the sampled form takes at most maxc chunks per row and maxs sub-chunks
+  // per chunk (rows up to maxc x maxs x 4096 positions): the sub-chunks per
+  // chunk it uses for a wish of `sub`, or 0 when max_ctx is too long for it
+  const int maxc = smla::topk_sampled_max_chunks(), maxs = smla::topk_sampled_max_sub();
+  auto sampled_sub = [&](int sub) {
+    const int c1 = smla::topk_chunks(max_ctx, 1);
+    const int need = (c1 + maxc - 1) / maxc;
+    const int s2 = sub > need ? (sub < maxs ? sub : maxs) : need;
+    return s2 <= maxs && s2 >= need ? s2 : 0;
+  };
   if (form != SMLA_TOPK_ROWS && workspace && workspace_bytes >= (size_t)rows * tp.ws_row_bytes &&
       rows * tp.chunks <= 0x7fffffffLL && tp.chunks >= 2) {
     if (form == SMLA_TOPK_CHUNKS) {
       tp.ws = workspace;  // one sub-chunk per chunk: every chunk a workgroup
+    } else if (form == SMLA_TOPK_SAMPLED) {
+      tp.ws = workspace;  // rows too long for the sampled form: four launches
+      const int ss = sampled_sub(1);
+      if (ss > 0) {
+        tp.sampled = 1;
+        tp.sub = ss;
+        tp.chunks = smla::topk_chunks(max_ctx, tp.sub);
+      }
     } else {
       int cus = 0;
       const int rc = device_cus(&cus);
@@ -425,6 +449,11 @@ SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, i
       if (topk_multi_auto(rows, max_ctx, cus)) {
         tp.ws = workspace;
         tp.sub = topk_sub(rows, max_ctx, cus);
+        const int ss = kTopkAutoSampled ? sampled_sub(tp.sub) : 0;
+        if (ss > 0) {
+          tp.sampled = 1;
+          tp.sub = ss;
+        }
         tp.chunks = smla::topk_chunks(max_ctx, tp.sub);
       }
     }

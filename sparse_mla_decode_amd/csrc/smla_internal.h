@@ -72,11 +72,14 @@ struct TopkParams {
   size_t ws_row_bytes;
   int chunks;           // chunks of a max_ctx row (multi-workgroup form)
   int sub;              // sub-chunks of 4096 positions per chunk
+  int sampled;          // multi-workgroup form: 1 sampled (two launches), 0 four launches
 };
 
 hipError_t launch_topk(const TopkParams& p, hipStream_t st);
 size_t topk_ws_row_bytes(int max_ctx);  // workspace of one row (multi-workgroup form)
 int topk_chunks(int max_ctx, int sub);
+int topk_sampled_max_chunks();  // most chunks per row of the sampled form
+int topk_sampled_max_sub();     // most sub-chunks per chunk of the sampled form
 hipError_t launch_split(const SplitParams& p, hipStream_t st);
 hipError_t launch_combine(const CombineParams& p, hipStream_t st);
 int split_heads_per_block(int heads);

@@ -169,6 +169,35 @@ __device__ __forceinline__ void find_digit(const uint32_t* hist, uint32_t need, 
   __syncthreads();
 }
 
+// find_digit for a workgroup of NT threads (kBins / NT bins per thread, from
+// the top).  The caller knows that at least `need` keys were counted.
+template <int NT>
+__device__ __forceinline__ void find_digit_nt(const uint32_t* hist, uint32_t need, uint32_t* sw,
+                                              uint32_t* sel) {
+  constexpr int B = kBins / NT;
+  const int top = kBins - 1 - B * (int)threadIdx.x;
+  uint32_t c[B], sum = 0;
+#pragma unroll
+  for (int i = 0; i < B; ++i) {
+    c[i] = hist[top - i];
+    sum += c[i];
+  }
+  uint32_t tot;
+  const uint32_t ex = scan_excl<NT>(sum, sw, &tot);
+  if (ex < need && ex + sum >= need) {
+    uint32_t run = ex;
+#pragma unroll
+    for (int i = 0; i < B; ++i) {
+      if (run < need && run + c[i] >= need) {
+        sel[0] = (uint32_t)(top - i);
+        sel[1] = run;
+      }
+      run += c[i];
+    }
+  }
+  __syncthreads();
+}
+
 // LDS of a row's selection (one workgroup of kTopkThreads).
 struct TopkSmem {
   uint32_t hist[kBins];
@@ -742,6 +771,208 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(SMLA_TOPK_ARG
   select_candidates(p, row, sm, b1, need, total);
 }
 
+// ---------------------------------------------------------------------------
+// Sampled form for few long rows: two launches, and the scores are read once.
+//   1. topk_scand_kernel (row x chunk, chunks of sub <= 4 sub-chunks of kSub
+//      positions, the next one's loads issued before the current one is
+//      counted; the chunk workgroups of a row on one XCD).  Every chunk
+//      workgroup of a row takes the same sample of the row: 256
+//      blocks of 16 consecutive positions at even strides, or the whole row
+//      when it holds at most 4096 positions.  From the sample's keys (two
+//      LDS histogram passes, 11 + 11 bits) it finds tau, the key at which R
+//      sample keys lie at or above (tau rounded down to 22 bits), with R
+//      about 1.5 x topk x (sample / row) + 32, so that about 1.5 x topk of
+//      the row's keys are expected at or above tau.  It then writes its own
+//      keys >= tau with their positions, in position order, to its region
+//      of the row's candidate area (kCandCap / chunks-of-the-row entries),
+//      and their count (more than the region holds: overflow).
+//   2. topk_sel2_kernel (row): the regions concatenated in chunk order (so
+//      in position order) into LDS, the three digits of the topk-th largest
+//      key T among them, then the ordered selection (select_candidates).
+// Exactness: if at least topk keys are >= tau then T >= tau, so every key
+// >= T is a candidate.  A row with fewer than topk candidates, or a region
+// that overflowed, takes the one-workgroup path in launch 2.  No atomics in
+// device memory; the workspace needs no clearing (every region a row reads
+// is written by the same call).
+// ---------------------------------------------------------------------------
+constexpr int kSampleBlocks = 256;  // one 16-position block per chunk thread
+constexpr int kSample = kSampleBlocks * 16;
+static_assert(kSampleBlocks == kChunkThreads, "one sample block per thread");
+constexpr int kSampledMaxChunks = 64;  // regions of at least 128 entries
+constexpr int kSampledMaxSub = 4;      // sub-chunks per chunk (longer rows: four launches)
+
+// The dispatcher hands workgroup i to XCD i % 8; this renumbering gives every
+// XCD a contiguous range of logical ids, so the chunk workgroups of a row
+// share an L2 (the row's sample is fetched from HBM once).  A bijection for
+// any grid size.
+__device__ __forceinline__ int xcd_contiguous_id(int bid, int n) {
+  constexpr int kX = 8;
+  const int xcd = bid % kX, k = bid / kX;
+  const int per = n / kX, rem = n % kX;
+  return xcd < rem ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
+}
+
+struct TopkWs2 {
+  uint2* cand;    // [kCandCap] (key, position), region c at c * (kCandCap / nch)
+  uint32_t* cnt;  // [chunks] candidates found per chunk
+};
+__device__ __forceinline__ TopkWs2 row_ws2(const TopkParams& p, int64_t row) {
+  uint8_t* base = (uint8_t*)p.ws + row * p.ws_row_bytes;
+  return TopkWs2{(uint2*)base, (uint32_t*)(base + kCandCap * sizeof(uint2))};
+}
+
+template <bool V4>
+__global__ __launch_bounds__(kChunkThreads) void topk_scand_kernel(SMLA_TOPK_ARGS) {
+  const TopkParams p = SMLA_TOPK_PARAMS;
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t sw[kChunkThreads / 64 + 1];
+  __shared__ uint32_t sel[2];
+  const int tid = threadIdx.x;
+  const int bid = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  const int64_t row = bid / p.chunks;
+  const int c = bid % p.chunks;
+  const int n = row_len(p, row);
+  const int span = p.sub * kSub;  // p.sub <= kSampledMaxSub (host)
+  const int base = c * span;
+  if (n <= p.topk || base >= n) return;  // trivial row, or past its end
+  const TopkWs2 w = row_ws2(p, row);
+  const float* sc = p.scores + row * p.max_ctx;
+  uint32_t k[kPer], valid, kn[kPer], vn = 0;
+  load_chunk<V4>(sc, base + kPer * tid, n, k, valid);
+  const bool whole = n <= kSample;
+  const int s0 = whole ? 16 * tid : (int)(((int64_t)tid * n / kSampleBlocks) & ~3LL);
+  uint32_t sk[16], sv;
+  load_chunk<V4>(sc, s0, n, sk, sv);
+  for (int i = tid; i < kBins; i += kChunkThreads) hist[i] = 0;
+  const int S = whole ? n : kSample;
+  const int64_t r_est = (3LL * p.topk * S) / (2LL * n) + 32;
+  const uint32_t R = (uint32_t)(whole ? p.topk : (r_est < S ? r_est : S));
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if (sv >> e & 1) atomicAdd(&hist[sk[e] >> 21], 1u);
+  __syncthreads();
+  find_digit_nt<kChunkThreads>(hist, R, sw, sel);
+  const uint32_t d1 = sel[0], need2 = R - sel[1];
+  for (int i = tid; i < kBins; i += kChunkThreads) hist[i] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < 16; ++e)
+    if ((sv >> e & 1) && (sk[e] >> 21) == d1) atomicAdd(&hist[(sk[e] >> 10) & (kBins - 1)], 1u);
+  __syncthreads();
+  find_digit_nt<kChunkThreads>(hist, need2, sw, sel);
+  const uint32_t tau = (d1 << 21) | (sel[0] << 10);
+  const int nch = (n + span - 1) / span;
+  const uint32_t cap = (uint32_t)(kCandCap / nch);
+  uint2* const region = w.cand + (size_t)c * cap;
+  uint32_t off = 0;
+  for (int g = 0; g < p.sub; ++g) {
+    const int p0 = base + g * kSub + kPer * tid;
+    const int nb = base + (g + 1) * kSub;
+    if (g + 1 < p.sub && nb < n) load_chunk<V4>(sc, nb + kPer * tid, n, kn, vn);
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) m |= (uint32_t)((valid >> e & 1) && k[e] >= tau) << e;
+    uint32_t tot;
+    uint32_t o = off + scan_excl<kChunkThreads>((uint32_t)__builtin_popcount(m), sw, &tot);
+    if (m) {
+#pragma unroll
+      for (int e = 0; e < kPer; ++e)
+        if (m >> e & 1) {
+          if (o < cap) region[o] = make_uint2(k[e], (uint32_t)(p0 + e));
+          ++o;
+        }
+    }
+    off += tot;
+    if (g + 1 >= p.sub || nb >= n) break;
+#pragma unroll
+    for (int e = 0; e < kPer; ++e) k[e] = kn[e];
+    valid = vn;
+  }
+  if (tid == 0) w.cnt[c] = off;
+}
+
+template <bool V4>
+__global__ __launch_bounds__(kTopkThreads) void topk_sel2_kernel(SMLA_TOPK_ARGS) {
+  const TopkParams p = SMLA_TOPK_PARAMS;
+  __shared__ TopkSmem sm;
+  __shared__ uint32_t off_s[kSampledMaxChunks + 1];
+  __shared__ uint32_t bad_s;
+  const int tid = threadIdx.x;
+  const int64_t row = blockIdx.x;
+  const int n = row_len(p, row);
+  if (n <= p.topk) {
+    take_all(p, row, n);
+    return;
+  }
+  const TopkWs2 w = row_ws2(p, row);
+  const int span = p.sub * kSub;
+  const int nch = (n + span - 1) / span;  // <= kSampledMaxChunks (host)
+  if (nch > kSampledMaxChunks) {  // never taken: the host sizes the chunks
+    topk_row<V4>(p, row, n, sm);
+    return;
+  }
+  const uint32_t cap = (uint32_t)(kCandCap / nch);
+  // the chunks' counts in one round trip (thread c reads chunk c's), then
+  // their prefix in the first wave
+  if (tid < 64) {
+    const uint32_t v = tid < nch ? w.cnt[tid] : 0u;
+    const uint32_t vc = v > cap ? cap : v;
+    uint32_t inc = vc;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const uint32_t y = __shfl_up(inc, d, 64);
+      if (tid >= d) inc += y;
+    }
+    if (tid < nch) off_s[tid] = inc - vc;
+    const bool over = __any(v > cap);
+    if (tid == nch - 1) {
+      off_s[nch] = inc;
+      bad_s = (uint32_t)over | (uint32_t)(inc < (uint32_t)p.topk);
+    }
+  }
+  __syncthreads();
+  if (bad_s) {  // tau too high, or a region overflowed: the one-workgroup path
+    topk_row<V4>(p, row, n, sm);
+    return;
+  }
+  const uint32_t total = off_s[nch];  // <= kCandCap
+  // wave v copies the regions of chunks v, v + 16, ...: eight loads per lane
+  // in flight at a time
+  {
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int c = wave; c < nch; c += kTopkWaves) {
+      const uint32_t o0 = off_s[c], cn = off_s[c + 1] - o0;
+      const uint2* src = w.cand + (size_t)c * cap;
+      for (uint32_t j0 = 0; j0 < cn; j0 += 64 * 8) {
+        uint2 e[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t j = j0 + u * 64 + lane;
+          e[u] = j < cn ? src[j] : make_uint2(0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const uint32_t j = j0 + u * 64 + lane;
+          if (j < cn) {
+            sm.cand[o0 + j] = e[u].x;
+            sm.cpos[o0 + j] = (int32_t)e[u].y;
+          }
+        }
+      }
+    }
+  }
+  // first digit of T among the candidates (every key above tau's is here)
+  for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
+  __syncthreads();
+  for (uint32_t i = tid; i < total; i += kTopkThreads) atomicAdd(&sm.hist[sm.cand[i] >> 21], 1u);
+  __syncthreads();
+  find_digit(sm.hist, (uint32_t)p.topk, sm.sw, sm.sel);
+  const uint32_t b1 = sm.sel[0], need = (uint32_t)p.topk - sm.sel[1];
+  __syncthreads();
+  select_candidates(p, row, sm, b1, need, total);
+}
+
 }  // namespace
 
 // sized for one sub-chunk per chunk, the most chunks any call uses
@@ -752,6 +983,9 @@ size_t topk_ws_row_bytes(int max_ctx) {
 }
 
 int topk_chunks(int max_ctx, int sub) { return (max_ctx + sub * kSub - 1) / (sub * kSub); }
+
+int topk_sampled_max_chunks() { return kSampledMaxChunks; }
+int topk_sampled_max_sub() { return kSampledMaxSub; }
 
 #define SMLA_TOPK_PASS(p) \
   (p).scores, (p).ctx, (p).out, (p).rows, (p).q_len, (p).max_ctx, (p).topk, (p).ws, (p).ws_row_bytes, (p).chunks, \
@@ -765,6 +999,13 @@ static hipError_t launch_topk_t(const TopkParams& p, hipStream_t st) {
     return hipGetLastError();
   }
   const unsigned rc = (unsigned)(p.rows * p.chunks);
+  if (p.sampled) {
+    if (p.sub > kSampledMaxSub) return hipErrorInvalidValue;  // the host never asks for it
+    hipLaunchKernelGGL(topk_scand_kernel<V4>, dim3(rc), dim3(kChunkThreads), 0, st, SMLA_TOPK_PASS(p));
+    hipLaunchKernelGGL(topk_sel2_kernel<V4>, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st,
+                       SMLA_TOPK_PASS(p));
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(topk_hist_kernel<V4>, dim3(rc), dim3(kChunkThreads), 0, st, SMLA_TOPK_PASS(p));
   hipLaunchKernelGGL(topk_scan_kernel, dim3((unsigned)p.rows), dim3(kTopkThreads), 0, st,
                      SMLA_TOPK_PASS(p));

@@ -328,7 +328,7 @@ def test_topk_arguments(smla):
     assert f(sc, ctx, 1, 1, -5, 8, out, None, 0, 0, None) == -2
     assert f(sc, ctx, 1, 1, 100, -1, out, None, 0, 0, None) == -2
     assert f(sc, ctx, 1, 1, 100, (1 << 24) + 1, out, None, 0, 0, None) == -2
-    assert f(sc, ctx, 1, 1, 100, 8, out, None, 0, 3, None) == -2   # unknown form
+    assert f(sc, ctx, 1, 1, 100, 8, out, None, 0, 4, None) == -2   # unknown form
     assert f(sc, ctx, 1, 1, 100, 8, out, None, 0, -1, None) == -2
     assert f(sc, ctx, 1, 1, 100, 8, None, None, 0, 0, None) == -1
     assert f(None, ctx, 1, 1, 100, 8, out, None, 0, 0, None) == -1

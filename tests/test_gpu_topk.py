@@ -7,9 +7,11 @@ values (+-0, +-inf, +-NaN, subnormals), over rows that are shorter than topk,
 exactly topk, one longer, not a multiple of the workgroup width, with and
 without per-sequence context lengths, with more equal keys than the LDS
 candidate copy holds, with rows 16-byte aligned (16-byte loads) or not,
-each through both work splits (one workgroup per row, and rows cut into
-4096-position chunks over several workgroups, whose workspace starts as
-garbage); then the full sizes of the batch-1
+each through the three work splits (one workgroup per row; rows cut into
+4096-position chunks over several workgroups in four launches; and the
+sampled two-launch form, whose candidate threshold comes from a sample of
+the row, with the heavy-tie cases taking its fallback), the workspace
+starting as garbage; then the full sizes of the batch-1
 (65536) and batch-64 (32768) shapes and ragged contexts up to 131072,
 compared on every row.  Last, the path end to end: scores -> smla_topk ->
 smla_decode_paged against oracle.topk_positions -> rows_of_positions ->
@@ -36,19 +38,23 @@ def smla():
     return m
 
 
-def _run(smla, scores, topk, ctx=None, multi=True):
-    """multi: rows cut into 4096-position chunks over several workgroups
-    (forced from two chunks on, with a workspace that starts as garbage),
-    else one workgroup per row."""
+FORMS = ["chunks", "row", "sampled"]
+
+
+def _run(smla, scores, topk, ctx=None, form="chunks"):
+    """form: "chunks" (rows cut into 4096-position chunks, four launches) or
+    "sampled" (two launches), each forced from two chunks on with a
+    workspace that starts as garbage; "row": one workgroup per row."""
     import torch
     s = torch.from_numpy(scores).cuda()
     out = torch.full((scores.shape[0], scores.shape[1], topk), 12345, dtype=torch.int32, device="cuda")
     c = None if ctx is None else torch.tensor(ctx, dtype=torch.int32, device="cuda")
     ws = None
-    if multi:
+    if form != "row":
         n = smla.smla_topk_workspace_bytes(scores.shape[0], scores.shape[1], scores.shape[2])
         ws = torch.full((max(n, 256),), 0xA5, dtype=torch.uint8, device="cuda")
-    smla.smla_topk(s, topk, out, c, workspace_t=ws, form=smla.TOPK_CHUNKS if multi else smla.TOPK_ROWS)
+    f = {"chunks": smla.TOPK_CHUNKS, "row": smla.TOPK_ROWS, "sampled": smla.TOPK_SAMPLED}[form]
+    smla.smla_topk(s, topk, out, c, workspace_t=ws, form=f)
     torch.cuda.synchronize()
     return out.cpu().numpy()
 
@@ -73,22 +79,22 @@ CASES = [  # kind, batch, q_len, max_ctx, topk, ctx
 ]
 
 
-@pytest.mark.parametrize("multi", [True, False], ids=["chunks", "row"])
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c[0]}-b{c[1]}q{c[2]}m{c[3]}k{c[4]}")
-def test_topk_parity(smla, case, multi):
+def test_topk_parity(smla, case, form):
     kind, b, lq, m, k, ctx = case
     scores = index_scores(700 + m + k, b, lq, m, kind)
-    got = _run(smla, scores, k, ctx, multi)
-    _same(got, oracle.topk_positions(scores, ctx, k), f"{kind} b{b} q{lq} m{m} k{k} multi={multi}")
+    got = _run(smla, scores, k, ctx, form)
+    _same(got, oracle.topk_positions(scores, ctx, k), f"{kind} b{b} q{lq} m{m} k{k} form={form}")
 
 
-@pytest.mark.parametrize("multi", [True, False], ids=["chunks", "row"])
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("shape", [(1, 1, 65536), (64, 1, 32768)], ids=["long", "batched"])
-def test_topk_full_size(smla, shape, multi):
+def test_topk_full_size(smla, shape, form):
     b, lq, m = shape
     scores = index_scores(7100 + b, b, lq, m, "normal")
-    got = _run(smla, scores, 2048, multi=multi)
-    _same(got, oracle.topk_positions(scores, None, 2048), f"full size {shape} multi={multi}")
+    got = _run(smla, scores, 2048, form=form)
+    _same(got, oracle.topk_positions(scores, None, 2048), f"full size {shape} form={form}")
 
 
 def test_topk_two_values(smla):
@@ -98,9 +104,9 @@ def test_topk_two_values(smla):
     rng = np.random.default_rng(7150)
     scores = (rng.random((2, 1, 30000)) < 0.5).astype(np.float32)
     for k in (2048, 15000, 29999):
-        for multi in (True, False):
-            _same(_run(smla, scores, k, multi=multi), oracle.topk_positions(scores, None, k),
-                  f"two values k={k} multi={multi}")
+        for form in FORMS:
+            _same(_run(smla, scores, k, form=form), oracle.topk_positions(scores, None, k),
+                  f"two values k={k} form={form}")
 
 
 def test_topk_ragged_contexts(smla):
@@ -110,8 +116,8 @@ def test_topk_ragged_contexts(smla):
     ctx[0], ctx[1] = 131072, 1000  # the largest context, and one below topk
     scores = index_scores(7201, 8, 1, 131072, "normal")
     want = oracle.topk_positions(scores, ctx, 2048)
-    for multi in (True, False):
-        _same(_run(smla, scores, 2048, ctx, multi), want, f"ragged contexts multi={multi}")
+    for form in FORMS:
+        _same(_run(smla, scores, 2048, ctx, form), want, f"ragged contexts form={form}")
 
 
 def test_topk_auto_many_long_rows(smla):

@@ -51,28 +51,34 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (lane i
+// gets v_0 + ... + v_i): within each row of 16 lanes by shifts of 1, 2, 4
+// and 8, then the last lane of row 0 added to row 1 and of row 2 to row 3,
+// then lane 31 added to rows 2 and 3.  Lanes whose source lies outside the
+// row add 0.  (A shuffle loop goes through the LDS crossbar: six dependent
+// round trips.)
+__device__ __forceinline__ uint32_t wave_scan_incl(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return v;
+}
+
 // Exclusive prefix sum of one value per thread over a workgroup of NT
 // threads; *total receives the sum.  sw: NT / 64 + 1 words of LDS.
 template <int NT = kTopkThreads>
 __device__ __forceinline__ uint32_t scan_excl(uint32_t v, uint32_t* sw, uint32_t* total) {
   constexpr int kW = NT / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  uint32_t inc = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t y = __shfl_up(inc, d, 64);
-    if (lane >= d) inc += y;
-  }
+  const uint32_t inc = wave_scan_incl(v);
   if (lane == 63) sw[w] = inc;
   __syncthreads();
   if (w == 0) {
     const uint32_t t = lane < kW ? sw[lane] : 0u;
-    uint32_t ti = t;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = __shfl_up(ti, d, 64);
-      if (lane >= d) ti += y;
-    }
+    const uint32_t ti = wave_scan_incl(t);
     if (lane < kW) sw[lane] = ti - t;
     if (lane == kW - 1) sw[kW] = ti;
   }
@@ -427,15 +433,10 @@ __device__ void topk_row(const TopkParams& p, int64_t row, int n, TopkSmem& sm) 
       for (int j = 0; j < kPerScan; ++j) mm |= (uint32_t)((valid >> j & 1) && (k[j] >> 21) == prefix) << j;
       // one LDS reservation per wave: its lanes' counts, scanned
       const uint32_t c = (uint32_t)__builtin_popcount(mm);
-      uint32_t inc = c;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t y = __shfl_up(inc, d, 64);
-        if (lane >= d) inc += y;
-      }
+      const uint32_t inc = wave_scan_incl(c);
       uint32_t wbase = 0;
       if (lane == 63 && inc) wbase = atomicAdd(&ncand, inc);
-      uint32_t o = __shfl(wbase, 63, 64) + inc - c;
+      uint32_t o = (uint32_t)__builtin_amdgcn_readlane((int)wbase, 63) + inc - c;
       if (mm) {
 #pragma unroll
         for (int j = 0; j < kPerScan; ++j)
@@ -918,12 +919,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sel2_kernel(SMLA_TOPK_ARGS)
   if (tid < 64) {
     const uint32_t v = tid < nch ? w.cnt[tid] : 0u;
     const uint32_t vc = v > cap ? cap : v;
-    uint32_t inc = vc;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const uint32_t y = __shfl_up(inc, d, 64);
-      if (tid >= d) inc += y;
-    }
+    const uint32_t inc = wave_scan_incl(vc);
     if (tid < nch) off_s[tid] = inc - vc;
     const bool over = __any(v > cap);
     if (tid == nch - 1) {

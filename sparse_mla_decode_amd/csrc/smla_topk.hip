@@ -900,7 +900,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sel2_kernel(SMLA_TOPK_ARGS)
   __shared__ uint32_t off_s[kSampledMaxChunks + 1];
   __shared__ uint32_t bad_s;
   const int tid = threadIdx.x;
-  const int64_t row = blockIdx.x;
+  // rows numbered as the chunk launch numbers them, so a row is selected on
+  // the XCD whose L2 took its candidates
+  const int64_t row = xcd_contiguous_id(blockIdx.x, gridDim.x);
   const int n = row_len(p, row);
   if (n <= p.topk) {
     take_all(p, row, n);

@@ -120,6 +120,26 @@ def test_topk_ragged_contexts(smla):
         _same(_run(smla, scores, 2048, ctx, form), want, f"ragged contexts form={form}")
 
 
+def test_topk_sample_misleads(smla):
+    """Scores large exactly on the sampled form's sample (256 blocks of 16
+    positions at offsets floor(t n / 256) rounded down to a multiple of 4)
+    and small elsewhere: its threshold then lands among the sampled keys,
+    far fewer than topk keys reach it, and the row must take the exact
+    fallback.  Rows of 65536 and 40000 positions, topk 2048 and 5000; every
+    form must give the oracle's selection."""
+    rng = np.random.default_rng(7400)
+    lens = [65536, 40000]
+    scores = rng.standard_normal((2, 1, 65536)).astype(np.float32) * 0.01
+    for r, n in enumerate(lens):
+        for t in range(256):
+            s0 = (t * n // 256) & ~3
+            scores[r, 0, s0:s0 + 16] = 10.0 + rng.random(16).astype(np.float32)
+    for k in (2048, 5000):
+        want = oracle.topk_positions(scores, lens, k)
+        for form in FORMS:
+            _same(_run(smla, scores, k, lens, form), want, f"misleading sample k={k} form={form}")
+
+
 def test_topk_auto_many_long_rows(smla):
     """The automatic form on 96 rows of ragged contexts up to 131072
     positions: chunked, and with this many rows each chunk workgroup takes

@@ -287,7 +287,8 @@ int smla_combine(const float *part_o, const float *part_lse, void *out, float *l
  * and a row spans at least two chunks of 4096 positions, each row is cut
  * into chunks over several workgroups (four launches: chunk histograms, a
  * row scan, candidate lists in position order, the selection), else as
- * SMLA_TOPK_ROWS.  SMLA_TOPK_SAMPLED: as SMLA_TOPK_CHUNKS, but in two
+ * SMLA_TOPK_ROWS.  A chunk is one or more sub-chunks of 4096 positions,
+ * about four chunk workgroups per CU.  SMLA_TOPK_SAMPLED: as SMLA_TOPK_CHUNKS, but in two
  * launches that read the scores once: each chunk workgroup takes a
  * threshold from a fixed sample of its row and writes its keys at or above
  * it, and one workgroup per row selects among them (rows where the
@@ -299,9 +300,9 @@ int smla_combine(const float *part_o, const float *part_lse, void *out, float *l
  * a row spans at least 12 chunks), else one workgroup per row.  Every form
  * gives the same output.  The workspace (256-byte aligned) is scratch: any
  * content on entry, nothing kept after the call.
- * Errors as smla_decode (SMLA_ERR_DEVICE only when SMLA_TOPK_AUTO with a
- * workspace needs the CU count and it cannot be read; SMLA_ERR_DIM for an
- * unknown form).
+ * Errors as smla_decode (SMLA_ERR_DEVICE only when SMLA_TOPK_AUTO or
+ * SMLA_TOPK_CHUNKS with a workspace needs the CU count and it cannot be
+ * read; SMLA_ERR_DIM for an unknown form).
  */
 int smla_topk(const float *scores, const int32_t *ctx_len, int batch, int q_len, int max_ctx,
               int topk, int32_t *out_pos, void *workspace, size_t workspace_bytes, int form,

@@ -433,7 +433,12 @@ SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, i
   if (form != SMLA_TOPK_ROWS && workspace && workspace_bytes >= (size_t)rows * tp.ws_row_bytes &&
       rows * tp.chunks <= 0x7fffffffLL && tp.chunks >= 2) {
     if (form == SMLA_TOPK_CHUNKS) {
-      tp.ws = workspace;  // one sub-chunk per chunk: every chunk a workgroup
+      int cus = 0;  // sub-chunks per chunk as the automatic choice takes them
+      const int rc = device_cus(&cus);
+      if (rc != SMLA_OK) return rc;
+      tp.ws = workspace;
+      tp.sub = topk_sub(rows, max_ctx, cus);
+      tp.chunks = smla::topk_chunks(max_ctx, tp.sub);
     } else if (form == SMLA_TOPK_SAMPLED) {
       tp.ws = workspace;  // rows too long for the sampled form: four launches
       const int ss = sampled_sub(1);

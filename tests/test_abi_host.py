@@ -312,10 +312,12 @@ def test_planner_path_without_device(smla):
     assert smla.lib.smla_fused_in_launch(1, 1, 8, 4) == -6
     # a valid fused call with NSPLIT > 1 asks the device whether to merge in-launch
     assert _call(smla, "smla_decode_fused", nsplit=4, ws=0x60000, ws_bytes=1 << 24) == -6
-    # an explicit top-k form needs no device; AUTO with a workspace asks for the CU count
+    # AUTO and CHUNKS with a workspace ask for the CU count (the sub-chunks per
+    # chunk depend on it)
     f = smla.lib.smla_topk
     vp = ctypes.c_void_p
     assert f(vp(0x10000), None, 1, 1, 65536, 8, vp(0x30000), vp(0x40000), 1 << 30, 0, None) == -6
+    assert f(vp(0x10000), None, 1, 1, 65536, 8, vp(0x30000), vp(0x40000), 1 << 30, 2, None) == -6
 
 
 def test_topk_arguments(smla):

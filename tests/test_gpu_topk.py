@@ -141,10 +141,11 @@ def test_topk_sample_misleads(smla):
 
 
 def test_topk_auto_many_long_rows(smla):
-    """The automatic form on 96 rows of ragged contexts up to 131072
-    positions: chunked, and with this many rows each chunk workgroup takes
-    several 4096-position sub-chunks (three on a 256-CU device), including
-    chunks that end inside a sub-chunk."""
+    """96 rows of ragged contexts up to 131072 positions through the
+    automatic form (the sampled one here) and the forced four-launch form:
+    with this many rows each chunk workgroup takes several 4096-position
+    sub-chunks (three on a 256-CU device), including chunks that end inside
+    a sub-chunk."""
     import torch
     rng = np.random.default_rng(7250)
     rows = 96
@@ -156,11 +157,14 @@ def test_topk_auto_many_long_rows(smla):
     s = torch.from_numpy(scores).cuda()
     out = torch.full((rows, 1, 2048), 12345, dtype=torch.int32, device="cuda")
     n = smla.smla_topk_workspace_bytes(rows, 1, 131072)
-    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
-    smla.smla_topk(s, 2048, out, torch.tensor(ctx, dtype=torch.int32, device="cuda"), workspace_t=ws,
-                   form=smla.TOPK_AUTO)
-    torch.cuda.synchronize()
-    _same(out.cpu().numpy(), oracle.topk_positions(scores, ctx, 2048), "auto form, 96 long rows")
+    want = oracle.topk_positions(scores, ctx, 2048)
+    for form in (smla.TOPK_AUTO, smla.TOPK_CHUNKS):
+        ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+        out.fill_(12345)
+        smla.smla_topk(s, 2048, out, torch.tensor(ctx, dtype=torch.int32, device="cuda"), workspace_t=ws,
+                       form=form)
+        torch.cuda.synchronize()
+        _same(out.cpu().numpy(), want, f"96 long rows, form {form}")
 
 
 def test_topk_feeds_paged_decode(smla):

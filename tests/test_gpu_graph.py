@@ -9,7 +9,8 @@ call.  Covered: smla_decode at NSPLIT 1 and 4 (split and combine kernels),
 and over 64-head slices long enough for the role-specialised kernel (its
 list ring refilled during the call),
 smla_decode_paged, smla_decode_dense (folded), smla_decode_fused (single
-launch, with its synchronisation words) and smla_topk.
+launch, with its synchronisation words) and smla_topk in each of its forms
+(one workgroup per row; chunks in four launches; sampled, two launches).
 """
 from __future__ import annotations
 
@@ -162,4 +163,27 @@ def test_graph_topk(smla):
 
     def disturb():
         smla.smla_topk(other, 2048, pos2, ctx)
+    _replays(fn, [pos], disturb)
+
+
+@pytest.mark.parametrize("form", ["auto", "chunks", "sampled"])
+def test_graph_topk_multi(smla, form):
+    """The multi-workgroup top-k forms captured: 4 rows of up to 65536
+    positions (AUTO takes the sampled form), with one workspace that the
+    disturbing calls between replays overwrite (the forms need no clearing)."""
+    import torch
+    scores = torch.from_numpy(index_scores(9710, 2, 2, 65536)).cuda()
+    other = torch.from_numpy(index_scores(9711, 2, 2, 65536)).cuda()
+    ctx = torch.tensor([65536, 30001], dtype=torch.int32, device="cuda")
+    pos = torch.empty((2, 2, 2048), dtype=torch.int32, device="cuda")
+    pos2 = torch.empty_like(pos)
+    n = smla.smla_topk_workspace_bytes(2, 2, 65536)
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    f = {"auto": smla.TOPK_AUTO, "chunks": smla.TOPK_CHUNKS, "sampled": smla.TOPK_SAMPLED}[form]
+
+    def fn():
+        smla.smla_topk(scores, 2048, pos, ctx, workspace_t=ws, form=f)
+
+    def disturb():
+        smla.smla_topk(other, 2048, pos2, ctx, workspace_t=ws, form=f)
     _replays(fn, [pos], disturb)

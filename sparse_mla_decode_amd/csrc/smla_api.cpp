@@ -364,24 +364,18 @@ SMLA_API int smla_combine(const float* part_o, const float* part_lse, void* out,
   return SMLA_OK;
 }
 
-// the multi-workgroup top-k form pays for its four launches when the rows
-// alone leave CUs idle and rows are long (measured: 1 x 65536 and 128 rows
-// up to 131072 gain, 64 x 32768 loses)
+// the multi-workgroup top-k forms pay for their extra launch(es) when the
+// rows alone leave CUs idle and rows are long (measured: 1 x 65536 and 128
+// rows up to 131072 gain, 64 x 32768 loses)
 constexpr int kTopkMultiMinChunks = 12;  // 45057 positions and more
 bool topk_multi_auto(int64_t rows, int max_ctx, int cus) {
   return rows < 2 * (int64_t)cus && smla::topk_chunks(max_ctx, 1) >= kTopkMultiMinChunks;
 }
 // sub-chunks per chunk workgroup: as many as keep about kTopkChunkWgPerCu
 // chunk workgroups per CU (one when a few rows need every chunk to fill the
-// device)
-#ifndef SMLA_TOPK_WG_PER_CU
-#define SMLA_TOPK_WG_PER_CU 4
-#endif
-constexpr int kTopkChunkWgPerCu = SMLA_TOPK_WG_PER_CU;
-#ifndef SMLA_TOPK_AUTO_SAMPLED
-#define SMLA_TOPK_AUTO_SAMPLED 1
-#endif
-constexpr bool kTopkAutoSampled = SMLA_TOPK_AUTO_SAMPLED != 0;
+// device; measured on 128 rows up to 131072 with four launches: 4 per CU
+// 44.7 us, 2 per CU 50.0, 8 per CU 46.8)
+constexpr int kTopkChunkWgPerCu = 4;
 int topk_sub(int64_t rows, int max_ctx, int cus) {
   const int64_t subs = rows * smla::topk_chunks(max_ctx, 1);
   const int64_t s = subs / ((int64_t)kTopkChunkWgPerCu * cus);
@@ -454,7 +448,7 @@ SMLA_API int smla_topk(const float* scores, const int32_t* ctx_len, int batch, i
       if (topk_multi_auto(rows, max_ctx, cus)) {
         tp.ws = workspace;
         tp.sub = topk_sub(rows, max_ctx, cus);
-        const int ss = kTopkAutoSampled ? sampled_sub(tp.sub) : 0;
+        const int ss = sampled_sub(tp.sub);  // 0: rows too long for the sampled form
         if (ss > 0) {
           tp.sampled = 1;
           tp.sub = ss;

@@ -120,6 +120,29 @@ def test_topk_ragged_contexts(smla):
         _same(_run(smla, scores, 2048, ctx, form), want, f"ragged contexts form={form}")
 
 
+def _random_case(seed):
+    """A seeded random shape: rows, length, ragged contexts (some below
+    topk), topk and score kind."""
+    rng = np.random.default_rng(seed)
+    b, lq = int(rng.integers(1, 9)), int(rng.integers(1, 4))
+    m = int(rng.integers(4097, 140000))
+    k = int(rng.choice([1, 64, 2048, int(rng.integers(2, 6000))]))
+    ctx = rng.integers(0, m + 1, size=b).tolist()
+    ctx[0] = m
+    kind = str(rng.choice(["normal", "normal", "ties", "special"]))
+    return b, lq, m, k, ctx, kind
+
+
+@pytest.mark.parametrize("seed", range(7500, 7508))
+def test_topk_random_shapes(smla, seed):
+    """Eight seeded random shapes, every form against the oracle."""
+    b, lq, m, k, ctx, kind = _random_case(seed)
+    scores = index_scores(seed, b, lq, m, kind)
+    want = oracle.topk_positions(scores, ctx, k)
+    for form in FORMS:
+        _same(_run(smla, scores, k, ctx, form), want, f"seed {seed}: b{b} q{lq} m{m} k{k} {kind} form={form}")
+
+
 def test_topk_sample_misleads(smla):
     """Scores large exactly on the sampled form's sample (256 blocks of 16
     positions at offsets floor(t n / 256) rounded down to a multiple of 4)

@@ -801,6 +801,9 @@ constexpr int kSample = kSampleBlocks * 16;
 static_assert(kSampleBlocks == kChunkThreads, "one sample block per thread");
 constexpr int kSampledMaxChunks = 64;  // regions of at least 128 entries
 constexpr int kSampledMaxSub = 4;      // sub-chunks per chunk (longer rows: four launches)
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+constexpr int kStageLoads = kCandCap * 8 / 16 / kTopkThreads;  // 16-byte loads per thread
+static_assert(kStageLoads * kTopkThreads * 16 == kCandCap * 8, "staging covers the area");
 
 // The dispatcher hands workgroup i to XCD i % 8; this renumbering gives every
 // XCD a contiguous range of logical ids, so the chunk workgroups of a row
@@ -897,6 +900,7 @@ template <bool V4>
 __global__ __launch_bounds__(kTopkThreads) void topk_sel2_kernel(SMLA_TOPK_ARGS) {
   const TopkParams p = SMLA_TOPK_PARAMS;
   __shared__ TopkSmem sm;
+  __shared__ __attribute__((aligned(16))) uint2 stage[kCandCap];  // the row's candidate area
   __shared__ uint32_t off_s[kSampledMaxChunks + 1];
   __shared__ uint32_t bad_s;
   const int tid = threadIdx.x;
@@ -916,9 +920,22 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sel2_kernel(SMLA_TOPK_ARGS)
     return;
   }
   const uint32_t cap = (uint32_t)(kCandCap / nch);
-  // the chunks' counts in one round trip (thread c reads chunk c's), then
-  // their prefix in the first wave
-  if (tid < 64) {
+  // the row's whole candidate area (64 KB, whatever the counts) into LDS by
+  // LDS-DMA, in flight together with the chunks' counts: one round trip
+  // (reads past a region's count stay in the area and are dropped)
+  {
+    const u32x4v* src = (const u32x4v*)w.cand + tid;
+    const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);  // the LDS base is wave-uniform
+    uint8_t* const st = (uint8_t*)stage + wave_u * 64 * 16;
+#pragma unroll
+    for (int u = 0; u < kStageLoads; ++u) {
+      auto* dst = (__attribute__((address_space(3))) uint8_t*)(st + u * kTopkThreads * 16);
+      asm volatile("" : "+s"(dst));
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + u * kTopkThreads),
+                                       (__attribute__((address_space(3))) void*)dst, 16, 0, 0);
+    }
+  }
+  if (tid < 64) {  // the counts and their prefix in the first wave
     const uint32_t v = tid < nch ? w.cnt[tid] : 0u;
     const uint32_t vc = v > cap ? cap : v;
     const uint32_t inc = wave_scan_incl(vc);
@@ -929,37 +946,27 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sel2_kernel(SMLA_TOPK_ARGS)
       bad_s = (uint32_t)over | (uint32_t)(inc < (uint32_t)p.topk);
     }
   }
+  __builtin_amdgcn_s_waitcnt(0xF70);  // vmcnt(0): this wave's copies have landed
   __syncthreads();
   if (bad_s) {  // tau too high, or a region overflowed: the one-workgroup path
     topk_row<V4>(p, row, n, sm);
     return;
   }
   const uint32_t total = off_s[nch];  // <= kCandCap
-  // wave v copies the regions of chunks v, v + 16, ...: eight loads per lane
-  // in flight at a time
+  // the regions, in chunk order, from the staged area (wave v: chunks v, v + 16, ...)
   {
     const int lane = tid & 63, wave = tid >> 6;
     for (int c = wave; c < nch; c += kTopkWaves) {
       const uint32_t o0 = off_s[c], cn = off_s[c + 1] - o0;
-      const uint2* src = w.cand + (size_t)c * cap;
-      for (uint32_t j0 = 0; j0 < cn; j0 += 64 * 8) {
-        uint2 e[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t j = j0 + u * 64 + lane;
-          e[u] = j < cn ? src[j] : make_uint2(0u, 0u);
-        }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const uint32_t j = j0 + u * 64 + lane;
-          if (j < cn) {
-            sm.cand[o0 + j] = e[u].x;
-            sm.cpos[o0 + j] = (int32_t)e[u].y;
-          }
-        }
+      const uint2* rs = stage + (size_t)c * cap;
+      for (uint32_t j = lane; j < cn; j += 64) {
+        const uint2 e = rs[j];
+        sm.cand[o0 + j] = e.x;
+        sm.cpos[o0 + j] = (int32_t)e.y;
       }
     }
   }
+  __syncthreads();
   // first digit of T among the candidates (every key above tau's is here)
   for (int i = tid; i < kBins; i += kTopkThreads) sm.hist[i] = 0;
   __syncthreads();

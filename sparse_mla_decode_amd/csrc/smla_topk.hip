@@ -100,58 +100,60 @@ __device__ __forceinline__ int tile_pos(int base, int e) {
             : base + e * kTopkThreads + (int)threadIdx.x;
 }
 
-// Keys of one tile; positions at or past n read as key 0 with their valid
-// bit clear.  All loads are issued before any is used.
-template <int P, bool V4>
-__device__ __forceinline__ void load_tile(const float* sc, int base, int n, uint32_t (&k)[P],
-                                          uint32_t& valid) {
-  static_assert(P <= 32 && P % 4 == 0, "tile shape");
-  float v[P];
-  valid = 0;
+// Raw scores of P elements, element e at position pos(e): the loads only,
+// so a caller keeps them in flight while it works on earlier data and takes
+// the keys (raw_keys) where it uses them.  Every element is loaded, without
+// branches: a position at or past the row's end reads a clamped address in
+// the row (mc = the row length of the score array) and has its valid bit
+// clear, so the wait counts the compiler derives for these loads are exact.
+// With V4, elements 4g .. 4g+3 are 4 consecutive positions from a multiple
+// of 4 (one 16-byte load; mc is then a multiple of 4).
+template <int P, bool V4, class Pos>
+__device__ __forceinline__ void load_raw(const float* sc, int n, int mc, Pos pos, float (&v)[P],
+                                         uint32_t& valid) {
+  static_assert(P <= 32 && P % 4 == 0, "element count");
   if constexpr (V4) {
 #pragma unroll
     for (int g = 0; g < P / 4; ++g) {
-      const int p0 = tile_pos<true>(base, 4 * g);
-      if (p0 + 3 < n) {
-        const float4 x = *(const float4*)(sc + p0);
-        v[4 * g] = x.x;
-        v[4 * g + 1] = x.y;
-        v[4 * g + 2] = x.z;
-        v[4 * g + 3] = x.w;
-      } else {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v[4 * g + c] = p0 + c < n ? sc[p0 + c] : 0.f;
-      }
+      const float4 x = *(const float4*)(sc + min(pos(4 * g), mc - 4));
+      v[4 * g] = x.x;
+      v[4 * g + 1] = x.y;
+      v[4 * g + 2] = x.z;
+      v[4 * g + 3] = x.w;
     }
   } else {
 #pragma unroll
-    for (int e = 0; e < P; ++e) {
-      const int pos = tile_pos<false>(base, e);
-      v[e] = pos < n ? sc[pos] : 0.f;
-    }
+    for (int e = 0; e < P; ++e) v[e] = sc[min(pos(e), mc - 1)];
   }
+  valid = 0;
 #pragma unroll
-  for (int e = 0; e < P; ++e) {
-    valid |= (uint32_t)(tile_pos<V4>(base, e) < n) << e;
-    k[e] = score_key(v[e]);
-  }
+  for (int e = 0; e < P; ++e) valid |= (uint32_t)(pos(e) < n) << e;
+}
+template <int P>
+__device__ __forceinline__ void raw_keys(const float (&v)[P], uint32_t (&k)[P]) {
+#pragma unroll
+  for (int e = 0; e < P; ++e) k[e] = score_key(v[e]);
 }
 
 // f(base, keys, valid) over the tiles of a row, in order, with the next
-// tile's loads issued before f works on the current one (the loads of one
-// tile are a memory round trip; this overlaps it with the previous tile's
-// work).  f returns false to stop early.
+// tile's loads in flight while f works on the current one (the loads of one
+// tile are a memory round trip).  f returns false to stop early.
 template <int P, bool V4, class F>
-__device__ __forceinline__ void for_tiles(const float* sc, int n, F&& f) {
-  uint32_t k[P], kn[P], valid, vn = 0;
-  load_tile<P, V4>(sc, 0, n, k, valid);
+__device__ __forceinline__ void for_tiles(const float* sc, int n, int mc, F&& f) {
+  float v[P], vn[P];
+  uint32_t valid, vv;
+  load_raw<P, V4>(sc, n, mc, [](int e) { return tile_pos<V4>(0, e); }, v, valid);
   for (int base = 0; base < n; base += P * kTopkThreads) {
-    const int nb = base + P * kTopkThreads;
-    if (nb < n) load_tile<P, V4>(sc, nb, n, kn, vn);
+    // the next tile, or this one again at the end (cached; never used): a
+    // load issued on every path keeps the wait counts exact
+    const int nb = base + P * kTopkThreads < n ? base + P * kTopkThreads : base;
+    load_raw<P, V4>(sc, n, mc, [nb](int e) { return tile_pos<V4>(nb, e); }, vn, vv);
+    uint32_t k[P];
+    raw_keys(v, k);
     if (!f(base, k, valid)) break;
 #pragma unroll
-    for (int e = 0; e < P; ++e) k[e] = kn[e];
-    valid = vn;
+    for (int e = 0; e < P; ++e) v[e] = vn[e];
+    valid = vv;
   }
 }
 
@@ -226,31 +228,11 @@ __device__ __forceinline__ void take_all(const TopkParams& p, int64_t row, int n
   for (int i = threadIdx.x; i < p.topk; i += blockDim.x) out[i] = i < n ? i : -1;
 }
 
-// kPer consecutive keys from position p0 (16-byte loads with V4 when all are
-// in the row); valid bit e: p0 + e < n
+// kPer consecutive raw scores from position p0 (load_raw)
 template <bool V4>
-__device__ __forceinline__ void load_chunk(const float* sc, int p0, int n, uint32_t (&k)[kPer],
+__device__ __forceinline__ void load_chunk(const float* sc, int p0, int n, int mc, float (&v)[kPer],
                                            uint32_t& valid) {
-  float v[kPer];
-  if (V4 && p0 + kPer <= n) {
-#pragma unroll
-    for (int g = 0; g < kPer / 4; ++g) {
-      const float4 x = *(const float4*)(sc + p0 + 4 * g);
-      v[4 * g] = x.x;
-      v[4 * g + 1] = x.y;
-      v[4 * g + 2] = x.z;
-      v[4 * g + 3] = x.w;
-    }
-  } else {
-#pragma unroll
-    for (int e = 0; e < kPer; ++e) v[e] = p0 + e < n ? sc[p0 + e] : 0.f;
-  }
-  valid = 0;
-#pragma unroll
-  for (int e = 0; e < kPer; ++e) {
-    k[e] = score_key(v[e]);
-    valid |= (uint32_t)(p0 + e < n) << e;
-  }
+  load_raw<kPer, V4>(sc, n, mc, [p0](int e) { return p0 + e; }, v, valid);
 }
 
 // A row's keys with first digit >= b1, with their positions, into LDS
@@ -259,15 +241,19 @@ __device__ __forceinline__ void load_chunk(const float* sc, int p0, int n, uint3
 // gives its slots; the next tile's loads are issued before the current one is
 // counted.  The caller knows the count fits kCandCap.
 template <bool V4>
-__device__ __forceinline__ void ordered_candidates(const float* sc, int n, uint32_t b1,
+__device__ __forceinline__ void ordered_candidates(const float* sc, int n, int mc, uint32_t b1,
                                                    TopkSmem& sm) {
   const int tid = threadIdx.x;
   uint32_t run = 0;  // candidates stored so far
-  uint32_t k[kPer], kn[kPer], valid, vn = 0;
-  load_chunk<V4>(sc, kPer * tid, n, k, valid);
+  float v[kPer], vn[kPer];
+  uint32_t valid, vv;
+  load_chunk<V4>(sc, kPer * tid, n, mc, v, valid);
   for (int base = 0; base < n; base += kPer * kTopkThreads) {
-    const int nb = base + kPer * kTopkThreads;
-    if (nb < n) load_chunk<V4>(sc, nb + kPer * tid, n, kn, vn);
+    // the next span, or this one again at the end (cached; never used)
+    const int nb = base + kPer * kTopkThreads < n ? base + kPer * kTopkThreads : base;
+    load_chunk<V4>(sc, nb + kPer * tid, n, mc, vn, vv);
+    uint32_t k[kPer];
+    raw_keys(v, k);
     uint32_t m = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) m |= (uint32_t)((valid >> e & 1) && (k[e] >> 21) >= b1) << e;
@@ -285,8 +271,8 @@ __device__ __forceinline__ void ordered_candidates(const float* sc, int n, uint3
     }
     run += tot;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) k[e] = kn[e];
-    valid = vn;
+    for (int e = 0; e < kPer; ++e) v[e] = vn[e];
+    valid = vv;
   }
 }
 
@@ -384,14 +370,14 @@ __device__ void topk_row(const TopkParams& p, int64_t row, int n, TopkSmem& sm) 
     const int c = tid & 3;
     uint32_t* const dst = sub + c * kBins;
     const uint32_t sw16 = 16u * (uint32_t)c;
-    for_tiles<kPerScan, V4>(sc, n, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
+    for_tiles<kPerScan, V4>(sc, n, p.max_ctx, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
 #pragma unroll
       for (int j = 0; j < kPerScan; ++j)
         if (valid >> j & 1) atomicAdd(&dst[(k[j] >> 21) ^ sw16], 1u);
       return true;
     });
   } else {
-    for_tiles<kPerScan, V4>(sc, n, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
+    for_tiles<kPerScan, V4>(sc, n, p.max_ctx, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
 #pragma unroll
       for (int j = 0; j < kPerScan; ++j)
         if (valid >> j & 1) atomicAdd(&hist[k[j] >> 21], 1u);
@@ -418,7 +404,7 @@ __device__ void topk_row(const TopkParams& p, int64_t row, int n, TopkSmem& sm) 
     // rows of more than one tile: on a one-tile row the extra block scan of
     // this pass costs more than the pass over the row it saves, 12.3 against
     // 11.7 us on 1024 positions; 64 rows of 32768: 22.8 against 25.4 us)
-    ordered_candidates<V4>(sc, n, prefix, sm);
+    ordered_candidates<V4>(sc, n, p.max_ctx, prefix, sm);
     __syncthreads();
     select_candidates(p, row, sm, prefix, need, total);
     return;
@@ -427,7 +413,7 @@ __device__ void topk_row(const TopkParams& p, int64_t row, int n, TopkSmem& sm) 
   // ---- keys of that bin into LDS (order irrelevant: only counted below)
   const int lane = tid & 63;
   if (cached) {
-    for_tiles<kPerScan, V4>(sc, n, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
+    for_tiles<kPerScan, V4>(sc, n, p.max_ctx, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
       uint32_t mm = 0;  // bit j: element j is in the bin
 #pragma unroll
       for (int j = 0; j < kPerScan; ++j) mm |= (uint32_t)((valid >> j & 1) && (k[j] >> 21) == prefix) << j;
@@ -463,7 +449,7 @@ __device__ void topk_row(const TopkParams& p, int64_t row, int n, TopkSmem& sm) 
         if ((k >> hsh) == prefix) atomicAdd(&hist[(k >> sh) & mask], 1u);
       }
     } else {
-      for_tiles<kPerScan, V4>(sc, n, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
+      for_tiles<kPerScan, V4>(sc, n, p.max_ctx, [&](int, const uint32_t(&k)[kPerScan], uint32_t valid) {
 #pragma unroll
         for (int j = 0; j < kPerScan; ++j)
           if ((valid >> j & 1) && (k[j] >> hsh) == prefix) atomicAdd(&hist[(k[j] >> sh) & mask], 1u);
@@ -611,19 +597,24 @@ __global__ __launch_bounds__(kChunkThreads) void topk_hist_kernel(SMLA_TOPK_ARGS
   const TopkWs w = row_ws(p, row);
   for (int i = threadIdx.x; i < kBins; i += kChunkThreads) hist[i] = 0;
   const float* sc = p.scores + row * p.max_ctx;
-  uint32_t k[kPer], valid, kn[kPer], vn = 0;
-  load_chunk<V4>(sc, base + kPer * threadIdx.x, n, k, valid);
+  float v[kPer], vn[kPer];
+  uint32_t valid, vv;
+  load_chunk<V4>(sc, base + kPer * threadIdx.x, n, p.max_ctx, v, valid);
   __syncthreads();
   for (int g = 0; g < p.sub; ++g) {
-    const int nb = base + (g + 1) * kSub;
-    if (g + 1 < p.sub && nb < n) load_chunk<V4>(sc, nb + kPer * threadIdx.x, n, kn, vn);
+    const bool more = g + 1 < p.sub && base + (g + 1) * kSub < n;
+    // the next sub-chunk, or this one again (cached; never used)
+    const int nb = base + (more ? g + 1 : g) * kSub;
+    load_chunk<V4>(sc, nb + kPer * threadIdx.x, n, p.max_ctx, vn, vv);
+    uint32_t k[kPer];
+    raw_keys(v, k);
 #pragma unroll
     for (int e = 0; e < kPer; ++e)
       if (valid >> e & 1) atomicAdd(&hist[k[e] >> 21], 1u);
-    if (g + 1 >= p.sub || nb >= n) break;
+    if (!more) break;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) k[e] = kn[e];
-    valid = vn;
+    for (int e = 0; e < kPer; ++e) v[e] = vn[e];
+    valid = vv;
   }
   __syncthreads();
   uint32_t* dst = w.hist + (size_t)c * kBins;
@@ -707,15 +698,20 @@ __global__ __launch_bounds__(kChunkThreads) void topk_cand_kernel(SMLA_TOPK_ARGS
   if (n <= p.topk || base >= n) return;
   const TopkWs w = row_ws(p, row);
   const float* sc = p.scores + row * p.max_ctx;
-  uint32_t k[kPer], valid, kn[kPer], vn = 0;
-  load_chunk<V4>(sc, base + kPer * threadIdx.x, n, k, valid);  // in flight with the reads below
+  float v[kPer], vn[kPer];
+  uint32_t valid, vv;
+  load_chunk<V4>(sc, base + kPer * threadIdx.x, n, p.max_ctx, v, valid);  // in flight with the reads below
   const uint32_t flags = w.meta[0], b1 = w.meta[1];
   uint32_t off = w.off[c];
   if (flags != 0u) return;  // trivial or fallback row
   for (int g = 0; g < p.sub; ++g) {
     const int p0 = base + g * kSub + kPer * threadIdx.x;
-    const int nb = base + (g + 1) * kSub;
-    if (g + 1 < p.sub && nb < n) load_chunk<V4>(sc, nb + kPer * threadIdx.x, n, kn, vn);
+    const bool more = g + 1 < p.sub && base + (g + 1) * kSub < n;
+    // the next sub-chunk, or this one again (cached; never used)
+    const int nb = base + (more ? g + 1 : g) * kSub;
+    load_chunk<V4>(sc, nb + kPer * threadIdx.x, n, p.max_ctx, vn, vv);
+    uint32_t k[kPer];
+    raw_keys(v, k);
     uint32_t m = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) m |= (uint32_t)((valid >> e & 1) && (k[e] >> 21) >= b1) << e;
@@ -727,10 +723,10 @@ __global__ __launch_bounds__(kChunkThreads) void topk_cand_kernel(SMLA_TOPK_ARGS
         if (m >> e & 1) w.cand[o++] = make_uint2(k[e], (uint32_t)(p0 + e));
     }
     off += tot;
-    if (g + 1 >= p.sub || nb >= n) break;
+    if (!more) break;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) k[e] = kn[e];
-    valid = vn;
+    for (int e = 0; e < kPer; ++e) v[e] = vn[e];
+    valid = vv;
   }
 }
 
@@ -841,12 +837,18 @@ __global__ __launch_bounds__(kChunkThreads) void topk_scand_kernel(SMLA_TOPK_ARG
   if (n <= p.topk || base >= n) return;  // trivial row, or past its end
   const TopkWs2 w = row_ws2(p, row);
   const float* sc = p.scores + row * p.max_ctx;
-  uint32_t k[kPer], valid, kn[kPer], vn = 0;
-  load_chunk<V4>(sc, base + kPer * tid, n, k, valid);
+  // the sample's loads, then this chunk's first sub-chunk's: the sample is
+  // waited for first, the sub-chunk stays in flight through tau
   const bool whole = n <= kSample;
   const int s0 = whole ? 16 * tid : (int)(((int64_t)tid * n / kSampleBlocks) & ~3LL);
-  uint32_t sk[16], sv;
-  load_chunk<V4>(sc, s0, n, sk, sv);
+  float sr[16];
+  uint32_t sv;
+  load_chunk<V4>(sc, s0, n, p.max_ctx, sr, sv);
+  float v[kPer], vn[kPer];
+  uint32_t valid, vv;
+  load_chunk<V4>(sc, base + kPer * tid, n, p.max_ctx, v, valid);
+  uint32_t sk[16];
+  raw_keys(sr, sk);
   for (int i = tid; i < kBins; i += kChunkThreads) hist[i] = 0;
   const int S = whole ? n : kSample;
   const int64_t r_est = (3LL * p.topk * S) / (2LL * n) + 32;
@@ -872,8 +874,12 @@ __global__ __launch_bounds__(kChunkThreads) void topk_scand_kernel(SMLA_TOPK_ARG
   uint32_t off = 0;
   for (int g = 0; g < p.sub; ++g) {
     const int p0 = base + g * kSub + kPer * tid;
-    const int nb = base + (g + 1) * kSub;
-    if (g + 1 < p.sub && nb < n) load_chunk<V4>(sc, nb + kPer * tid, n, kn, vn);
+    const bool more = g + 1 < p.sub && base + (g + 1) * kSub < n;
+    // the next sub-chunk, or this one again (cached; never used)
+    const int nb = base + (more ? g + 1 : g) * kSub;
+    load_chunk<V4>(sc, nb + kPer * tid, n, p.max_ctx, vn, vv);
+    uint32_t k[kPer];
+    raw_keys(v, k);
     uint32_t m = 0;
 #pragma unroll
     for (int e = 0; e < kPer; ++e) m |= (uint32_t)((valid >> e & 1) && k[e] >= tau) << e;
@@ -888,10 +894,10 @@ __global__ __launch_bounds__(kChunkThreads) void topk_scand_kernel(SMLA_TOPK_ARG
         }
     }
     off += tot;
-    if (g + 1 >= p.sub || nb >= n) break;
+    if (!more) break;
 #pragma unroll
-    for (int e = 0; e < kPer; ++e) k[e] = kn[e];
-    valid = vn;
+    for (int e = 0; e < kPer; ++e) v[e] = vn[e];
+    valid = vv;
   }
   if (tid == 0) w.cnt[c] = off;
 }

@@ -770,9 +770,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_select_kernel(SMLA_TOPK_ARG
 
 // ---------------------------------------------------------------------------
 // Sampled form for few long rows: two launches, and the scores are read once.
-//   1. topk_scand_kernel (row x chunk, chunks of sub <= 4 sub-chunks of kSub
+//   1. topk_scand_kernel (chunk x row, chunks of sub <= 4 sub-chunks of kSub
 //      positions, the next one's loads issued before the current one is
-//      counted; the chunk workgroups of a row on one XCD).  Every chunk
+//      counted).  Every chunk
 //      workgroup of a row takes the same sample of the row: 256
 //      blocks of 16 consecutive positions at even strides, or the whole row
 //      when it holds at most 4096 positions.  From the sample's keys (two
@@ -801,17 +801,6 @@ typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 constexpr int kStageLoads = kCandCap * 8 / 16 / kTopkThreads;  // 16-byte loads per thread
 static_assert(kStageLoads * kTopkThreads * 16 == kCandCap * 8, "staging covers the area");
 
-// The dispatcher hands workgroup i to XCD i % 8; this renumbering gives every
-// XCD a contiguous range of logical ids, so the chunk workgroups of a row
-// share an L2 (the row's sample is fetched from HBM once).  A bijection for
-// any grid size.
-__device__ __forceinline__ int xcd_contiguous_id(int bid, int n) {
-  constexpr int kX = 8;
-  const int xcd = bid % kX, k = bid / kX;
-  const int per = n / kX, rem = n % kX;
-  return xcd < rem ? xcd * (per + 1) + k : rem * (per + 1) + (xcd - rem) * per + k;
-}
-
 struct TopkWs2 {
   uint2* cand;    // [kCandCap] (key, position), region c at c * (kCandCap / nch)
   uint32_t* cnt;  // [chunks] candidates found per chunk
@@ -828,9 +817,14 @@ __global__ __launch_bounds__(kChunkThreads) void topk_scand_kernel(SMLA_TOPK_ARG
   __shared__ uint32_t sw[kChunkThreads / 64 + 1];
   __shared__ uint32_t sel[2];
   const int tid = threadIdx.x;
-  const int bid = xcd_contiguous_id(blockIdx.x, gridDim.x);
-  const int64_t row = bid / p.chunks;
-  const int c = bid % p.chunks;
+  // chunk-major numbering: every row's chunk 0 first, then every row's chunk
+  // 1, ..., so the chunks that exist (shorter rows have fewer; the others'
+  // workgroups exit at once) spread evenly over the CUs (ragged rows: 35.3 ->
+  // 33.9 us per call against row-major); with rows a multiple of 8, all of a
+  // row's chunks sit on XCD row % 8 (the dispatcher's round robin), so its
+  // sample is fetched from HBM once
+  const int c = (int)(blockIdx.x / p.rows);
+  const int64_t row = blockIdx.x % p.rows;
   const int n = row_len(p, row);
   const int span = p.sub * kSub;  // p.sub <= kSampledMaxSub (host)
   const int base = c * span;
@@ -910,9 +904,9 @@ __global__ __launch_bounds__(kTopkThreads) void topk_sel2_kernel(SMLA_TOPK_ARGS)
   __shared__ uint32_t off_s[kSampledMaxChunks + 1];
   __shared__ uint32_t bad_s;
   const int tid = threadIdx.x;
-  // rows numbered as the chunk launch numbers them, so a row is selected on
-  // the XCD whose L2 took its candidates
-  const int64_t row = xcd_contiguous_id(blockIdx.x, gridDim.x);
+  // row r on XCD r % 8, where the chunk launch put its chunks (rows a
+  // multiple of 8), so its candidates are in that XCD's L2
+  const int64_t row = blockIdx.x;
   const int n = row_len(p, row);
   if (n <= p.topk) {
     take_all(p, row, n);

@@ -143,6 +143,27 @@ def test_topk_random_shapes(smla, seed):
         _same(_run(smla, scores, k, ctx, form), want, f"seed {seed}: b{b} q{lq} m{m} k{k} {kind} form={form}")
 
 
+def test_topk_rows_past_sampled_limit(smla):
+    """Rows of 1100000 positions, past the 1048576 the sampled form takes:
+    AUTO and the forced sampled form run the four launches there; two rows,
+    one cut short by its context."""
+    m = 1_100_000
+    scores = index_scores(7450, 2, 1, m, "normal")
+    ctx = [m, 700_001]
+    want = oracle.topk_positions(scores, ctx, 2048)
+    for form in ("chunks", "sampled"):
+        _same(_run(smla, scores, 2048, ctx, form), want, f"1.1M positions form={form}")
+    import torch
+    s = torch.from_numpy(scores).cuda()
+    out = torch.full((2, 1, 2048), 12345, dtype=torch.int32, device="cuda")
+    n = smla.smla_topk_workspace_bytes(2, 1, m)
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    smla.smla_topk(s, 2048, out, torch.tensor(ctx, dtype=torch.int32, device="cuda"), workspace_t=ws,
+                   form=smla.TOPK_AUTO)
+    torch.cuda.synchronize()
+    _same(out.cpu().numpy(), want, "1.1M positions form=auto")
+
+
 def test_topk_sample_misleads(smla):
     """Scores large exactly on the sampled form's sample (256 blocks of 16
     positions at offsets floor(t n / 256) rounded down to a multiple of 4)

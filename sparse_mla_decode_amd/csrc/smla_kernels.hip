@@ -1208,6 +1208,8 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
   constexpr int NTD = 256;                      // loading threads: the four PV waves
   constexpr int L = TR * kRowGran / NTD;        // 9 loads per loading lane per tile
   constexpr int CBP = 8;                        // 16-column blocks of O per PV wave
+  constexpr int kStageRow = 1056;               // staged output row: 1 KB + 32 B (banks)
+  static_assert(32 * kStageRow <= TR * kRow * 2, "32 staged rows fit a tile buffer");
   static_assert(TR == 32 && L == 9, "tile shape");
 
   __shared__ __attribute__((aligned(16))) uint8_t tb0[kTileBytes];
@@ -1600,12 +1602,15 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
       if (h >= p.heads) continue;
       const int64_t th = (int64_t)tok * p.heads + h;
       if (p.nsplit == 1) {
-        uint16_t* orow = p.out + th * kDV;
+        // into LDS (the free tile buffers, head rows of kStageRow bytes);
+        // copied out below with 16-byte stores, 1 KB per wave instruction
+        const int r = gi * 16 + l16;
+        uint8_t* srow = (r < 32 ? tb0 : tb1) + (r & 31) * kStageRow;
 #pragma unroll
         for (int cb = 0; cb < CBP; ++cb) {
           const int c0 = (c * CBP + cb) * 16 + 4 * g;
           const floatx4 o = oacc[gi][cb] * inv;
-          *(u32x2*)(orow + c0) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+          *(u32x2*)(srow + c0 * 2) = u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
         }
       } else {
         const int64_t slot = ((int64_t)tok * p.nsplit + split) * p.heads + h;
@@ -1620,6 +1625,19 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
             *(floatx4*)(orow + c0) = oacc[gi][cb] * inv;
           }
         }
+      }
+    }
+  }
+  if (p.nsplit == 1) {  // the staged outputs of the block's heads, row by row
+    barrier_lds();
+    const int hv = min(kHeadsPerBlock, p.heads - hblk * kHeadsPerBlock);
+#pragma unroll
+    for (int u = 0; u < kHeadsPerBlock * 64 / NT; ++u) {
+      const int q = u * NT + tid, r = q >> 6, c16 = q & 63;
+      if (r < hv) {
+        const uint8_t* srow = (r < 32 ? tb0 : tb1) + (r & 31) * kStageRow;
+        const u32x4 v = *(const u32x4*)(srow + c16 * 16);
+        *(u32x4*)(p.out + ((int64_t)tok * p.heads + hblk * kHeadsPerBlock + r) * kDV + c16 * 8) = v;
       }
     }
   }

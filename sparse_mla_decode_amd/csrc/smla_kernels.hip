@@ -17,9 +17,9 @@
 //   * workgroup = (token, head block, split); a head block is 16, 32 or 64
 //     heads (by head count) in groups of 16, the N width of one MFMA.
 //   * the split's rows are gathered in 32-row tiles (x 1152 B) by LDS-DMA
-//     (global_load_lds, 16 bytes per lane), straight into one of two LDS
-//     tile buffers laid out for the measured bank rules: tile n+1 loads while
-//     tile n is computed.  Every wave of the workgroup reads the same tile,
+//     (global_load_lds, 16 bytes per lane), straight into LDS tile buffers
+//     laid out for the measured bank rules (two: tile n+1 loads while tile n
+//     is computed; four in split64_kernel: two tiles in flight).  Every wave of the workgroup reads the same tile,
 //     so a row is fetched from HBM once per workgroup.
 //   * S^T = KV_tile * Q^T on v_mfma_f32_16x16x32_bf16 (rows on M, heads on N)
 //     so that each lane owns one head: the online-softmax max needs two
@@ -41,7 +41,9 @@
 //     all-zero row, so their V contribution is exactly zero, and get a score
 //     of -inf.
 //   * the partials are merged by a second launch (combine kernels), or, for
-//     smla_decode_fused, inside the split launch (fused_combine).
+//     smla_decode_fused, inside the split launch (fused_combine).  With
+//     NSPLIT 1 split64_kernel writes the final bf16 output, staged in its
+//     free tile buffers and stored 1 KB of a head row per wave instruction.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>

@@ -41,9 +41,10 @@
 //     all-zero row, so their V contribution is exactly zero, and get a score
 //     of -inf.
 //   * the partials are merged by a second launch (combine kernels), or, for
-//     smla_decode_fused, inside the split launch (fused_combine).  With
-//     NSPLIT 1 split64_kernel writes the final bf16 output, staged in its
-//     free tile buffers and stored 1 KB of a head row per wave instruction.
+//     smla_decode_fused, inside the split launch (fused_combine).
+//     split64_kernel stages what it writes at the end (the final bf16 output
+//     with NSPLIT 1, else the fp32 partials) in its free tile buffers and
+//     stores it 1 KB of a head row per wave instruction.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -1211,6 +1212,8 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
   constexpr int L = TR * kRowGran / NTD;        // 9 loads per loading lane per tile
   constexpr int CBP = 8;                        // 16-column blocks of O per PV wave
   constexpr int kStageRow = 1056;               // staged output row: 1 KB + 32 B (banks)
+  constexpr int kStageRowF = 2080;              // staged fp32 partial row: 2 KB + 32 B
+  static_assert(16 * kStageRowF <= TR * kRow * 2, "16 staged partial rows fit a tile buffer");
   static_assert(32 * kStageRow <= TR * kRow * 2, "32 staged rows fit a tile buffer");
   static_assert(TR == 32 && L == 9, "tile shape");
 
@@ -1621,12 +1624,31 @@ void split64_kernel(const int32_t* a_idx, const uint16_t* a_q, const uint16_t* a
 #pragma unroll
           for (int cb = 0; cb < CBP; ++cb) st_agent(orow + (c * CBP + cb) * 16 + 4 * g, oacc[gi][cb] * inv);
         } else {
+          // into LDS (16 head rows of kStageRowF bytes per tile buffer),
+          // copied out below with 16-byte stores, 1 KB per wave instruction
+          const int r = gi * 16 + l16;
+          uint8_t* const sb = r < 16 ? tb0 : r < 32 ? tb1 : r < 48 ? tb2 : tb3;
+          uint8_t* const srow = sb + (r & 15) * kStageRowF;
 #pragma unroll
           for (int cb = 0; cb < CBP; ++cb) {
             const int c0 = (c * CBP + cb) * 16 + 4 * g;
-            *(floatx4*)(orow + c0) = oacc[gi][cb] * inv;
+            *(floatx4*)(srow + c0 * 4) = oacc[gi][cb] * inv;
           }
         }
+      }
+    }
+  }
+  if (p.nsplit > 1 && !p.sync) {  // the staged partials of the block's heads, row by row
+    barrier_lds();
+    const int hv = min(kHeadsPerBlock, p.heads - hblk * kHeadsPerBlock);
+    const int64_t slot0 = ((int64_t)tok * p.nsplit + split) * p.heads + hblk * kHeadsPerBlock;
+#pragma unroll
+    for (int u = 0; u < kHeadsPerBlock * 128 / NT; ++u) {
+      const int q = u * NT + tid, r = q >> 7, c16 = q & 127;
+      if (r < hv) {
+        const uint8_t* const sb = r < 16 ? tb0 : r < 32 ? tb1 : r < 48 ? tb2 : tb3;
+        const floatx4 v = *(const floatx4*)(sb + (r & 15) * kStageRowF + c16 * 16);
+        *(floatx4*)(p.part_o + (slot0 + r) * kDV + c16 * 4) = v;
       }
     }
   }

@@ -243,7 +243,11 @@ class Workload:
 
     def fused_fn(self, nsplit):
         ws = self.workspace(nsplit)
-        sync = self.smla.fused_sync(self.dev)
+        # one set of synchronisation words per workload, alive as long as the
+        # graphs that use it (every call leaves it zero)
+        if getattr(self, "sync", None) is None:
+            self.sync = self.smla.fused_sync(self.dev)
+        sync = self.sync
 
         def f(i):
             c, ix = self._args(i)

@@ -194,9 +194,10 @@ __device__ __forceinline__ shortx4 lds_tr16(const uint8_t* p) {
 // The partials travel between XCDs, whose L2 caches are not coherent with
 // each other for ordinary accesses: they are written and read with
 // agent-scope atomic accesses (8 bytes each), which the L2 keeps coherent.
-// (Ordinary 16-byte stores and loads ordered only by the ticket's release
-// and acquire measured slower: batched 57.1 -> 66.2 us per step, long
-// 10.1 -> 15.3; the release then writes every dirty partial line back.)
+// (Ordinary 16-byte stores and loads, ordered only by the ticket's release
+// and acquire, measured mixed: batched 69.3 -> 64.9 us per step and tiny
+// 8.65 -> 8.07, but long 13.9 -> 15.3 and spec 27.0 -> 30.0; every form
+// stays slower than two launches.)
 // The ticket's agent-scope release and acquire still cost an L2 writeback
 // and invalidate on this target (the compiler's implementation of those
 // orderings), part of why the single launch is slower than two.
